@@ -1,0 +1,213 @@
+"""CPU oracle for the SVDQuant W4A4 + low-rank linear (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It wraps ``svdq_oracle.c`` (plain C,
+fp64 where the method's pages fix no precision) through ctypes and shares
+no code with the HIP implementation.  The C file states the definition it
+follows and the readings taken where the pages are silent.
+
+Functions whose result is pinned by a test against something other than
+the oracle itself (closed forms, invariants, brute force, library special
+cases) are listed in ``tests/test_oracle_pins.py``; every function here has
+such a pin.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "svdq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GROUP = 64
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into ``oracle/liboracle.so`` with gcc."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int32
+    lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_gelu.argtypes = [ctypes.c_double]
+    lib.oracle_gelu.restype = ctypes.c_double
+    lib.oracle_smooth.argtypes = [P, P, I64, I64, P]
+    lib.oracle_quantize_groups.argtypes = [P, I64, I64, P, P]
+    lib.oracle_unpack.argtypes = [P, I64, I64, P]
+    lib.oracle_down_proj.argtypes = [P, P, I64, I64, I32, P]
+    lib.oracle_group_sums.argtypes = [P, P, I64, I64, I64, I64, I64, I64, I64, P]
+    lib.oracle_gemm_rows.argtypes = [P, P, P, P, P, P, P, I32, I64, I64, I64, I32,
+                                     P, I64, P, P]
+    for f in ("oracle_smooth", "oracle_quantize_groups", "oracle_unpack",
+              "oracle_down_proj", "oracle_group_sums", "oracle_gemm_rows"):
+        getattr(lib, f).restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    """OpenMP thread count used by the oracle (via omp_set_num_threads)."""
+    lib = _load()
+    try:
+        fn = lib.omp_set_num_threads
+    except AttributeError:
+        fn = ctypes.CDLL("libgomp.so.1").omp_set_num_threads
+    fn.argtypes = [ctypes.c_int]
+    fn(int(n))
+
+
+def bf16_rne(v: float) -> int:
+    """bf16 bit pattern of the nearest bf16 value to the double v (ties to even)."""
+    return int(_load().oracle_bf16_rne(float(v)))
+
+
+def gelu(x: float) -> float:
+    return float(_load().oracle_gelu(float(x)))
+
+
+def smooth(X: np.ndarray, lam: np.ndarray) -> np.ndarray:
+    """xh = fl32(bf16 X * fl32(1 / lam)) -> float32 [M, K]."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    lam = np.ascontiguousarray(lam, dtype=np.float32)
+    M, K = X.shape
+    xh = np.empty((M, K), np.float32)
+    _load().oracle_smooth(_ptr(X), _ptr(lam), M, K, _ptr(xh))
+    return xh
+
+
+def quantize_groups(v: np.ndarray):
+    """Group-64 symmetric INT4 quantization -> (packed uint8 [R, K/2], scales f32 [R, K/64])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, K = v.shape
+    assert K % GROUP == 0
+    packed = np.empty((rows, K // 2), np.uint8)
+    scales = np.empty((rows, K // GROUP), np.float32)
+    _load().oracle_quantize_groups(_ptr(v), rows, K, _ptr(packed), _ptr(scales))
+    return packed, scales
+
+
+def unpack(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    codes = np.empty((rows, K), np.int8)
+    _load().oracle_unpack(_ptr(packed), rows, K, _ptr(codes))
+    return codes
+
+
+def quantize_act(X: np.ndarray, lam: np.ndarray):
+    """Smoothing + activation quantization -> (qa, sa, xh)."""
+    xh = smooth(X, lam)
+    qa, sa = quantize_groups(xh)
+    return qa, sa, xh
+
+
+def pack_weights(R: np.ndarray):
+    """Offline residual quantization -> (qw uint8 [N, K/2], sw f32 [N, K/64])."""
+    return quantize_groups(R)
+
+
+def down_proj(xh: np.ndarray, L1: np.ndarray) -> np.ndarray:
+    """xl1 = xh @ L1 in fp64 -> float64 [M, r]."""
+    xh = np.ascontiguousarray(xh, dtype=np.float32)
+    L1 = np.ascontiguousarray(L1, dtype=np.uint16)
+    M, K = xh.shape
+    r = L1.shape[1] if L1.ndim == 2 else 0
+    out = np.zeros((M, r), np.float64)
+    if r > 0 and M > 0:
+        _load().oracle_down_proj(_ptr(xh), _ptr(L1), M, K, r, _ptr(out))
+    return out
+
+
+def group_sums(qa, qw, K: int, m0: int, n0: int, tm: int, tn: int) -> np.ndarray:
+    """Exact int32 per-group dot products for a block -> int32 [tm, tn, K/64]."""
+    qa = np.ascontiguousarray(qa, dtype=np.uint8)
+    qw = np.ascontiguousarray(qw, dtype=np.uint8)
+    M, N = qa.shape[0], qw.shape[0]
+    S = np.empty((tm, tn, K // GROUP), np.int32)
+    _load().oracle_group_sums(_ptr(qa), _ptr(qw), M, N, K, m0, n0, tm, tn, _ptr(S))
+    return S
+
+
+def gemm_rows(qa, sa, qw, sw, xl1: Optional[np.ndarray], L2: Optional[np.ndarray],
+              bias: Optional[np.ndarray], act: int, K: int,
+              rows: Optional[Sequence[int]] = None):
+    """Layer output for the given rows (all rows if None) -> (acc f64 [R, N], y bf16 bits [R, N])."""
+    qa = np.ascontiguousarray(qa, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    qw = np.ascontiguousarray(qw, dtype=np.uint8)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, N = qa.shape[0], qw.shape[0]
+    r = 0 if xl1 is None else xl1.shape[1]
+    if r > 0:
+        xl1 = np.ascontiguousarray(xl1, dtype=np.float64)
+        L2 = np.ascontiguousarray(L2, dtype=np.uint16)
+        assert L2.shape == (r, N)
+    else:
+        xl1 = None
+        L2 = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+    if rows is None:
+        rows_arr = None
+        nrows = M
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = len(rows_arr)
+    acc = np.empty((nrows, N), np.float64)
+    y = np.empty((nrows, N), np.uint16)
+    if nrows > 0:
+        _load().oracle_gemm_rows(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(xl1), _ptr(L2),
+                                 _ptr(bias), int(act), M, N, K, r, _ptr(rows_arr), nrows,
+                                 _ptr(acc), _ptr(y))
+    return acc, y
+
+
+def linear(X, lam, L1, qw, sw, L2, bias, act: int, rows=None):
+    """The whole layer from its call inputs: quantize + down-proj, then the W4A4 GEMM."""
+    K = X.shape[1]
+    qa, sa, xh = quantize_act(X, lam)
+    r = 0 if L1 is None else L1.shape[1]
+    xl1 = down_proj(xh, L1) if r > 0 else None
+    return gemm_rows(qa, sa, qw, sw, xl1, L2, bias, act, K, rows)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """ulp of bf16 values: 2^(floor(log2|v|) - 7) for normal v, 2^-133 below 2^-126, 0 for v == 0."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    out = np.zeros_like(a)
+    nz = a > 0
+    e = np.floor(np.log2(a[nz]))
+    e = np.maximum(e, -126.0)
+    out[nz] = np.exp2(e - 7.0)
+    return out
