@@ -1,0 +1,133 @@
+"""SVDQuant W4A4 + low-rank linear layer for MI355X (gfx950).
+
+The layer computes ``Y = act(Q4(X diag(lam)^-1) Q4(R)^T + (X diag(lam)^-1 L1) L2 + bias)``
+with group-64 INT4 activations and weights and a bf16 rank-r branch, in two
+HIP kernels behind the C ABI of ``include/svdq.h``.  This package is the
+thin Python binding: the ``svdq_*`` functions mirror the C entry points one
+to one, and the tensor helpers below only allocate outputs and workspaces.
+
+bf16 tensors may be passed as ``torch.bfloat16`` or as their ``int16``/
+``uint16`` bit patterns; they are reinterpreted, never converted.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError,  # noqa: F401
+                       load_library, svdq_abi_version, svdq_debug_group_sums,
+                       svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
+                       svdq_pack_weights, svdq_quantize_act_down,
+                       svdq_quantize_act_down_workspace_bytes, svdq_status_string,
+                       svdq_w4a4_lr_gemm)
+
+
+def _bits(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """bf16 tensor -> the same storage viewed as int16 (no copy)."""
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError("expected bf16 (or its 16-bit pattern), got %s" % t.dtype)
+
+
+def _rank(L: Optional[torch.Tensor], dim: int) -> int:
+    return 0 if L is None or L.numel() == 0 else int(L.shape[dim])
+
+
+def pack_weights(R: torch.Tensor):
+    """Residual fp32 [N, K] -> (qw uint8 [N, K/2], sw fp32 [N, K/64])."""
+    N, K = R.shape
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=R.device)
+    sw = torch.empty((N, K // GROUP), dtype=torch.float32, device=R.device)
+    svdq_pack_weights(R, N, K, qw, sw)
+    return qw, sw
+
+
+def quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Tensor]):
+    """X bf16 [M, K] -> (qa uint8 [M, K/2], sa fp32 [M, K/64], xl1 fp32 [M, r] or None)."""
+    M, K = X.shape
+    r = _rank(L1, 1)
+    dev = X.device
+    qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
+    xl1 = torch.empty((M, r), dtype=torch.float32, device=dev) if r > 0 else None
+    ws_bytes = svdq_quantize_act_down_workspace_bytes(K, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    svdq_quantize_act_down(_bits(X), lam, _bits(L1) if r > 0 else None, M, K, r, qa, sa, xl1,
+                           ws, ws_bytes)
+    return qa, sa, xl1
+
+
+def w4a4_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act: int = ACT_NONE) -> torch.Tensor:
+    """The W4A4 GEMM with the low-rank up-projection, bias and act -> Y bf16 [M, N]."""
+    M = qa.shape[0]
+    N = qw.shape[0]
+    K = qa.shape[1] * 2
+    r = _rank(L2, 0)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    svdq_w4a4_lr_gemm(qa, sa, qw, sw, xl1 if r > 0 else None, _bits(L2) if r > 0 else None,
+                      _bits(bias), act, M, N, K, r, _bits(Y))
+    return Y
+
+
+def linear(X, lam, L1, qw, sw, L2, bias, act: int = ACT_NONE,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole layer (svdq_linear) -> Y bf16 [M, N]."""
+    M, K = X.shape
+    N = qw.shape[0]
+    r = _rank(L1, 1)
+    need = svdq_linear_workspace_bytes(M, K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    svdq_linear(_bits(X), lam, _bits(L1) if r > 0 else None, qw, sw,
+                _bits(L2) if r > 0 else None, _bits(bias), act, M, N, K, r, _bits(Y),
+                workspace, need)
+    return Y
+
+
+def group_sums(qa, qw, m0: int, n0: int, tm: int, tn: int) -> torch.Tensor:
+    """Exact per-group int32 sums of a block (test hook) -> int32 [tm, tn, K/64]."""
+    M, N, K = qa.shape[0], qw.shape[0], qa.shape[1] * 2
+    S = torch.empty((tm, tn, K // GROUP), dtype=torch.int32, device=qa.device)
+    svdq_debug_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S)
+    return S
+
+
+class SVDQLinear:
+    """A drop-in W4A4 replacement for one linear layer.
+
+    ``from_parts`` takes the offline artefacts of SVDQuant (smoothing
+    factors, low-rank factors, fp32 residual, bias), packs the residual on
+    the GPU once, and ``__call__`` runs the fused layer.
+    """
+
+    def __init__(self, lam, L1, qw, sw, L2, bias, act: int = ACT_NONE):
+        self.lam, self.L1, self.qw, self.sw, self.L2, self.bias, self.act = \
+            lam, L1, qw, sw, L2, bias, act
+        self._ws = None
+
+    @classmethod
+    def from_parts(cls, lam, L1, R, L2, bias=None, act: int = ACT_NONE):
+        qw, sw = pack_weights(R)
+        return cls(lam, L1, qw, sw, L2, bias, act)
+
+    @property
+    def in_features(self) -> int:
+        return self.qw.shape[1] * 2
+
+    @property
+    def out_features(self) -> int:
+        return self.qw.shape[0]
+
+    def __call__(self, X: torch.Tensor) -> torch.Tensor:
+        M, K = X.shape
+        need = svdq_linear_workspace_bytes(M, K, _rank(self.L1, 1))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+        return linear(X, self.lam, self.L1, self.qw, self.sw, self.L2, self.bias, self.act,
+                      workspace=self._ws)

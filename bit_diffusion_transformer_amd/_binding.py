@@ -1,0 +1,148 @@
+"""ctypes binding of libsvdq.so (the C ABI in include/svdq.h).
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels.  torch supplies device memory and the current HIP stream.
+There is no fallback: if the library is missing and cannot be built, or the
+device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsvdq.so")
+
+STATUS = {
+    0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARG", 2: "SVDQ_ERR_UNSUPPORTED_SHAPE",
+    3: "SVDQ_ERR_MISALIGNED", 4: "SVDQ_ERR_WORKSPACE_TOO_SMALL",
+    5: "SVDQ_ERR_UNSUPPORTED_DEVICE", 6: "SVDQ_ERR_HIP",
+}
+ACT_NONE, ACT_GELU = 0, 1
+GROUP = 64
+
+# Every symbol declared in include/svdq.h.
+EXPORTS = (
+    "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_pack_weights",
+    "svdq_quantize_act_down_workspace_bytes", "svdq_quantize_act_down", "svdq_w4a4_lr_gemm",
+    "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
+)
+
+
+class SVDQError(RuntimeError):
+    def __init__(self, status: int, detail: str, fn: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (fn, STATUS.get(status, status), detail))
+
+
+_lib = None
+
+
+def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load libsvdq.so; build it first only if it has never been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise FileNotFoundError(LIB_PATH)
+        from .build import build
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "svdq_abi_version": ([], I32),
+        "svdq_status_string": ([I32], ctypes.c_char_p),
+        "svdq_last_error": ([], ctypes.c_char_p),
+        "svdq_pack_weights": ([P, I64, I64, P, P, P], I32),
+        "svdq_quantize_act_down_workspace_bytes": ([I64, I32], SZ),
+        "svdq_quantize_act_down": ([P, P, P, I64, I64, I32, P, P, P, P, SZ, P], I32),
+        "svdq_w4a4_lr_gemm": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P], I32),
+        "svdq_linear_workspace_bytes": ([I64, I64, I32], SZ),
+        "svdq_linear": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, SZ, P], I32),
+        "svdq_debug_group_sums": ([P, P, I64, I64, I64, I64, I64, I64, I64, P, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libsvdq must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        detail = load_library().svdq_last_error().decode(errors="replace")
+        raise SVDQError(status, detail, fn)
+
+
+# ------------------------------------------------------------- raw C-ABI calls
+# Same names and argument order as include/svdq.h; tensors in, status checked.
+
+def svdq_abi_version() -> int:
+    return int(load_library().svdq_abi_version())
+
+
+def svdq_status_string(status: int) -> str:
+    return load_library().svdq_status_string(int(status)).decode()
+
+
+def svdq_last_error() -> str:
+    return load_library().svdq_last_error().decode(errors="replace")
+
+
+def svdq_pack_weights(R, N, K, qw, sw, stream=None):
+    _check(load_library().svdq_pack_weights(_p(R), N, K, _p(qw), _p(sw), _stream(stream)),
+           "svdq_pack_weights")
+
+
+def svdq_quantize_act_down_workspace_bytes(K, r) -> int:
+    return int(load_library().svdq_quantize_act_down_workspace_bytes(K, r))
+
+
+def svdq_quantize_act_down(X, lam, L1, M, K, r, qa, sa, xl1, workspace, ws_bytes, stream=None):
+    _check(load_library().svdq_quantize_act_down(
+        _p(X), _p(lam), _p(L1), M, K, r, _p(qa), _p(sa), _p(xl1), _p(workspace), ws_bytes,
+        _stream(stream)), "svdq_quantize_act_down")
+
+
+def svdq_w4a4_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, stream=None):
+    _check(load_library().svdq_w4a4_lr_gemm(
+        _p(qa), _p(sa), _p(qw), _p(sw), _p(xl1), _p(L2), _p(bias), act, M, N, K, r, _p(Y),
+        _stream(stream)), "svdq_w4a4_lr_gemm")
+
+
+def svdq_linear_workspace_bytes(M, K, r) -> int:
+    return int(load_library().svdq_linear_workspace_bytes(M, K, r))
+
+
+def svdq_linear(X, lam, L1, qw, sw, L2, bias, act, M, N, K, r, Y, workspace, ws_bytes,
+                stream=None):
+    _check(load_library().svdq_linear(
+        _p(X), _p(lam), _p(L1), _p(qw), _p(sw), _p(L2), _p(bias), act, M, N, K, r, _p(Y),
+        _p(workspace), ws_bytes, _stream(stream)), "svdq_linear")
+
+
+def svdq_debug_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S, stream=None):
+    _check(load_library().svdq_debug_group_sums(
+        _p(qa), _p(qw), M, N, K, m0, n0, tm, tn, _p(S), _stream(stream)),
+        "svdq_debug_group_sums")

@@ -1,0 +1,301 @@
+// svdq_api.hip -- the C ABI declared in include/svdq.h: argument validation,
+// the gfx950 device check, workspace carving and kernel launches.
+//
+// Order of checks: every argument first (no device call needed, so argument
+// errors are reported on any host), then the device architecture, then the
+// launches.  Nothing is written before all checks pass.  Unsupported hardware
+// is refused with a clear error instead of running (the "Hardware support"
+// section of the Nunchaku 4-bit in Diffusers blog does the same at load time).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "svdq.h"
+#include "svdq_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int32_t check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_DEVICE, "no HIP device available (%s)",
+                    hipGetErrorString(e));
+    if (dev < kMaxDevices) {
+        int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (v == 1) return SVDQ_OK;
+        if (v == 2) return fail(SVDQ_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+        return fail(SVDQ_ERR_UNSUPPORTED_DEVICE, "hipGetDeviceProperties failed: %s",
+                    hipGetErrorString(e));
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    if (!ok)
+        return fail(SVDQ_ERR_UNSUPPORTED_DEVICE,
+                    "device %d is %s; this library is built for gfx950 (MI355X) only", dev,
+                    prop.gcnArchName);
+    return SVDQ_OK;
+}
+
+int32_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return SVDQ_OK;
+    return fail(SVDQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t check_k(int64_t K) {
+    if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "K must be a positive multiple of 64 (got %lld)",
+                    (long long)K);
+    return SVDQ_OK;
+}
+
+int32_t check_r(int32_t r) {
+    if (r < 0 || r > SVDQ_MAX_RANK || r % 16 != 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
+                    "rank r must be a multiple of 16 in [0, %d] (got %d)", SVDQ_MAX_RANK, r);
+    return SVDQ_OK;
+}
+
+int32_t check_n(int64_t N) {
+    if (N < 8 || N % 8 != 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "N must be a positive multiple of 8 (got %lld)",
+                    (long long)N);
+    return SVDQ_OK;
+}
+
+#define SVDQ_TRY(expr)                       \
+    do {                                     \
+        int32_t _s = (expr);                 \
+        if (_s != SVDQ_OK) return _s;        \
+    } while (0)
+
+int32_t need_ptr(const void *p, const char *name) {
+    if (!p) return fail(SVDQ_ERR_INVALID_ARG, "%s must not be NULL", name);
+    if (!aligned16(p)) return fail(SVDQ_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+    return SVDQ_OK;
+}
+
+int32_t lr_ptrs(const void *a, const char *an, const void *b, const char *bn, int32_t r) {
+    if (r == 0) {
+        if (a || b)
+            return fail(SVDQ_ERR_INVALID_ARG, "%s and %s must be NULL when r == 0", an, bn);
+        return SVDQ_OK;
+    }
+    SVDQ_TRY(need_ptr(a, an));
+    return need_ptr(b, bn);
+}
+
+int32_t validate_down(const uint16_t *X, const float *lambda, const uint16_t *L1, int64_t M,
+                      int64_t K, int32_t r, const uint8_t *qa, const float *sa,
+                      const float *xl1, const void *ws, size_t ws_bytes) {
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_r(r));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(X, "X"));
+    SVDQ_TRY(need_ptr(lambda, "lambda"));
+    SVDQ_TRY(need_ptr(qa, "qa"));
+    SVDQ_TRY(need_ptr(sa, "sa"));
+    SVDQ_TRY(lr_ptrs(L1, "L1", xl1, "xl1", r));
+    const size_t need = svdq::down_workspace_bytes(K, r);
+    if (ws_bytes < need)
+        return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed",
+                    ws_bytes, need);
+    return need_ptr(ws, "workspace");
+}
+
+int32_t validate_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
+                      const float *xl1, const uint16_t *L2, const uint16_t *bias, int32_t act,
+                      int64_t M, int64_t N, int64_t K, int32_t r, const uint16_t *Y) {
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
+        return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
+    SVDQ_TRY(check_n(N));
+    SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_r(r));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(qa, "qa"));
+    SVDQ_TRY(need_ptr(sa, "sa"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
+    SVDQ_TRY(need_ptr(Y, "Y"));
+    SVDQ_TRY(lr_ptrs(xl1, "xl1", L2, "L2", r));
+    if (bias && !aligned16(bias)) return fail(SVDQ_ERR_MISALIGNED, "bias is not 16-byte aligned");
+    return SVDQ_OK;
+}
+
+struct LinearWorkspace {
+    uint8_t *qa;
+    float *sa;
+    float *xl1;
+    void *down;
+    size_t bytes;
+};
+
+LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r) {
+    using svdq::align256;
+    LinearWorkspace w{};
+    char *p = static_cast<char *>(base);
+    size_t off = 0;
+    w.qa = reinterpret_cast<uint8_t *>(p + off);
+    off += align256((size_t)M * (size_t)(K / 2));
+    w.sa = reinterpret_cast<float *>(p + off);
+    off += align256((size_t)M * (size_t)(K / SVDQ_GROUP) * 4);
+    w.xl1 = r > 0 ? reinterpret_cast<float *>(p + off) : nullptr;
+    off += align256((size_t)M * (size_t)r * 4);
+    w.down = p + off;
+    off += svdq::down_workspace_bytes(K, r);
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
+
+const char *svdq_status_string(int32_t s) {
+    switch (s) {
+        case SVDQ_OK: return "ok";
+        case SVDQ_ERR_INVALID_ARG: return "invalid argument";
+        case SVDQ_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case SVDQ_ERR_MISALIGNED: return "misaligned pointer";
+        case SVDQ_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case SVDQ_ERR_UNSUPPORTED_DEVICE: return "unsupported device";
+        case SVDQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *svdq_last_error(void) { return g_last_error; }
+
+int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
+                          void *stream) {
+    g_last_error[0] = 0;
+    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+    SVDQ_TRY(check_k(K));
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(R, "R"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_pack_weights(R, N, K, qw, sw, (hipStream_t)stream),
+                      "pack_weights launch");
+}
+
+size_t svdq_quantize_act_down_workspace_bytes(int64_t K, int32_t r) {
+    if (K < 0 || r < 0) return 0;
+    return svdq::down_workspace_bytes(K, r);
+}
+
+int32_t svdq_quantize_act_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                               int64_t M, int64_t K, int32_t r, uint8_t *qa, float *sa,
+                               float *xl1, void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    SVDQ_TRY(validate_down(X, lambda, L1, M, K, r, qa, sa, xl1, workspace, ws_bytes));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(workspace, K, r);
+    SVDQ_TRY(hip_status(svdq::launch_prep_down(lambda, L1, K, r, dw, s), "prep launch"));
+    return hip_status(svdq::launch_quant_down(X, M, K, r, dw, qa, sa, xl1, s),
+                      "quantize_act_down launch");
+}
+
+int32_t svdq_w4a4_lr_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                          const float *sw, const float *xl1, const uint16_t *L2,
+                          const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                          int32_t r, uint16_t *Y, void *stream) {
+    g_last_error[0] = 0;
+    SVDQ_TRY(validate_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_w4a4_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y,
+                                             (hipStream_t)stream),
+                      "w4a4_lr_gemm launch");
+}
+
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t r) {
+    if (M < 0 || K < 0 || r < 0) return 0;
+    return carve_linear(nullptr, M, K, r).bytes;
+}
+
+int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                    const uint8_t *qw, const float *sw, const uint16_t *L2,
+                    const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                    int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
+        return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
+    SVDQ_TRY(check_n(N));
+    SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_r(r));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(X, "X"));
+    SVDQ_TRY(need_ptr(lambda, "lambda"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
+    SVDQ_TRY(need_ptr(Y, "Y"));
+    SVDQ_TRY(lr_ptrs(L1, "L1", L2, "L2", r));
+    if (bias && !aligned16(bias)) return fail(SVDQ_ERR_MISALIGNED, "bias is not 16-byte aligned");
+    const size_t need = carve_linear(nullptr, M, K, r).bytes;
+    if (ws_bytes < need)
+        return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed", ws_bytes,
+                    need);
+    SVDQ_TRY(need_ptr(workspace, "workspace"));
+    SVDQ_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    const LinearWorkspace w = carve_linear(workspace, M, K, r);
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.down, K, r);
+    SVDQ_TRY(hip_status(svdq::launch_prep_down(lambda, L1, K, r, dw, s), "prep launch"));
+    SVDQ_TRY(hip_status(svdq::launch_quant_down(X, M, K, r, dw, w.qa, w.sa, w.xl1, s),
+                        "quantize_act_down launch"));
+    return hip_status(svdq::launch_w4a4_gemm(w.qa, w.sa, qw, sw, w.xl1, L2, bias, act, M, N, K,
+                                             r, Y, s),
+                      "w4a4_lr_gemm launch");
+}
+
+int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
+                              int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
+                              int32_t *S, void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0 || N < 0 || m0 < 0 || n0 < 0 || tm < 0 || tn < 0 || m0 + tm > M || n0 + tn > N)
+        return fail(SVDQ_ERR_INVALID_ARG, "block [%lld,+%lld) x [%lld,+%lld) outside %lld x %lld",
+                    (long long)m0, (long long)tm, (long long)n0, (long long)tn, (long long)M,
+                    (long long)N);
+    SVDQ_TRY(check_k(K));
+    if (tm == 0 || tn == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(qa, "qa"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(S, "S"));
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S,
+                                              (hipStream_t)stream),
+                      "group_sums launch");
+}
+
+}  // extern "C"

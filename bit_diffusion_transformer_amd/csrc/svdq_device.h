@@ -1,0 +1,106 @@
+// svdq_device.h -- device helpers shared by the gfx950 kernels of the
+// SVDQuant W4A4 + low-rank linear layer (internal; not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+constexpr int kGroup = 64;   // quantization group along K
+
+typedef int      i32x4 __attribute__((ext_vector_type(4)));
+typedef float    f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16   bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16   bf16x2 __attribute__((ext_vector_type(2)));
+typedef float    f32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 b = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// 16x16 output tile, K = 64 int8 per call.  Lane l supplies, for row/column
+// l % 16, 16 int8 of k-slot l / 16; the output lane l holds rows
+// 4*(l/16) + j, j = 0..3, of column l % 16.
+__device__ __forceinline__ i32x4 mfma_i8_16x16x64(i32x4 a, i32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// 16x16 output tile, K = 32 bf16 per call (8 per lane), fp32 accumulate; the
+// output layout is the same as the int8 instruction's.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- 4-bit operands
+
+// Widen 16 packed two's-complement nibbles (two dwords, element 2j in the
+// low nibble of byte j) into 16 int8 holding 16 * code: the even elements
+// land in dwords 0 and 2, the odd ones in dwords 1 and 3.  Both GEMM
+// operands are widened the same way, so the k pairing is preserved and the
+// int32 dot product is exactly 256 * (the dot product of the codes).
+__device__ __forceinline__ i32x4 widen_nibbles(u32x2 p) {
+    i32x4 r;
+    r.x = (int)((p.x << 4) & 0xF0F0F0F0u);
+    r.y = (int)(p.x & 0xF0F0F0F0u);
+    r.z = (int)((p.y << 4) & 0xF0F0F0F0u);
+    r.w = (int)(p.y & 0xF0F0F0F0u);
+    return r;
+}
+
+// ---------------------------------------------------------------- quantizer
+
+// Quantize one group of 64 values spread over the four lanes
+// l, l^16, l^32, l^48 (16 consecutive values per lane).  Returns the group
+// scale s = max|v| / 7 (every lane of the group gets it) and writes the
+// lane's 16 codes, packed two per byte (element 2j in the low nibble), into
+// `packed`.  The code is rint(fl32(v * fl32(1/s))) clamped to [-7, 7]; a
+// zero scale or a non-finite 1/s gives zero codes.  Division is IEEE
+// correctly rounded (hipcc's default); no contraction is allowed here.
+__device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &packed) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float s = amax / 7.0f;
+    float inv = 0.0f;
+    if (s != 0.0f) {
+        const float t = 1.0f / s;
+        inv = __builtin_isfinite(t) ? t : 0.0f;
+    }
+    // rint via the 1.5*2^23 bias: after the clamp |y| <= 7, so y + 12582912
+    // rounds (nearest even) to an integer whose low 4 bits are the code's
+    // two's-complement nibble.  Funnel-shifting the nibbles in from the top
+    // leaves element j in nibble j.
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float y = __builtin_amdgcn_fmed3f(v[j] * inv, -7.0f, 7.0f);
+        w0 = __builtin_amdgcn_alignbit(__float_as_uint(y + 12582912.0f), w0, 4);
+    }
+#pragma unroll
+    for (int j = 8; j < 16; ++j) {
+        const float y = __builtin_amdgcn_fmed3f(v[j] * inv, -7.0f, 7.0f);
+        w1 = __builtin_amdgcn_alignbit(__float_as_uint(y + 12582912.0f), w1, 4);
+    }
+    packed.x = w0;
+    packed.y = w1;
+    return s;
+}
+
+}  // namespace svdq

@@ -1,0 +1,178 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 + low-rank linear layer.
+ *
+ * The layer (SVDQuant: "svdq-int4-flux.1-canny-dev" model card, section
+ * "SVDQuant overview", stages 1-3; "Nunchaku 4-bit in Diffusers" blog,
+ * sections "Background: SVDQuant and Nunchaku" and "Introducing Nunchaku
+ * Lite", kernel family svdq_w4a4) computes, for activations X [M, K]:
+ *
+ *   Xs = X diag(lambda)^-1                       smoothing (stage 2)
+ *   Y  = Q4(Xs) Q4(R)^T  +  (Xs L1) L2  +  bias  4-bit residual path plus the
+ *                                                16-bit rank-r branch (stage 3)
+ *   Y  = GELU(Y) optionally (erf form)
+ *
+ * Q4 is symmetric group quantization along K: groups of 64 consecutive
+ * inputs, one fp32 scale s = max|v| / 7 per (row, group), code
+ * q = rint(fl32(v * fl32(1/s))) (ties to even) in [-7, 7]; s == 0, or a
+ * 1/s that is not finite, gives all-zero codes.  The pages leave these
+ * details open; this is the reading the library implements and its tests
+ * pin.  The product of the two quantized operands is taken as an exact
+ * integer sum per group, S[m][n][g] = sum_{k in g} qa[m][k] qw[n][k], then
+ * rescaled: Y_4bit[m][n] = sum_g sa[m][g] sw[n][g] S[m][n][g].
+ *
+ * The engine-design section of the model card fuses the low-rank
+ * down-projection with quantization (they read the same input) and the
+ * up-projection with the 4-bit product (they write the same output); the
+ * entry points below follow that split: svdq_quantize_act_down reads X once
+ * and emits codes, scales and X L1; svdq_w4a4_lr_gemm runs the 4-bit GEMM and
+ * adds the low-rank up-projection, bias and activation to the same output
+ * tile before its single bf16 store.  svdq_linear runs both.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are
+ *     row-major and contiguous.  Pointers marked "device" must point to
+ *     memory of the current HIP device and be 16-byte aligned.
+ *   - Packed codes: two per byte, element 2j in the low nibble, two's
+ *     complement (nibble 0x9 = -7, 0xF = -1).  Scales: fp32 [rows, K/64].
+ *   - The caller owns and allocates every buffer.  The library allocates
+ *     nothing and keeps no state except a per-device architecture check.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and the call returns without synchronizing.  Outputs are defined once
+ *     the stream reaches that point.
+ *   - Every argument is validated before anything is launched, so an error
+ *     status means no output was written.  Arguments are checked first,
+ *     then the device: argument errors are reported on any host.
+ *   - Outputs must not alias inputs.  Calls on different streams may run
+ *     concurrently when their buffers are disjoint.
+ *   - Results are deterministic: no atomics take part in any sum, so two
+ *     runs with the same inputs give bitwise identical outputs.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVDQ_ABI_VERSION 1
+#define SVDQ_GROUP 64      /* quantization group along K */
+#define SVDQ_MAX_RANK 128  /* largest supported low-rank r */
+
+typedef enum {
+    SVDQ_OK = 0,
+    SVDQ_ERR_INVALID_ARG = 1,       /* NULL pointer where data is needed, negative size, bad act */
+    SVDQ_ERR_UNSUPPORTED_SHAPE = 2, /* K % 64 != 0, K < 64, N % 8 != 0, r not a multiple of 16 or > 128 */
+    SVDQ_ERR_MISALIGNED = 3,        /* a device pointer not 16-byte aligned */
+    SVDQ_ERR_WORKSPACE_TOO_SMALL = 4,
+    SVDQ_ERR_UNSUPPORTED_DEVICE = 5, /* current device is not gfx950 (or no device) */
+    SVDQ_ERR_HIP = 6                 /* HIP runtime / launch error, see svdq_last_error() */
+} svdq_status;
+
+typedef enum {
+    SVDQ_ACT_NONE = 0,
+    SVDQ_ACT_GELU = 1 /* 0.5 x (1 + erf(x / sqrt 2)) */
+} svdq_act;
+
+/* ABI version (SVDQ_ABI_VERSION). */
+int32_t svdq_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *svdq_status_string(int32_t status);
+
+/* Detail of the last error on the calling thread ("" if none). Valid until
+ * the next call on this thread. */
+const char *svdq_last_error(void);
+
+/*
+ * Offline weight preparation of the 4-bit residual (stage 3 of the SVDQuant
+ * overview; the offline toolchain's "quantize, pack" steps in the blog's
+ * section "Quantize your own model").
+ *   R   device fp32 [N, K]  residual weight (nn.Linear orientation, out x in)
+ *   qw  device u8   [N, K/2] packed 4-bit codes (out)
+ *   sw  device fp32 [N, K/64] group scales (out)
+ * Same quantizer as the activations, without smoothing.  N >= 0 (0: no-op),
+ * K % 64 == 0, K >= 64.
+ */
+int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
+                          void *stream);
+
+/*
+ * Workspace bytes svdq_quantize_act_down needs: the reciprocal smoothing
+ * factors and the transposed, smoothed low-rank factor L1 diag(lambda)^-1 as
+ * a bf16 hi/lo pair (rebuilt on every call from lambda and L1).
+ */
+size_t svdq_quantize_act_down_workspace_bytes(int64_t K, int32_t r);
+
+/*
+ * Smoothing, activation quantization and low-rank down-projection in one
+ * pass over X (model card, section "Nunchaku engine design", item (b): the
+ * down-projection and the quantizer share their input).
+ *   X       device bf16 [M, K]   activations
+ *   lambda  device fp32 [K]      smoothing factors, finite and > 0
+ *   L1      device bf16 [K, r]   low-rank down factor (NULL iff r == 0)
+ *   qa      device u8   [M, K/2] packed codes of X diag(lambda)^-1 (out)
+ *   sa      device fp32 [M, K/64] group scales (out)
+ *   xl1     device fp32 [M, r]   (X diag(lambda)^-1) L1, fp32 (out; NULL iff r == 0)
+ *   workspace / ws_bytes  device scratch of at least
+ *           svdq_quantize_act_down_workspace_bytes(K, r) bytes (may be NULL
+ *           when that is 0)
+ * M >= 0 (0: no-op), K % 64 == 0, r in {0, 16, 32, ..., 128}.
+ * qa and sa are bit-exact with the definition above; xl1 is accurate to
+ * about 2^-16 relative per term (bf16 hi/lo products, fp32 sums).
+ */
+int32_t svdq_quantize_act_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                               int64_t M, int64_t K, int32_t r, uint8_t *qa, float *sa,
+                               float *xl1, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The W4A4 GEMM with the low-rank up-projection, bias and activation in its
+ * epilogue (model card, section "Nunchaku engine design", item (b): the
+ * up-projection and the 4-bit compute share their output).
+ *   qa, sa     device  codes / scales of the activations (from svdq_quantize_act_down)
+ *   qw, sw     device  codes / scales of the residual weight (from svdq_pack_weights)
+ *   xl1        device fp32 [M, r]  (NULL iff r == 0)
+ *   L2         device bf16 [r, N]  low-rank up factor (NULL iff r == 0)
+ *   bias       device bf16 [N] or NULL
+ *   act        svdq_act
+ *   Y          device bf16 [M, N]  output (out)
+ * M >= 0 (0: no-op), N % 8 == 0, N >= 8, K % 64 == 0, r in {0, 16, ..., 128}.
+ * Y = act(sum_g sa sw S + xl1 L2 + bias), accumulated in fp32 and rounded
+ * once to bf16 (nearest even).
+ */
+int32_t svdq_w4a4_lr_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                          const float *sw, const float *xl1, const uint16_t *L2,
+                          const uint16_t *bias, int32_t act, int64_t M, int64_t N,
+                          int64_t K, int32_t r, uint16_t *Y, void *stream);
+
+/* Workspace bytes svdq_linear needs for a given shape (qa, sa, xl1 and the
+ * down-projection scratch, each 256-byte aligned). */
+size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t r);
+
+/*
+ * The whole layer: svdq_quantize_act_down then svdq_w4a4_lr_gemm on the same
+ * stream, with qa/sa/xl1 carved out of `workspace`
+ * (>= svdq_linear_workspace_bytes(M, K, r) bytes).  Arguments as above.
+ */
+int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                    const uint8_t *qw, const float *sw, const uint16_t *L2,
+                    const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                    int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Test hook: the exact per-group integer sums of a block, computed with the
+ * same operand unpacking and int8 matrix instructions as the GEMM.
+ *   S  device int32 [tm, tn, K/64]: S[i][j][g] = sum_{k in g} qa[m0+i][k] qw[n0+j][k]
+ * Requires 0 <= m0, m0 + tm <= M, 0 <= n0, n0 + tn <= N.
+ */
+int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
+                              int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
+                              int32_t *S, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -1,0 +1,61 @@
+"""Shared helpers of the GPU parity tests (host side only)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from synth import bf16_bits_to_f32
+
+DEV = "cuda:0"
+
+
+def to_dev(a: np.ndarray | None, dtype=None):
+    """numpy -> device tensor; uint16 bf16 bit patterns become torch.bfloat16."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return t if dtype is None else t.to(dtype)
+
+
+def bf16_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_f64(bits: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def y_tolerance(y_oracle_bits: np.ndarray, rms: float | None = None) -> np.ndarray:
+    """1 bf16 ulp of |y_oracle| + 1e-3 * rms(y_oracle)."""
+    yo = bf16_f64(y_oracle_bits)
+    if rms is None:
+        rms = float(np.sqrt(np.mean(yo ** 2))) if yo.size else 0.0
+    return oracle.bf16_ulp(yo) + 1e-3 * rms
+
+
+def assert_y_close(y_gpu_bits: np.ndarray, y_oracle_bits: np.ndarray, what: str = "Y",
+                   rms: float | None = None) -> float:
+    """Element-wise |y_gpu - y_oracle| <= tol; returns max |err| / tol."""
+    assert y_gpu_bits.shape == y_oracle_bits.shape
+    yg = bf16_f64(y_gpu_bits)
+    yo = bf16_f64(y_oracle_bits)
+    assert np.all(np.isfinite(yg)), "%s: non-finite GPU output" % what
+    tol = y_tolerance(y_oracle_bits, rms)
+    err = np.abs(yg - yo)
+    ratio = err / np.where(tol > 0, tol, 1e-300)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(ratio), ratio.shape)
+        raise AssertionError("%s: %d of %d outside tolerance; worst at %s: gpu %r oracle %r tol %r"
+                             % (what, int(bad.sum()), bad.size, i, yg[i], yo[i], tol[i]))
+    return float(ratio.max()) if ratio.size else 0.0
+
+
+def xl1_bound(xh: np.ndarray, L1_bits: np.ndarray) -> np.ndarray:
+    """|xl1_gpu - xl1_oracle| bound: (2^-15 + K 2^-24) * sum_k |xh_k L1_ki|."""
+    K = xh.shape[1]
+    mag = np.abs(xh.astype(np.float64)) @ np.abs(bf16_f64(L1_bits))
+    return (2.0 ** -15 + K * 2.0 ** -24) * mag + 1e-30

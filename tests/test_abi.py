@@ -1,0 +1,137 @@
+"""The C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments before touching a device (no compute calls here).
+
+The fake pointers below are never dereferenced: every call in this file
+fails argument validation, which runs before the device check and before
+any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_diffusion_transformer_amd as bdt
+from bit_diffusion_transformer_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, NODEV, HIPERR = range(7)
+A = 0x10000      # 16-byte aligned fake address (never dereferenced)
+U = 0x10008      # misaligned fake address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_0-9 ]+\**\s*\**(svdq_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = declared_functions()
+    assert len(decl) == 10, decl
+    assert sorted(_binding.EXPORTS) == decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert bdt.svdq_abi_version() == 1
+    assert bdt.svdq_status_string(0) == "ok"
+    assert bdt.svdq_status_string(MISALIGNED) == "misaligned pointer"
+    assert bdt.svdq_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    K, r, M = 3072, 32, 4608
+    down = lib.svdq_quantize_act_down_workspace_bytes(K, r)
+    assert down == 4 * K + 2 * 2 * K * r          # all 256-aligned here
+    assert lib.svdq_quantize_act_down_workspace_bytes(K, 0) == 4 * K
+    lin = lib.svdq_linear_workspace_bytes(M, K, r)
+    assert lin == M * K // 2 + M * (K // 64) * 4 + M * r * 4 + down
+    assert lib.svdq_linear_workspace_bytes(-1, K, r) == 0
+
+
+P = ctypes.c_void_p
+
+
+def _down(lib, X=A, lam=A, L1=A, M=16, K=128, r=16, qa=A, sa=A, xl1=A, ws=A, ws_bytes=1 << 20):
+    return lib.svdq_quantize_act_down(P(X), P(lam), P(L1), M, K, r, P(qa), P(sa), P(xl1),
+                                      P(ws), ws_bytes, None)
+
+
+def _gemm(lib, qa=A, sa=A, qw=A, sw=A, xl1=A, L2=A, bias=A, act=0, M=16, N=64, K=128, r=16, Y=A):
+    return lib.svdq_w4a4_lr_gemm(P(qa), P(sa), P(qw), P(sw), P(xl1), P(L2), P(bias), act,
+                                 M, N, K, r, P(Y), None)
+
+
+def _lin(lib, X=A, lam=A, L1=A, qw=A, sw=A, L2=A, bias=A, act=0, M=16, N=64, K=128, r=16, Y=A,
+         ws=A, ws_bytes=1 << 30):
+    return lib.svdq_linear(P(X), P(lam), P(L1), P(qw), P(sw), P(L2), P(bias), act, M, N, K, r,
+                           P(Y), P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), INVALID),
+    (dict(K=100), SHAPE), (dict(K=0), SHAPE), (dict(K=32), SHAPE),
+    (dict(r=8), SHAPE), (dict(r=-16), SHAPE), (dict(r=144), SHAPE),
+    (dict(X=0), INVALID), (dict(lam=0), INVALID), (dict(qa=0), INVALID), (dict(sa=0), INVALID),
+    (dict(L1=0), INVALID), (dict(xl1=0), INVALID),
+    (dict(r=0), INVALID),                      # L1/xl1 given although r == 0
+    (dict(X=U), MISALIGNED), (dict(sa=U), MISALIGNED), (dict(L1=U), MISALIGNED),
+    (dict(ws_bytes=16), WS_SMALL), (dict(ws=0), INVALID),
+])
+def test_quantize_act_down_rejects(lib, kw, code):
+    assert _down(lib, **kw) == code
+    assert lib.svdq_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-2), INVALID), (dict(act=2), INVALID), (dict(act=-1), INVALID),
+    (dict(N=60), SHAPE), (dict(N=0), SHAPE), (dict(K=96), SHAPE), (dict(r=24), SHAPE),
+    (dict(qa=0), INVALID), (dict(sw=0), INVALID), (dict(Y=0), INVALID),
+    (dict(xl1=0), INVALID), (dict(L2=0), INVALID), (dict(r=0), INVALID),
+    (dict(qw=U), MISALIGNED), (dict(Y=U), MISALIGNED), (dict(bias=U), MISALIGNED),
+])
+def test_gemm_rejects(lib, kw, code):
+    assert _gemm(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), INVALID), (dict(act=7), INVALID), (dict(N=12), SHAPE), (dict(K=65), SHAPE),
+    (dict(r=17), SHAPE), (dict(X=0), INVALID), (dict(qw=0), INVALID), (dict(L2=0), INVALID),
+    (dict(ws_bytes=1000), WS_SMALL), (dict(ws=0), INVALID), (dict(lam=U), MISALIGNED),
+])
+def test_linear_rejects(lib, kw, code):
+    assert _lin(lib, **kw) == code
+
+
+def test_pack_and_debug_reject(lib):
+    assert lib.svdq_pack_weights(P(A), -1, 128, P(A), P(A), None) == INVALID
+    assert lib.svdq_pack_weights(P(A), 8, 100, P(A), P(A), None) == SHAPE
+    assert lib.svdq_pack_weights(P(0), 8, 128, P(A), P(A), None) == INVALID
+    assert lib.svdq_pack_weights(P(A), 8, 128, P(U), P(A), None) == MISALIGNED
+    assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 128, 8, 0, 16, 16, P(A), None) == INVALID
+    assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 100, 0, 0, 16, 16, P(A), None) == SHAPE
+
+
+def test_empty_inputs_are_noops(lib):
+    # M == 0 (or N == 0 for packing) succeeds without touching any pointer.
+    assert _down(lib, X=0, lam=0, L1=0, qa=0, sa=0, xl1=0, ws=0, M=0) == OK
+    assert _gemm(lib, qa=0, sa=0, qw=0, sw=0, xl1=0, L2=0, bias=0, Y=0, M=0) == OK
+    assert _lin(lib, X=0, lam=0, L1=0, qw=0, sw=0, L2=0, bias=0, Y=0, ws=0, M=0) == OK
+    assert lib.svdq_pack_weights(P(0), 0, 128, P(0), P(0), None) == OK
+    assert lib.svdq_debug_group_sums(P(0), P(0), 16, 16, 128, 0, 0, 0, 5, P(0), None) == OK
+
+
+def test_refuses_without_a_gfx950_device(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the device check is exercised by the GPU tests")
+    assert _gemm(lib) == NODEV
+    assert "device" in lib.svdq_last_error().decode()

@@ -1,0 +1,103 @@
+"""GPU parity of every step of the layer against the CPU oracle.
+
+Bit-exact: packed codes, scales, per-group integer sums.  Tolerance: the
+bf16 output within 1 bf16 ulp of |y_oracle| + 1e-3 rms(y_oracle); the fp32
+down-projection within (2^-15 + K 2^-24) sum|xh L1| of the oracle's fp64.
+All calls go through the C ABI (bit_diffusion_transformer_amd -> libsvdq.so).
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_diffusion_transformer_amd as bdt
+import oracle
+from synth import LayerSpec, make_layer
+from tests.helpers import (assert_y_close, bf16_host, to_dev, xl1_bound)
+
+pytestmark = pytest.mark.gpu
+
+# (M, K, N, r, act, bias): tiles of 128 in M and N, stages of 4 groups in K,
+# ragged tails in every dimension, the extreme ranks, both activations.
+SHAPES = [
+    (256, 512, 512, 16, 0, True),
+    (77, 192, 264, 32, 1, True),
+    (1, 64, 8, 0, 0, False),
+    (130, 320, 136, 48, 1, False),
+    (300, 256, 256, 128, 0, True),
+    (33, 128, 1024, 64, 1, True),
+    (517, 1088, 392, 32, 0, True),
+]
+
+
+def _spec(M, K, N, r, act, bias, cid):
+    return LayerSpec("t%d" % cid, M, K, N, r, 0.01, 20.0, min(4, r) if r else 2, False,
+                     act=act, bias=bias, cfg_id=100 + cid)
+
+
+@pytest.fixture(scope="module", params=list(enumerate(SHAPES)),
+                ids=lambda p: "M%d_K%d_N%d_r%d_act%d_bias%d" % p[1])
+def case(request):
+    cid, (M, K, N, r, act, bias) = request.param
+    L = make_layer(_spec(M, K, N, r, act, bias, cid))
+    qa, sa, xh = oracle.quantize_act(L.X, L.lam)
+    qw, sw = oracle.pack_weights(L.R)
+    xl1 = oracle.down_proj(xh, L.L1) if r > 0 else None
+    return dict(L=L, M=M, K=K, N=N, r=r, act=act, qa=qa, sa=sa, xh=xh, qw=qw, sw=sw, xl1=xl1)
+
+
+def test_pack_weights_bit_exact(case):
+    qw, sw = bdt.pack_weights(to_dev(case["L"].R))
+    assert np.array_equal(qw.cpu().numpy(), case["qw"])
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), case["sw"].view(np.uint32))
+
+
+def test_quantize_act_down(case):
+    L, r = case["L"], case["r"]
+    qa, sa, xl1 = bdt.quantize_act_down(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None)
+    assert np.array_equal(qa.cpu().numpy(), case["qa"])
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), case["sa"].view(np.uint32))
+    if r:
+        got = xl1.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - case["xl1"]) <= xl1_bound(case["xh"], L.L1))
+    else:
+        assert xl1 is None
+
+
+def test_group_sums_bit_exact(case):
+    M, N, K = case["M"], case["N"], case["K"]
+    qa, qw = to_dev(case["qa"]), to_dev(case["qw"])
+    for (m0, tm, n0, tn) in [(0, M, 0, N), (M // 3, M - M // 3, N // 5, min(37, N - N // 5))]:
+        S = bdt.group_sums(qa, qw, m0, n0, tm, tn).cpu().numpy()
+        ref = oracle.group_sums(case["qa"], case["qw"], K, m0, n0, tm, tn)
+        assert np.array_equal(S, ref)
+
+
+def test_gemm_stagewise(case):
+    # Same inputs on both sides: the oracle's codes/scales and its xl1 in fp32.
+    L, r, K = case["L"], case["r"], case["K"]
+    xl1_32 = case["xl1"].astype(np.float32) if r else None
+    Y = bdt.w4a4_lr_gemm(to_dev(case["qa"]), to_dev(case["sa"]), to_dev(case["qw"]),
+                         to_dev(case["sw"]), to_dev(xl1_32), to_dev(L.L2) if r else None,
+                         to_dev(L.bias), case["act"])
+    _, y_or = oracle.gemm_rows(case["qa"], case["sa"], case["qw"], case["sw"],
+                               None if xl1_32 is None else xl1_32.astype(np.float64),
+                               L.L2, L.bias, case["act"], K)
+    assert_y_close(bf16_host(Y), y_or, "gemm")
+
+
+def test_linear_end_to_end(case):
+    L, r = case["L"], case["r"]
+    Y = bdt.linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
+                   to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
+    _, y_or = oracle.linear(L.X, L.lam, L.L1 if r else None, case["qw"], case["sw"],
+                            L.L2 if r else None, L.bias, case["act"])
+    assert_y_close(bf16_host(Y), y_or, "linear")
+
+
+def test_linear_is_deterministic(case):
+    L, r = case["L"], case["r"]
+    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
+            to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
+    y1 = bf16_host(bdt.linear(*args))
+    y2 = bf16_host(bdt.linear(*args))
+    assert np.array_equal(y1, y2)
