@@ -1,0 +1,238 @@
+"""Benchmark of the SVDQuant W4A4 + rank-r linear layer on one MI355X.
+
+One step = one call of svdq_linear (smoothing + quantization + down-projection
+kernel, then the W4A4 GEMM with the low-rank/bias/activation epilogue) on one
+batch of synthetic, seeded DiT-shaped inputs already resident in HBM.  The
+weights are packed once beforehand (offline, not timed).
+
+Prints one JSON line.  value = effective TOPS = 2 M N K / t_step.
+The roofline object describes the dominant kernel (the GEMM), timed with
+HIP events over its own timed loop on the stream it runs on; the
+cpu_baseline object times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+CACHE_BYTES = 256 << 20      # Infinity Cache; rotating input sets exceed 2x this
+METRIC = "effective TOPS (2MNK/t) of W4A4+rank-32 linear; % of INT8 MFMA / HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qkv", choices=["tiny", "qkv", "mlp_up", "mlp_down"])
+    ap.add_argument("--M", type=int, default=None, help="override the token count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def k1_bytes(M, K, r):
+    G = K // 64
+    return 2 * M * K + 4 * K + 2 * K * r + M * K // 2 + 4 * M * G + 4 * M * r
+
+
+def k2_bytes(M, N, K, r):
+    G = K // 64
+    return (M * K // 2 + 4 * M * G + N * K // 2 + 4 * N * G + 4 * M * r + 2 * r * N + 2 * N
+            + 2 * M * N)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the layer has no multi-GPU path in this build "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_diffusion_transformer_amd as bdt
+    from synth import CONFIGS, make_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    spec = CONFIGS[args.workload]
+    L = make_layer(spec, seed=0, M=args.M)
+    M, K, N, r, act = L.spec.M, L.spec.K, L.spec.N, L.spec.r, L.spec.act
+
+    def d(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base = dict(X=d(L.X), lam=d(L.lam), L1=d(L.L1), L2=d(L.L2), bias=d(L.bias))
+    qw, sw = bdt.pack_weights(d(L.R))
+    torch.cuda.synchronize()
+    base.update(qw=qw, sw=sw)
+    ws_bytes = bdt.svdq_linear_workspace_bytes(M, K, r)
+    set_bytes = (2 * M * K + qw.numel() + sw.numel() * 4 + 2 * M * N + ws_bytes
+                 + 4 * K + 2 * K * r + 2 * r * N + 2 * N)
+    nsets = max(2, int(np.ceil(2 * CACHE_BYTES / set_bytes)))
+    sets = []
+    for i in range(nsets):
+        s = {k: (v.clone() if v is not None else None) for k, v in base.items()}
+        s["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        sets.append(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    bits = bdt._bits
+
+    def step(s):
+        bdt.svdq_linear(bits(s["X"]), s["lam"], bits(s["L1"]) if r else None, s["qw"], s["sw"],
+                        bits(s["L2"]) if r else None, bits(s["bias"]), act, M, N, K, r,
+                        bits(s["Y"]), s["ws"], ws_bytes, stream)
+
+    # ---------------- timed region: exactly `steps` steps
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    ops = 2.0 * M * N * K
+    value = ops / t_step / 1e12
+
+    # ---------------- each kernel alone, HIP events on the stream they run on
+    carved = []
+    for s_ in sets:
+        carved.append(bdt.quantize_act_down(s_["X"], s_["lam"], s_["L1"] if r > 0 else None))
+        s_["ws_down"] = torch.empty(bdt.svdq_quantize_act_down_workspace_bytes(K, r),
+                                    dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    down_ws = bdt.svdq_quantize_act_down_workspace_bytes(K, r)
+
+    def quant(i):
+        s, (qa, sa, xl1) = sets[i % nsets], carved[i % nsets]
+        bdt.svdq_quantize_act_down(bits(s["X"]), s["lam"], bits(s["L1"]) if r else None, M, K, r,
+                                   qa, sa, xl1, s["ws_down"], down_ws, stream)
+
+    def gemm(i, rank):
+        s, (qa, sa, xl1) = sets[i % nsets], carved[i % nsets]
+        bdt.svdq_w4a4_lr_gemm(qa, sa, s["qw"], s["sw"], xl1 if rank else None,
+                              bits(s["L2"]) if rank else None, bits(s["bias"]), act, M, N, K,
+                              rank, bits(s["Y"]), stream)
+
+    def time_loop(fn, n):
+        for i in range(min(n, 5)):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    n_k = max(args.steps, 20)
+    t_gemm = time_loop(lambda i: gemm(i, r), n_k)
+    t_gemm_r0 = time_loop(lambda i: gemm(i, 0), n_k) if r > 0 else t_gemm
+
+    def linear_r0(i):
+        s = sets[i % nsets]
+        bdt.svdq_linear(bits(s["X"]), s["lam"], None, s["qw"], s["sw"], None, bits(s["bias"]),
+                        act, M, N, K, 0, bits(s["Y"]), s["ws"], ws_bytes, stream)
+
+    t_quant = time_loop(quant, n_k)
+    t_lin = time_loop(lambda i: step(sets[i % nsets]), n_k)
+    t_lin_r0 = time_loop(linear_r0, n_k) if r > 0 else t_lin
+    torch.cuda.synchronize()
+
+    gemm_tops = ops / t_gemm / 1e12
+    gemm_gbs = k2_bytes(M, N, K, r) / t_gemm / 1e9
+    bound_mfma = ops / (PEAK_INT8_TOPS * 1e12) >= k2_bytes(M, N, K, r) / (PEAK_HBM_GBS * 1e9)
+    if bound_mfma:
+        roof = {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "w4a4_lr_gemm_kernel"
+    roof["avg_launch_us"] = round(t_gemm * 1e6, 2)
+    roof["algorithmic_ops"] = ops
+    roof["algorithmic_bytes"] = k2_bytes(M, N, K, r)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
+        "config": {"workload": "%s: M=%d K=%d N=%d r=%d group=64 act=%s bias=%s"
+                               % (spec.name, M, K, N, r, "gelu" if act else "none",
+                                  L.bias is not None),
+                   "global_batch": M, "input_sets_rotated": nsets},
+        "roofline": roof,
+        "rank_branch_overhead": {
+            "gemm_r%d_us" % r: round(t_gemm * 1e6, 2), "gemm_r0_us": round(t_gemm_r0 * 1e6, 2),
+            "gemm_frac": round(t_gemm / t_gemm_r0 - 1, 4),
+            "linear_r%d_us" % r: round(t_lin * 1e6, 2), "linear_r0_us": round(t_lin_r0 * 1e6, 2),
+            "linear_frac": round(t_lin / t_lin_r0 - 1, 4)},
+        "quantize_act_down": {"us": round(t_quant * 1e6, 2),
+                              "algorithmic_bytes": k1_bytes(M, K, r),
+                              "GB/s": round(k1_bytes(M, K, r) / t_quant / 1e9, 1),
+                              "hbm_frac": round(k1_bytes(M, K, r) / t_quant / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(L, target_s):
+    """The CPU oracle on a bounded sample of the same layer (rows of X)."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    M, K, N, r, act = L.spec.M, L.spec.K, L.spec.N, L.spec.r, L.spec.act
+    qw, sw = oracle.pack_weights(L.R)             # offline, not timed
+
+    def run(rows):
+        X = np.ascontiguousarray(L.X[:rows])
+        t0 = time.perf_counter()
+        oracle.linear(X, L.lam, L.L1, qw, sw, L.L2, L.bias, act)
+        return time.perf_counter() - t0
+
+    rows = min(M, 16)
+    t = run(rows)
+    if t < target_s / 4 and rows < M:
+        rows = int(min(M, max(rows + 1, rows * target_s / max(t, 1e-3))))
+        t = run(rows)
+    tops = 2.0 * rows * N * K / t / 1e12
+    return {"value": round(tops, 5), "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": "first %d of %d token rows of the same layer (whole layer per row: "
+                      "smoothing, quantization, down-projection, W4A4 product, low-rank, "
+                      "bias, act), %.1f s" % (rows, M, t)}
+
+
+if __name__ == "__main__":
+    main()

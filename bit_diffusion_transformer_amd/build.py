@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # no packed fp32 (v_pk_*_f32) code generation
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in arch VGPRs: the rescale reads every result with VALU
+    # ops, and results in AGPRs would cost one v_accvgpr_read each
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]

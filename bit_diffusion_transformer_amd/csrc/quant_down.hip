@@ -42,7 +42,7 @@ prep_down_kernel(const float *__restrict__ lambda, const uint16_t *__restrict__ 
 // 8 consecutive k of row l % 16 in k-slot l / 16), with the transposed hi/lo
 // factor as the B operand; the partial products of the KW waves are summed
 // in LDS in wave order, so the result does not depend on scheduling.
-template <int KW>
+template <int KW, int NTMAX>
 __global__ void __launch_bounds__(64 * KW)
 quant_down_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_lam,
                   const uint16_t *__restrict__ l1_hi, const uint16_t *__restrict__ l1_lo,
@@ -61,17 +61,44 @@ quant_down_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_
     const int64_t g_end = G * (wave + 1) / KW;
     const int nt = r >> 4;
 
-    f32x4 acc[8];
+    f32x4 acc[NTMAX];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTMAX; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Software pipeline: the next group's X and 1/lambda are in flight while
+    // the current group is quantized; the current group's down-projection
+    // operands are issued before the quantizer math that hides their latency.
     const uint16_t *xrow = X + rowc * K;
+    u32x4 nxa = u32x4{0u, 0u, 0u, 0u}, nxb = nxa;
+    f32x4 ni0 = f32x4{0.f, 0.f, 0.f, 0.f}, ni1 = ni0, ni2 = ni0, ni3 = ni0;
+    if (g_begin < g_end) {
+        const int64_t k0 = g_begin * kGroup + 16 * ks;
+        nxa = *reinterpret_cast<const u32x4 *>(xrow + k0);
+        nxb = *reinterpret_cast<const u32x4 *>(xrow + k0 + 8);
+        const f32x4 *il4 = reinterpret_cast<const f32x4 *>(inv_lam + k0);
+        ni0 = il4[0]; ni1 = il4[1]; ni2 = il4[2]; ni3 = il4[3];
+    }
     for (int64_t g = g_begin; g < g_end; ++g) {
         const int64_t k0 = g * kGroup + 16 * ks;
-        const u32x4 xa = *reinterpret_cast<const u32x4 *>(xrow + k0);
-        const u32x4 xb = *reinterpret_cast<const u32x4 *>(xrow + k0 + 8);
-        const f32x4 *il4 = reinterpret_cast<const f32x4 *>(inv_lam + k0);
-        const f32x4 i0 = il4[0], i1 = il4[1], i2 = il4[2], i3 = il4[3];
+        const u32x4 xa = nxa, xb = nxb;
+        const f32x4 i0 = ni0, i1 = ni1, i2 = ni2, i3 = ni3;
+        if (g + 1 < g_end) {
+            nxa = *reinterpret_cast<const u32x4 *>(xrow + k0 + kGroup);
+            nxb = *reinterpret_cast<const u32x4 *>(xrow + k0 + kGroup + 8);
+            const f32x4 *il4 = reinterpret_cast<const f32x4 *>(inv_lam + k0 + kGroup);
+            ni0 = il4[0]; ni1 = il4[1]; ni2 = il4[2]; ni3 = il4[3];
+        }
+        u32x4 bh[NTMAX][2], bl[NTMAX][2];
+#pragma unroll
+        for (int t = 0; t < NTMAX; ++t) {
+            if (t < nt) {
+                const int64_t col = (int64_t)(16 * t + rl);
+                bh[t][0] = *reinterpret_cast<const u32x4 *>(l1_hi + col * K + k0);
+                bh[t][1] = *reinterpret_cast<const u32x4 *>(l1_hi + col * K + k0 + 8);
+                bl[t][0] = *reinterpret_cast<const u32x4 *>(l1_lo + col * K + k0);
+                bl[t][1] = *reinterpret_cast<const u32x4 *>(l1_lo + col * K + k0 + 8);
+            }
+        }
         float v[16];
         v[0] = bf16_lo(xa.x) * i0.x;  v[1] = bf16_hi(xa.x) * i0.y;
         v[2] = bf16_lo(xa.y) * i0.z;  v[3] = bf16_hi(xa.y) * i0.w;
@@ -88,17 +115,12 @@ quant_down_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_
             if (ks == 0) sa[row * G + g] = s;
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NTMAX; ++t) {
             if (t < nt) {
-                const int64_t col = (int64_t)(16 * t + rl);
-                const u32x4 h0 = *reinterpret_cast<const u32x4 *>(l1_hi + col * K + k0);
-                const u32x4 h1 = *reinterpret_cast<const u32x4 *>(l1_hi + col * K + k0 + 8);
-                const u32x4 o0 = *reinterpret_cast<const u32x4 *>(l1_lo + col * K + k0);
-                const u32x4 o1 = *reinterpret_cast<const u32x4 *>(l1_lo + col * K + k0 + 8);
-                acc[t] = mfma_bf16_16x16x32(xa, h0, acc[t]);
-                acc[t] = mfma_bf16_16x16x32(xa, o0, acc[t]);
-                acc[t] = mfma_bf16_16x16x32(xb, h1, acc[t]);
-                acc[t] = mfma_bf16_16x16x32(xb, o1, acc[t]);
+                acc[t] = mfma_bf16_16x16x32(xa, bh[t][0], acc[t]);
+                acc[t] = mfma_bf16_16x16x32(xa, bl[t][0], acc[t]);
+                acc[t] = mfma_bf16_16x16x32(xb, bh[t][1], acc[t]);
+                acc[t] = mfma_bf16_16x16x32(xb, bl[t][1], acc[t]);
             }
         }
     }
@@ -106,7 +128,7 @@ quant_down_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_
 
     // Partial XL1 of this wave: lane holds rows 4*ks + j, column 16 t + rl.
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NTMAX; ++t) {
         if (t < nt) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -179,15 +201,27 @@ hipError_t launch_quant_down(const uint16_t *X, int64_t M, int64_t K, int r,
     const int kw = choose_kw(M, K, r);
     const unsigned blocks = (unsigned)((M + 15) / 16);
     const size_t lds = (size_t)kw * 16 * (size_t)r * sizeof(float);
-#define SVDQ_K1(KWV)                                                                       \
-    case KWV:                                                                              \
-        quant_down_kernel<KWV><<<blocks, 64 * KWV, lds, stream>>>(                         \
-            X, ws.inv_lam, ws.l1_hi, ws.l1_lo, M, K, r, qa, sa, xl1);                      \
-        break;
-    switch (kw) {
-        SVDQ_K1(1) SVDQ_K1(2) SVDQ_K1(4) SVDQ_K1(8) SVDQ_K1(16)
-        default: return hipErrorInvalidValue;
+#define SVDQ_K1(KWV, NTM)                                                                  \
+    quant_down_kernel<KWV, NTM><<<blocks, 64 * KWV, lds, stream>>>(                        \
+        X, ws.inv_lam, ws.l1_hi, ws.l1_lo, M, K, r, qa, sa, xl1)
+#define SVDQ_K1_KW(NTM)                                                                    \
+    switch (kw) {                                                                          \
+        case 1: SVDQ_K1(1, NTM); break;                                                    \
+        case 2: SVDQ_K1(2, NTM); break;                                                    \
+        case 4: SVDQ_K1(4, NTM); break;                                                    \
+        case 8: SVDQ_K1(8, NTM); break;                                                    \
+        case 16: SVDQ_K1(16, NTM); break;                                                  \
+        default: return hipErrorInvalidValue;                                              \
     }
+    const int nt = r / 16;
+    if (nt <= 2) {
+        SVDQ_K1_KW(2)
+    } else if (nt <= 4) {
+        SVDQ_K1_KW(4)
+    } else {
+        SVDQ_K1_KW(8)
+    }
+#undef SVDQ_K1_KW
 #undef SVDQ_K1
     return hipGetLastError();
 }

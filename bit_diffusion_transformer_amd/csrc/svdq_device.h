@@ -46,6 +46,15 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 16x16 output tile, K = 16 bf16 per call (4 per lane: k-slot l / 16 holds
+// k = 4 (l / 16) .. + 3), fp32 accumulate; same output layout as above.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- 4-bit operands
 
 // Widen 16 packed two's-complement nibbles (two dwords, element 2j in the
