@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError,  # noqa: F401
+                       TILES_AUTO, TILES_FULL, TILES_QUARTER,
                        load_library, svdq_abi_version, svdq_debug_group_sums,
+                       svdq_debug_set_tile_policy,
                        svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
                        svdq_pack_weights, svdq_quantize_act_down,
                        svdq_quantize_act_down_workspace_bytes, svdq_status_string,

@@ -29,6 +29,7 @@ EXPORTS = (
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_pack_weights",
     "svdq_quantize_act_down_workspace_bytes", "svdq_quantize_act_down", "svdq_w4a4_lr_gemm",
     "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
+    "svdq_debug_set_tile_policy",
 )
 
 
@@ -64,6 +65,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_linear_workspace_bytes": ([I64, I64, I32], SZ),
         "svdq_linear": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, SZ, P], I32),
         "svdq_debug_group_sums": ([P, P, I64, I64, I64, I64, I64, I64, I64, P, P], I32),
+        "svdq_debug_set_tile_policy": ([I32], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -146,3 +148,10 @@ def svdq_debug_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S, stream=None):
     _check(load_library().svdq_debug_group_sums(
         _p(qa), _p(qw), M, N, K, m0, n0, tm, tn, _p(S), _stream(stream)),
         "svdq_debug_group_sums")
+
+
+TILES_AUTO, TILES_FULL, TILES_QUARTER = 0, 1, 2
+
+
+def svdq_debug_set_tile_policy(policy):
+    _check(load_library().svdq_debug_set_tile_policy(policy), "svdq_debug_set_tile_policy")

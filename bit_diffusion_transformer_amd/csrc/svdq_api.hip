@@ -299,3 +299,11 @@ int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, i
 }
 
 }  // extern "C"
+
+int32_t svdq_debug_set_tile_policy(int32_t policy) {
+    g_last_error[0] = 0;
+    if (policy != SVDQ_TILES_AUTO && policy != SVDQ_TILES_FULL && policy != SVDQ_TILES_QUARTER)
+        return fail(SVDQ_ERR_INVALID_ARG, "tile policy %d is not one of 0, 1, 2", (int)policy);
+    svdq::set_tile_policy(policy);
+    return SVDQ_OK;
+}

@@ -55,6 +55,30 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+typedef int   i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32 output tile, K = 32 int8 per call.  Lane l supplies, for row/column
+// l % 32, 16 int8 of k-slot l / 32; output element i of lane l is row
+// 8*(i/4) + 4*(l/32) + i%4, column l % 32.
+__device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b, i32x16 c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// 32x32 output tile, K = 8 bf16 per call (4 per lane, k-slot l / 32), fp32
+// accumulate; same output layout as the int8 instruction.
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x8(u32x2 a, u32x2 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// 32x32 output tile, K = 16 bf16 per call (8 per lane, k-slot l / 32), fp32
+// accumulate; same output layout.
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- 4-bit operands
 
 // Widen 16 packed two's-complement nibbles (two dwords, element 2j in the

@@ -41,6 +41,9 @@ hipError_t launch_quant_down(const uint16_t *X, int64_t M, int64_t K, int r,
                              hipStream_t stream);
 hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
                                hipStream_t stream);
+// 0 auto, 1 full tiles only, 2 quarter tiles only (process-wide test hook)
+void set_tile_policy(int policy);
+
 hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
                             const float *sw, const float *xl1, const uint16_t *L2,
                             const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,

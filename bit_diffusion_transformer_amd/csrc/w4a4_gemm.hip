@@ -9,19 +9,29 @@
 // output lane holds four consecutive n of one token row and stores them as
 // one 8-byte write.
 //
-// Per group of 64 along K and per 16 x 16 output block, the wave issues
-//   - one v_mfma_i32_16x16x64_i8 on the widened codes: S, exact int32;
-//   - one v_mfma_f32_16x16x16_bf16 that forms the scale products
+// Per group of 64 along K and per 32 x 32 output block the wave issues
+//   - two v_mfma_i32_32x32x32_i8 on the widened codes (the two k halves of
+//     the group, accumulated in the matrix unit): S, exact int32;
+//   - one v_mfma_f32_32x32x8_bf16 that forms the scale products
 //     P[n][m] = sw[n] sa[m] as an outer product of bf16 hi/lo pairs
 //     ((sw_hi + sw_lo)(sa_hi + sa_lo), exact bf16 products, fp32 sums,
 //     ~2^-16 relative to the fp32 product) in the same output layout;
-// and the VALU does only acc = fma(float(S), P, acc).  The rescale is the
-// VALU-bound part of the layer on this chip (one group of 64 MACs per
-// output against 3 VALU ops when the scale product is also formed on the
-// VALU), so moving the product onto the matrix unit, which has slack, leaves
-// two VALU ops per output and group.
+// and the VALU does only acc = fma(float(S), P, acc).  Formed on the VALU,
+// the scale product would be a third VALU op per output and group; the
+// rescale is what bounds this kernel on this chip (one group of 64 MACs per
+// output costs 1/16 of a 32x32x32 MFMA but 2 wave-wide VALU ops), so it is
+// kept to the minimum.
+//
+// Data movement: packed 4-bit codes and raw fp32 scales go from global
+// memory straight into a four-stage LDS ring with global_load_lds (no
+// registers, no LDS write instructions), up to three stages ahead of the one
+// being read; each wave reads its fragments with 16-byte LDS reads
+// (XOR-swizzled rows, no bank conflicts) and widens the codes to int8 in
+// registers.
 #include "svdq_device.h"
 #include "svdq_internal.h"
+
+#include <atomic>
 
 #define SVDQ_MAX_RANK_DEV 128
 
@@ -29,311 +39,411 @@ namespace svdq {
 
 namespace {
 
-constexpr int BN = 128;            // tile rows in n (weights)
-constexpr int BM = 128;            // tile cols in m (tokens)
-constexpr int GC = 2;              // K groups per LDS stage
-constexpr int ROWP = GC * 32;      // packed bytes of one row per stage
-constexpr int ASTR = ROWP + 8;     // LDS row stride: 72 B = 18 banks, so the 16
-                                   // rows read by one 16-lane phase hit distinct banks
-constexpr int NBUF = 3;            // LDS stages in flight
-constexpr int NTHR = 256;          // 4 waves, 2 (n) x 2 (m), 64 x 64 each
+// Tiles are BT x BT outputs with BT = 64 WB, four waves in a 2 x 2 grid,
+// each wave WB x WB blocks of 32 x 32.  WB = 2 (128 x 128 tiles) is the main
+// shape; WB = 1 (64 x 64 quarter tiles) serves the tiles of a partial last
+// round, so that they spread over four times as many workgroups.
+constexpr int GC = 2;              // K groups per stage
+constexpr int ROWP = GC * 32;      // packed bytes of one row per stage (4 x 16)
+constexpr int NBUF = 4;            // stages in the LDS ring
+constexpr int NTHR = 256;          // 4 waves
+constexpr int TILE = 128;          // the tile grid (a quarter tile is a quadrant of one)
 constexpr int GROUP_M = 8;         // m-tiles per raster group (L2 reuse of weights)
 
-// LDS.  Codes stay packed (4 bit) in LDS and are widened to int8 in
-// registers by each wave.  Three stage buffers rotate: one being computed,
-// one already published (the next group's fragments are read from it while
-// the current group computes), one being filled from registers.
-// Scale operands: per (group, row) one 8-byte bf16 quadruple, weights as
-// (hi, hi, lo, lo), activations as (hi, lo, hi, lo); lanes of k-slots 1..3
-// read the activation side from `zero`, so only k-slot 0 contributes.
+template <int WB>
+struct Cfg {
+    static constexpr int BT = 64 * WB;
+    static constexpr int NB = WB * WB;                 // blocks per wave
+    // One stage in LDS: codes of the BT weight rows, then of the BT token
+    // rows (64 bytes per row; 16-byte segment s of tile row R sits at slot
+    // s ^ swz(R)), then the raw fp32 scales [row][group] of both.
+    static constexpr int A_OFF = 0;
+    static constexpr int B_OFF = A_OFF + BT * ROWP;
+    static constexpr int SA_OFF = B_OFF + BT * ROWP;
+    static constexpr int SB_OFF = SA_OFF + BT * GC * 4;
+    static constexpr int STAGE = SB_OFF + BT * GC * 4;
+    // global_load_lds instructions per wave per stage: WB code transfers per
+    // operand, and one scale transfer per operand (WB = 2) or one in total
+    static constexpr int LOADS = 2 * WB + (WB == 2 ? 2 : 1);
+};
+
+// Row swizzle of the 16-byte segments.  A 16-byte LDS read by 8 consecutive
+// lanes (rows R..R+7 of one segment) or by 16 consecutive lanes touches 8
+// (16) distinct 16-byte bank groups of 128 (256) bytes with this mapping.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+template <int WB>
 struct __align__(16) Smem {
     union {
-        struct {
-            uint8_t a[NBUF][BN * ASTR];
-            uint8_t b[NBUF][BM * ASTR];
-        } t;
-        uint16_t l2t[BN * (SVDQ_MAX_RANK_DEV + 8)];
+        uint8_t ring[NBUF][Cfg<WB>::STAGE];
+        uint16_t l2t[Cfg<WB>::BT * (SVDQ_MAX_RANK_DEV + 8)];
     } u;
-    u32x2 swop[NBUF][GC][BN];
-    u32x2 saop[NBUF][GC][BM];
-    u32x2 zero[64];
 };
-static_assert(sizeof(Smem) <= 80 * 1024, "two workgroups per CU");
+static_assert(sizeof(Smem<2>) <= 80 * 1024, "two workgroups per CU");
 
-// Per-thread, loop-invariant offsets of the global -> LDS copy.
-struct CopyPlan {
-    int voff[2];        // byte offsets of this thread's two 16-byte pieces (rows clamped)
-    int voff_tail[2];   // same for a stage holding one group: the second group re-reads the first
-    int soff;           // element offset of this thread's scale row (times G)
-    int lds_off[2];     // LDS byte offsets (row * ASTR + seg) of the two pieces
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-struct StageRegs {
-    u32x4 a[2];
-    u32x4 b[2];
-    float s[GC];
-};
-
-// Global -> registers for stage c; every address is in bounds (see CopyPlan).
-__device__ __forceinline__ void load_stage(StageRegs &st, const CopyPlan &cp,
-                                           const uint8_t *__restrict__ qw0,
-                                           const uint8_t *__restrict__ qa0,
-                                           const float *__restrict__ s0, int G, int c,
-                                           bool partial) {
-    const uint8_t *qws = qw0 + c * ROWP;
-    const uint8_t *qas = qa0 + c * ROWP;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int off = partial ? cp.voff_tail[i] : cp.voff[i];
-        st.a[i] = *reinterpret_cast<const u32x4 *>(qws + off);
-        st.b[i] = *reinterpret_cast<const u32x4 *>(qas + off);
-    }
-    const float *ss = s0 + c * GC;
-    st.s[0] = ss[cp.soff];
-    st.s[1] = partial ? st.s[0] : ss[cp.soff + 1];
-    (void)G;
-}
-
-// Registers -> LDS buffer `buf` for a stage with `gvalid` (1 or 2) groups;
-// the scales of a missing group are zero, so that group adds exactly zero.
-__device__ __forceinline__ void store_stage(const StageRegs &st, const CopyPlan &cp, Smem &sm,
-                                            int buf, int gvalid) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        u32x2 *pa = reinterpret_cast<u32x2 *>(&sm.u.t.a[buf][cp.lds_off[i]]);
-        u32x2 *pb = reinterpret_cast<u32x2 *>(&sm.u.t.b[buf][cp.lds_off[i]]);
-        pa[0] = u32x2{st.a[i].x, st.a[i].y};
-        pa[1] = u32x2{st.a[i].z, st.a[i].w};
-        pb[0] = u32x2{st.b[i].x, st.b[i].y};
-        pb[1] = u32x2{st.b[i].z, st.b[i].w};
-    }
-    // The weight scale carries the 2^-8 that undoes the x16 of both widened
-    // operands (a power-of-two scaling, exact).
-    if (tid < BN) {
-#pragma unroll
-        for (int gi = 0; gi < GC; ++gi) {
-            const float v = gi < gvalid ? st.s[gi] * 0.00390625f : 0.0f;
-            const uint32_t h = pack_bf16x2(v, v);
-            const uint32_t l = pack_bf16x2(v - bf16_lo(h), v - bf16_lo(h));
-            sm.swop[buf][gi][tid] = u32x2{h, l};
-        }
-    } else {
-#pragma unroll
-        for (int gi = 0; gi < GC; ++gi) {
-            const float v = gi < gvalid ? st.s[gi] : 0.0f;
-            const uint32_t h = pack_bf16x2(v, 0.0f);
-            const uint32_t hl = pack_bf16x2(v, v - bf16_lo(h));
-            sm.saop[buf][gi][tid - BN] = u32x2{hl, hl};
-        }
-    }
-}
-
-__device__ __forceinline__ void tile_coords(int64_t M, int64_t N, int64_t &tm, int64_t &tn) {
-    const int64_t nbm = (M + BM - 1) / BM;
-    const int64_t nbn = (N + BN - 1) / BN;
-    const int64_t total = nbm * nbn;
-    int64_t b = blockIdx.x;
-    // Consecutive workgroups go to different XCDs (round robin over 8); give
-    // each XCD a contiguous range of tiles so the tiles sharing operands share
-    // that XCD's L2.
-    if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
+// Linear tile index -> (tm, tn) on the 128 x 128 grid: GROUP_M m-tiles per
+// raster group, so that consecutive tiles share weight rows in L2.
+__device__ __forceinline__ void raster(int64_t id, int64_t nbm, int64_t nbn, int64_t &tm,
+                                       int64_t &tn) {
     const int64_t per_group = (int64_t)GROUP_M * nbn;
-    const int64_t grp = b / per_group;
+    const int64_t grp = id / per_group;
     const int64_t first_m = grp * GROUP_M;
     const int64_t gsize = (nbm - first_m) < GROUP_M ? (nbm - first_m) : GROUP_M;
-    const int64_t in_grp = b - grp * per_group;
+    const int64_t in_grp = id - grp * per_group;
     tm = first_m + in_grp % gsize;
     tn = in_grp / gsize;
 }
 
-// Fragments of one group for the wave's 64 x 64 tile: widened codes of the
-// four 16-row blocks of A (weights) and B (tokens), and the scale operands.
-struct Frags {
-    i32x4 A[4], B[4];
-    u32x2 AS[4], BS[4];
+// Loop-invariant plan of one wave's global -> LDS copies of a stage.  Code
+// transfers: 1 KB each, lane l carries row 16 WB w + 16 i + l / 4 of its
+// operand into LDS slot l % 4.  Scale transfers: 256 bytes, lane l carries
+// row 32 j + l / 2, group l % 2 (WB = 2: block j = w of both operands;
+// WB = 1: waves 0, 1 the weight rows, waves 2, 3 the token rows).  Rows past
+// the matrix re-read its last row (never stored); a stage that holds only
+// one group (odd group count) re-reads that group for the second.  Offsets
+// are unsigned bytes from the tile's first row, so each copy is a uniform
+// (scalar) base plus a per-lane 32-bit offset.
+template <int WB>
+struct CopyPlan {
+    uint32_t a_off[WB], b_off[WB];   // code transfers
+    uint32_t a_tail[WB], b_tail[WB]; // same for a one-group stage
+    uint32_t s_off[2], s_tail[2];    // scale transfers (weights, tokens)
+    int wave;                        // wave index (uniform)
 };
 
-// Per-lane, loop-invariant LDS offsets of the fragment reads.
-struct ReadPlan {
-    int a_off, b_off;     // byte offsets into sm.u.t.a[0] / .b[0]
-    int as_off;           // element offset into sm.swop[0][0]
-    int bs_off, bs_step;  // element offset into sm.saop (or the zero row), and 1 / 0
+struct Operands {
+    const uint8_t *qw0, *qa0;      // first row of the tile
+    const uint8_t *sw0, *sa0;      // (scales, as bytes)
 };
 
-__device__ __forceinline__ void load_frags(Frags &f, const Smem &sm, const ReadPlan &rp,
-                                           int buf, int gi) {
-    const uint8_t *abase = &sm.u.t.a[buf][rp.a_off + gi * 32];
-    const uint8_t *bbase = &sm.u.t.b[buf][rp.b_off + gi * 32];
-    const u32x2 *asc = &sm.swop[buf][gi][rp.as_off];
-    // k-slot 0 lanes read the activation scale operands, the others a zero row
-    const u32x2 *bsc = &sm.saop[0][0][0] + rp.bs_off + rp.bs_step * ((buf * GC + gi) * BM);
+template <int WB>
+__device__ __forceinline__ void issue_copies(uint8_t *st, const Operands &op, int c, int wave,
+                                             const uint32_t (&ao)[WB], const uint32_t (&bo)[WB],
+                                             const uint32_t (&so)[2]) {
+    using C = Cfg<WB>;
+    const uint8_t *qws = op.qw0 + c * ROWP;
+    const uint8_t *qas = op.qa0 + c * ROWP;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f.A[i] = widen_nibbles(*reinterpret_cast<const u32x2 *>(abase + i * 16 * ASTR));
-        f.B[i] = widen_nibbles(*reinterpret_cast<const u32x2 *>(bbase + i * 16 * ASTR));
-        f.AS[i] = asc[16 * i];
-        f.BS[i] = bsc[16 * i];
+    for (int i = 0; i < WB; ++i) {
+        const int row = 16 * WB * wave + 16 * i;
+        __builtin_amdgcn_global_load_lds(qws + ao[i], (lds_void *)(st + C::A_OFF + row * ROWP), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qas + bo[i], (lds_void *)(st + C::B_OFF + row * ROWP), 16, 0, 0);
+    }
+    if (WB == 2) {
+        __builtin_amdgcn_global_load_lds(op.sw0 + c * GC * 4 + so[0],
+                                         (lds_void *)(st + C::SA_OFF + 32 * wave * GC * 4), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(op.sa0 + c * GC * 4 + so[1],
+                                         (lds_void *)(st + C::SB_OFF + 32 * wave * GC * 4), 4, 0, 0);
+    } else if (wave < 2) {
+        __builtin_amdgcn_global_load_lds(op.sw0 + c * GC * 4 + so[0],
+                                         (lds_void *)(st + C::SA_OFF + 32 * wave * GC * 4), 4, 0, 0);
+    } else {
+        __builtin_amdgcn_global_load_lds(op.sa0 + c * GC * 4 + so[1],
+                                         (lds_void *)(st + C::SB_OFF + 32 * (wave - 2) * GC * 4), 4, 0, 0);
     }
 }
 
-// One group for the wave's 16 blocks: the MFMAs of block t + 2 are issued
-// before the VALU converts and accumulates block t, so the matrix unit and
-// the VALU overlap within the wave.
-__device__ __forceinline__ void group_compute(f32x4 (&acc)[4][4], const Frags &f) {
-    i32x4 S[3];
-    f32x4 P[3];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        S[t] = mfma_i8_16x16x64(f.A[t >> 2], f.B[t & 3], i32x4{0, 0, 0, 0});
-        P[t] = mfma_bf16_16x16x16(f.AS[t >> 2], f.BS[t & 3], f32x4{0.f, 0.f, 0.f, 0.f});
+template <int WB>
+__device__ __forceinline__ void issue_stage(uint8_t *st, const CopyPlan<WB> &cp,
+                                            const Operands &op, int c, bool one_group) {
+    if (one_group)
+        issue_copies<WB>(st, op, c, cp.wave, cp.a_tail, cp.b_tail, cp.s_tail);
+    else
+        issue_copies<WB>(st, op, c, cp.wave, cp.a_off, cp.b_off, cp.s_off);
+}
+
+// Wait until at most `n` stages of this wave's copies are in flight (in the
+// main loop the only outstanding vector-memory instructions are these) and
+// this wave's LDS reads have returned (the barrier that follows releases the
+// buffer they read for refilling).
+template <int L>
+__device__ __forceinline__ void wait_stages(int n) {
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    constexpr int kNoExp = (0x7 << 4);
+    constexpr int v1 = L, v2 = 2 * L, v3 = 3 * L;
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(kNoExp); break;
+    case 1: __builtin_amdgcn_s_waitcnt((v1 & 0xF) | ((v1 >> 4) << 14) | kNoExp); break;
+    case 2: __builtin_amdgcn_s_waitcnt((v2 & 0xF) | ((v2 >> 4) << 14) | kNoExp); break;
+    default: __builtin_amdgcn_s_waitcnt((v3 & 0xF) | ((v3 >> 4) << 14) | kNoExp); break;
     }
+}
+
+// Workgroup barrier without a memory fence: the copies of the other stages
+// stay in flight across it.  The clobber keeps the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Loop-invariant LDS offsets of one lane's fragment reads.
+struct ReadPlan {
+    int a_code[GC], b_code[GC];    // block 0; block j is 32 j rows further
+    int a_scale, b_scale;          // group 0 of block 0
+    bool keep_b;                   // k-slot 0 lanes carry the token scale
+};
+
+template <int WB>
+struct Raw {
+    u32x4 a[WB], b[WB];
+    float sa[WB], sb[WB];
+};
+template <int WB>
+struct Frags {
+    i32x4 A[WB][2], B[WB][2];      // [block][k half]
+    u32x2 AS[WB], BS[WB];
+};
+
+template <int WB>
+__device__ __forceinline__ void read_raw(Raw<WB> &rw, const uint8_t *st, const ReadPlan &rp,
+                                         int gi) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const int bi = t >> 2, bj = t & 3;
-        if (t + 2 < 16) {
-            const int u = t + 2;
-            S[u % 3] = mfma_i8_16x16x64(f.A[u >> 2], f.B[u & 3], i32x4{0, 0, 0, 0});
-            P[u % 3] = mfma_bf16_16x16x16(f.AS[u >> 2], f.BS[u & 3], f32x4{0.f, 0.f, 0.f, 0.f});
-        }
+    for (int blk = 0; blk < WB; ++blk) {
+        rw.a[blk] = *reinterpret_cast<const u32x4 *>(st + rp.a_code[gi] + blk * 32 * ROWP);
+        rw.b[blk] = *reinterpret_cast<const u32x4 *>(st + rp.b_code[gi] + blk * 32 * ROWP);
+        rw.sa[blk] = *reinterpret_cast<const float *>(st + rp.a_scale + blk * 32 * GC * 4 + 4 * gi);
+        rw.sb[blk] = *reinterpret_cast<const float *>(st + rp.b_scale + blk * 32 * GC * 4 + 4 * gi);
+    }
+}
+
+// Widen the codes and build the scale operands.  A lane holds 32 codes of
+// its row: k half h of the group takes codes [16 h, 16 h + 16) of them in
+// both operands, so the pairing of k is the same on both sides.  Weight scale
+// operand: bf16 (hi, hi, lo, lo) of sw * 2^-8 (the 2^-8 undoes the x16 of
+// both widened operands; exact).  Token operand: (hi, lo, hi, lo) of sa on
+// k-slot 0 lanes and zero elsewhere; `keep` false also zeroes a group past K,
+// which then adds exactly nothing.
+template <int WB>
+__device__ __forceinline__ void make_frags(Frags<WB> &f, const Raw<WB> &rw, bool keep) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[bi][bj][j] = __builtin_fmaf((float)S[t % 3][j], P[t % 3][j], acc[bi][bj][j]);
-        // Keep the issue order (at most three blocks of results live): the
-        // empty asm pins the updated accumulator to this point so later
-        // passes cannot sink the VALU work below the following MFMAs.
-        asm volatile("" : "+v"(acc[bi][bj]));
+    for (int blk = 0; blk < WB; ++blk) {
+        f.A[blk][0] = widen_nibbles(u32x2{rw.a[blk].x, rw.a[blk].y});
+        f.A[blk][1] = widen_nibbles(u32x2{rw.a[blk].z, rw.a[blk].w});
+        f.B[blk][0] = widen_nibbles(u32x2{rw.b[blk].x, rw.b[blk].y});
+        f.B[blk][1] = widen_nibbles(u32x2{rw.b[blk].z, rw.b[blk].w});
+        const float va = rw.sa[blk] * 0.00390625f;
+        const uint32_t ha = pack_bf16x2(va, va);
+        const float la = va - bf16_lo(ha);
+        f.AS[blk] = u32x2{ha, pack_bf16x2(la, la)};
+        const float vb = keep ? rw.sb[blk] : 0.0f;
+        const uint32_t hb = pack_bf16x2(vb, 0.0f);
+        const uint32_t hl = pack_bf16x2(vb, vb - bf16_lo(hb));
+        f.BS[blk] = u32x2{hl, hl};
+    }
+}
+
+// The MFMA -> VALU pipeline of a wave.  The blocks of the two groups of a
+// stage form one stream j = 0 .. 2 NB - 1 (block j % NB, result slot j & 1):
+// the three MFMAs of block j go out while the VALU converts and accumulates
+// block j - 1, so the matrix unit and the VALU work side by side, also
+// across the group boundary.
+struct Pipe {
+    i32x16 S[2];
+    f32x16 P[2];
+};
+
+template <int WB>
+__device__ __forceinline__ void issue_block(Pipe &p, const Frags<WB> &f, int t, int k) {
+    const int bi = t / WB, bj = t % WB;
+    p.S[k] = mfma_i8_32x32x32(f.A[bi][0], f.B[bj][0], i32x16{});
+    p.S[k] = mfma_i8_32x32x32(f.A[bi][1], f.B[bj][1], p.S[k]);
+    p.P[k] = mfma_bf16_32x32x8(f.AS[bi], f.BS[bj], f32x16{});
+}
+
+template <int NB>
+__device__ __forceinline__ void valu_block(f32x16 (&acc)[NB], const Pipe &p, int t, int k) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        acc[t][i] = __builtin_fmaf((float)p.S[k][i], p.P[k][i], acc[t][i]);
+}
+
+// Issue stream element j while the VALU finishes element j - 1: one MFMA,
+// then about a third of the VALU work, three times.  The empty asm pins the
+// updated accumulator so later passes cannot sink the VALU work below the
+// following MFMAs.
+template <int WB>
+__device__ __forceinline__ void pair(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f, int j) {
+    constexpr int NB = WB * WB;
+    issue_block<WB>(p, f, j % NB, j & 1);
+    valu_block<NB>(acc, p, (j - 1) % NB, (j - 1) & 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+    asm volatile("" : "+v"(acc[(j - 1) % NB]));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int WB>
+__device__ __forceinline__ void group_first(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f) {
+    issue_block<WB>(p, f, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 1; j < WB * WB; ++j) pair<WB>(acc, p, f, j);
+}
+template <int WB>
+__device__ __forceinline__ void group_second(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f) {
+#pragma unroll
+    for (int j = WB * WB; j < 2 * WB * WB; ++j) pair<WB>(acc, p, f, j);
+}
+template <int WB>
+__device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p) {
+    constexpr int NB = WB * WB;
+    valu_block<NB>(acc, p, NB - 1, 1);
+    asm volatile("" : "+v"(acc[NB - 1]));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The K loop.  The four ring buffers are separate restrict pointers so that
+// the compiler can tell a read of one stage from the copies still landing in
+// the others (otherwise every LDS read would wait for all copies).
+template <int WB>
+__device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__restrict__ b1,
+                                       uint8_t *__restrict__ b2, uint8_t *__restrict__ b3,
+                                       const CopyPlan<WB> &cp, const ReadPlan &rp,
+                                       const Operands &op, int ns, bool odd,
+                                       f32x16 (&acc)[WB * WB]) {
+    constexpr int L = Cfg<WB>::LOADS;
+    // prologue: stages 0..3 in flight, stage 0 visible, group 0 in registers
+    issue_stage<WB>(b0, cp, op, 0, odd && ns == 1);
+    if (ns > 1) issue_stage<WB>(b1, cp, op, 1, odd && ns == 2);
+    if (ns > 2) issue_stage<WB>(b2, cp, op, 2, odd && ns == 3);
+    if (ns > 3) issue_stage<WB>(b3, cp, op, 3, odd && ns == 4);
+    wait_stages<L>(ns < 4 ? ns - 1 : 3);
+    barrier();
+    Raw<WB> raw;
+    Frags<WB> f;
+    read_raw<WB>(raw, b0, rp, 0);
+    make_frags<WB>(f, raw, rp.keep_b);
+
+    // Stage s: group 2s computes while group 2s + 1 is read; then stage
+    // s + 1 is published and stage s's buffer (read by every wave before
+    // the barrier) is refilled with stage s + 4; group 2s + 1 computes
+    // while the first group of stage s + 1 is read.
+    auto step = [&](int s, uint8_t *cur, uint8_t *nxt) {
+        Pipe p;
+        read_raw<WB>(raw, cur, rp, 1);
         __builtin_amdgcn_sched_barrier(0);
+        group_first<WB>(acc, p, f);
+        make_frags<WB>(f, raw, rp.keep_b && !(odd && s == ns - 1));
+        wait_stages<L>(s + 1 < ns ? (ns - 2 - s < 2 ? ns - 2 - s : 2) : 0);
+        barrier();
+        if (s + 4 < ns) issue_stage<WB>(cur, cp, op, s + 4, odd && s + 4 == ns - 1);
+        // (after the last stage this reads a stale, unused buffer: no branch,
+        // so the fragments carry no merge of old and new values)
+        read_raw<WB>(raw, nxt, rp, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        group_second<WB>(acc, p, f);
+        make_frags<WB>(f, raw, rp.keep_b);
+        group_drain<WB>(acc, p);
+    };
+    for (int s = 0; s < ns; s += 4) {
+        step(s, b0, b1);
+        if (s + 1 >= ns) break;
+        step(s + 1, b1, b2);
+        if (s + 2 >= ns) break;
+        step(s + 2, b2, b3);
+        if (s + 3 >= ns) break;
+        step(s + 3, b3, b0);
     }
 }
 
 }  // namespace
 
+// Tile `tile0 + blockIdx.x` (WB = 2, with the XCD-aware order when `xcd`) or
+// quarter blockIdx.x % 4 of tile `tile0 + blockIdx.x / 4` (WB = 1) of the
+// 128 x 128 tile grid.
+template <int WB>
 __global__ void __launch_bounds__(NTHR)
 w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
                     const uint8_t *__restrict__ qw, const float *__restrict__ sw,
                     const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
                     const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N,
-                    int64_t K, int r, uint16_t *__restrict__ Y) {
-    __shared__ Smem sm;
-    int64_t tm, tn;
-    tile_coords(M, N, tm, tn);
-    const int64_t m0 = tm * BM, n0 = tn * BN;
+                    int64_t K, int r, uint16_t *__restrict__ Y, int64_t tile0, int64_t ntiles) {
+    using C = Cfg<WB>;
+    constexpr int BT = C::BT, NB = C::NB;
+    __shared__ Smem<WB> sm;
+    const int64_t nbm = (M + TILE - 1) / TILE, nbn = (N + TILE - 1) / TILE;
+    int64_t m0, n0;
+    {
+        int64_t b = blockIdx.x, tm, tn;
+        if (WB == 2) {
+            // Consecutive workgroups go to different XCDs (round robin over
+            // 8); give each XCD a contiguous range of tiles so the tiles
+            // sharing operands share that XCD's L2.
+            if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
+            raster(tile0 + b, nbm, nbn, tm, tn);
+            m0 = tm * TILE;
+            n0 = tn * TILE;
+        } else {
+            raster(tile0 + b / 4, nbm, nbn, tm, tn);
+            m0 = tm * TILE + 64 * (b & 1);
+            n0 = tn * TILE + 64 * ((b >> 1) & 1);
+            if (m0 >= M || n0 >= N) return;   // quadrant outside a ragged edge
+        }
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wn = wave >> 1, wm = wave & 1;
-    const int rl = lane & 15, ks = lane >> 4;
+    const int r32 = lane & 31, ks2 = lane >> 5;
     const int G = (int)(K / kGroup);
     const int kb = (int)(K / 2);
     const int ns = (G + GC - 1) / GC;          // stages; only the last may hold one group
-    const int glast = G - (ns - 1) * GC;       // groups in the last stage (1 or 2)
-    const int nlast = (int)((N - n0 < BN ? N - n0 : BN) - 1);
-    const int mlast = (int)((M - m0 < BM ? M - m0 : BM) - 1);
+    const bool odd = (G & 1) != 0;
+    const int nlast = (int)((N - n0 < BT ? N - n0 : BT) - 1);
+    const int mlast = (int)((M - m0 < BT ? M - m0 : BT) - 1);
 
-    if (tid < 64) sm.zero[tid] = u32x2{0u, 0u};
+    Operands op;
+    op.qw0 = qw + n0 * (int64_t)kb;
+    op.qa0 = qa + m0 * (int64_t)kb;
+    op.sw0 = reinterpret_cast<const uint8_t *>(sw + n0 * (int64_t)G);
+    op.sa0 = reinterpret_cast<const uint8_t *>(sa + m0 * (int64_t)G);
 
-    // Loop-invariant offsets.
-    CopyPlan cp;
+    CopyPlan<WB> cp;
+    cp.wave = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = tid + NTHR * i;
-        const int row = q >> 2;
-        const int part = q & 3;
-        const int seg = part * 16;
-        // the weight and token tiles share the same per-thread layout; rows
-        // past the end are clamped (weights to nlast, tokens to mlast) by
-        // using the larger tile bound below for both and clamping each
-        cp.lds_off[i] = row * ASTR + seg;
-        cp.voff[i] = seg;               // row part added below per operand
-        cp.voff_tail[i] = part >= 2 ? seg - 32 : seg;
+    for (int i = 0; i < WB; ++i) {
+        const int row = 16 * WB * wave + 16 * i + (lane >> 2);
+        const int seg = (lane & 3) ^ swz(row);     // global segment landing in this lane's slot
+        const int ra = min(row, nlast), rb = min(row, mlast);
+        cp.a_off[i] = (uint32_t)(ra * kb + 16 * seg);
+        cp.b_off[i] = (uint32_t)(rb * kb + 16 * seg);
+        cp.a_tail[i] = (uint32_t)(ra * kb + 16 * (seg & 1));
+        cp.b_tail[i] = (uint32_t)(rb * kb + 16 * (seg & 1));
     }
-    // Operand base pointers at the tile's first row; each thread's row offset
-    // is folded into per-operand offsets (rows clamped separately).
-    const int q0 = tid, q1 = tid + NTHR;
-    const int rowa0 = min(q0 >> 2, nlast), rowa1 = min(q1 >> 2, nlast);
-    const int rowb0 = min(q0 >> 2, mlast), rowb1 = min(q1 >> 2, mlast);
-    CopyPlan cpa = cp, cpb = cp;
-    cpa.voff[0] += rowa0 * kb; cpa.voff[1] += rowa1 * kb;
-    cpa.voff_tail[0] += rowa0 * kb; cpa.voff_tail[1] += rowa1 * kb;
-    cpb.voff[0] += rowb0 * kb; cpb.voff[1] += rowb1 * kb;
-    cpb.voff_tail[0] += rowb0 * kb; cpb.voff_tail[1] += rowb1 * kb;
-    const bool is_w = tid < BN;
-    cp.soff = (is_w ? min(tid, nlast) : min(tid - BN, mlast)) * G;
-    const float *s0 = is_w ? sw + n0 * (int64_t)G : sa + m0 * (int64_t)G;
-    const uint8_t *qw0 = qw + n0 * (int64_t)kb;
-    const uint8_t *qa0 = qa + m0 * (int64_t)kb;
+    {
+        const int blk = WB == 2 ? wave : (wave & 1);
+        const int row = 32 * blk + (lane >> 1);
+        const int g = lane & 1;
+        cp.s_off[0] = (uint32_t)(4 * (min(row, nlast) * G + g));
+        cp.s_off[1] = (uint32_t)(4 * (min(row, mlast) * G + g));
+        cp.s_tail[0] = (uint32_t)(4 * min(row, nlast) * G);
+        cp.s_tail[1] = (uint32_t)(4 * min(row, mlast) * G);
+    }
 
     ReadPlan rp;
-    rp.a_off = (wn * 64 + rl) * ASTR + 8 * ks;
-    rp.b_off = (wm * 64 + rl) * ASTR + 8 * ks;
-    rp.as_off = wn * 64 + rl;
-    if (ks == 0) {
-        rp.bs_off = wm * 64 + rl;
-        rp.bs_step = 1;
-    } else {
-        rp.bs_off = (int)(&sm.zero[rl] - &sm.saop[0][0][0]);
-        rp.bs_step = 0;
-    }
-
-    f32x4 acc[4][4];
+    {
+        // rows wn * 32 WB + 32 blk + r32 (and wm ...) all share swz(r32)
+        const int x = swz(r32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Loads for stage c go through registers `st`: A rows use cpa, B rows cpb.
-    StageRegs st;
-    auto load = [&](int c) {
-        const bool partial = (c == ns - 1) && glast < GC;
-        StageRegs t;
-        const uint8_t *qws = qw0 + c * ROWP;
-        const uint8_t *qas = qa0 + c * ROWP;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            t.a[i] = *reinterpret_cast<const u32x4 *>(qws + (partial ? cpa.voff_tail[i] : cpa.voff[i]));
-            t.b[i] = *reinterpret_cast<const u32x4 *>(qas + (partial ? cpb.voff_tail[i] : cpb.voff[i]));
+        for (int gi = 0; gi < GC; ++gi) {
+            const int slot = (2 * gi + ks2) ^ x;
+            rp.a_code[gi] = C::A_OFF + (wn * 32 * WB + r32) * ROWP + 16 * slot;
+            rp.b_code[gi] = C::B_OFF + (wm * 32 * WB + r32) * ROWP + 16 * slot;
         }
-        const float *ss = s0 + c * GC;
-        t.s[0] = ss[cp.soff];
-        t.s[1] = partial ? t.s[0] : ss[cp.soff + 1];
-        st = t;
-    };
-    auto store = [&](int c) {
-        const int gvalid = c == ns - 1 ? glast : GC;
-        store_stage(st, cp, sm, c % NBUF, gvalid);
-    };
-
-    // Prologue: stages 0 and 1 in LDS, stage 2 in flight, group 0 in registers.
-    load(0);
-    store(0);
-    if (ns > 1) {
-        load(1);
-        store(1);
+        rp.a_scale = C::SA_OFF + (wn * 32 * WB + r32) * GC * 4;
+        rp.b_scale = C::SB_OFF + (wm * 32 * WB + r32) * GC * 4;
+        rp.keep_b = ks2 == 0;
     }
-    if (ns > 2) load(2);
-    __syncthreads();
-    Frags f0, f1;
-    load_frags(f0, sm, rp, 0, 0);
 
-    for (int s = 0; s < ns; ++s) {
-        const int b = s % NBUF;
-        // group 2s (f0) computes while group 2s + 1 is read from LDS
-        load_frags(f1, sm, rp, b, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        group_compute(acc, f0);
-        __builtin_amdgcn_sched_barrier(0);
-        // stage s + 2 -> LDS (its global loads were issued a stage ago), then
-        // publish it; buffer (s + 2) % 3 was last read before the previous barrier
-        if (s + 2 < ns) store(s + 2);
-        __syncthreads();
-        if (s + 3 < ns) load(s + 3);
-        // group 2s + 1 (f1) computes while group 2s + 2 is read from LDS
-        if (s + 1 < ns) load_frags(f0, sm, rp, (s + 1) % NBUF, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        group_compute(acc, f1);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    f32x16 acc[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) acc[t] = f32x16{};
+
+    k_loop<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, odd, acc);
     __syncthreads();
 
     // ---- epilogue: rank-r up-projection on the same tile (bf16 MFMA, the
@@ -341,71 +451,74 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
     if (r > 0) {
         const int lstr = r + 8;   // bf16 elements per LDS row of L2^T
         uint16_t *l2t = sm.u.l2t;
-        for (int q = tid; q < r * (BN / 8); q += NTHR) {
-            const int i = q / (BN / 8);
-            const int seg = (q - i * (BN / 8)) * 8;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (n0 + seg < N) v = *reinterpret_cast<const u32x4 *>(L2 + (int64_t)i * N + n0 + seg);
+        // Thread q stages rank rows [8 c, 8 c + 8) of column n = q % BT as one
+        // 16-byte row segment of L2^T (consecutive lanes: consecutive n, so
+        // both the global reads and the LDS writes are conflict-free).
+        for (int q = tid; q < r * (BT / 8); q += NTHR) {
+            const int n = q % BT;
+            const int c = q / BT;
+            uint32_t v[4] = {0u, 0u, 0u, 0u};
+            if (n0 + n < N) {
+                const uint16_t *src = L2 + (int64_t)(8 * c) * N + n0 + n;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                l2t[(seg + 2 * e) * lstr + i] = (uint16_t)(v[e] & 0xFFFFu);
-                l2t[(seg + 2 * e + 1) * lstr + i] = (uint16_t)(v[e] >> 16);
+                for (int e = 0; e < 4; ++e)
+                    v[e] = (uint32_t)src[(2 * e) * N] | ((uint32_t)src[(2 * e + 1) * N] << 16);
             }
+            *reinterpret_cast<u32x4 *>(&l2t[n * lstr + 8 * c]) = u32x4{v[0], v[1], v[2], v[3]};
         }
         __syncthreads();
-        for (int c32 = 0; c32 < r; c32 += 32) {
-            const int i0 = c32 + 8 * ks;
-            const bool live = i0 < r;
-            u32x4 AL[4];
+        for (int c16 = 0; c16 < r; c16 += 16) {
+            const int i0 = c16 + 8 * ks2;
+            u32x4 AL[WB];
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi) {
-                const int row = wn * 64 + 16 * bi + rl;
-                AL[bi] = live ? *reinterpret_cast<const u32x4 *>(&l2t[row * lstr + i0])
-                              : u32x4{0u, 0u, 0u, 0u};
+            for (int bi = 0; bi < WB; ++bi) {
+                const int row = wn * 32 * WB + 32 * bi + r32;
+                AL[bi] = *reinterpret_cast<const u32x4 *>(&l2t[row * lstr + i0]);
             }
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
-                const int64_t m = m0 + wm * 64 + 16 * bj + rl;
+            for (int bj = 0; bj < WB; ++bj) {
+                const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
                 const int64_t mc = m < M ? m : M - 1;
-                u32x4 hi = u32x4{0u, 0u, 0u, 0u}, lo = u32x4{0u, 0u, 0u, 0u};
-                if (live) {
-                    const f32x4 *p = reinterpret_cast<const f32x4 *>(xl1 + mc * r + i0);
-                    const f32x4 x0 = p[0], x1 = p[1];
-                    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(xl1 + mc * r + i0);
+                const f32x4 x0 = p[0], x1 = p[1];
+                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                u32x4 hi, lo;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t h = pack_bf16x2(xs[2 * e], xs[2 * e + 1]);
-                        hi[e] = h;
-                        lo[e] = pack_bf16x2(xs[2 * e] - bf16_lo(h), xs[2 * e + 1] - bf16_hi(h));
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t h = pack_bf16x2(xs[2 * e], xs[2 * e + 1]);
+                    hi[e] = h;
+                    lo[e] = pack_bf16x2(xs[2 * e] - bf16_lo(h), xs[2 * e + 1] - bf16_hi(h));
                 }
 #pragma unroll
-                for (int bi = 0; bi < 4; ++bi) {
-                    acc[bi][bj] = mfma_bf16_16x16x32(AL[bi], hi, acc[bi][bj]);
-                    acc[bi][bj] = mfma_bf16_16x16x32(AL[bi], lo, acc[bi][bj]);
+                for (int bi = 0; bi < WB; ++bi) {
+                    acc[bi * WB + bj] = mfma_bf16_32x32x16(AL[bi], hi, acc[bi * WB + bj]);
+                    acc[bi * WB + bj] = mfma_bf16_32x32x16(AL[bi], lo, acc[bi * WB + bj]);
                 }
             }
         }
     }
 
+    // Block (bi, bj); element i of the lane is n = base + 8 (i / 4) +
+    // 4 (lane / 32) + i % 4, m = base + lane % 32.
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-        const int64_t n = n0 + wn * 64 + 16 * bi + 4 * ks;
-        if (n >= N) continue;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias) {
-            const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + n);
-            bv[0] = bf16_lo(b2.x); bv[1] = bf16_hi(b2.x);
-            bv[2] = bf16_lo(b2.y); bv[3] = bf16_hi(b2.y);
-        }
+    for (int t = 0; t < NB; ++t) {
+        const int bi = t / WB, bj = t % WB;
+        const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+        if (m >= M) continue;
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const int64_t m = m0 + wm * 64 + 16 * bj + rl;
-            if (m >= M) continue;
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+            if (n >= N) continue;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias) {
+                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + n);
+                bv[0] = bf16_lo(b2.x); bv[1] = bf16_hi(b2.x);
+                bv[2] = bf16_lo(b2.y); bv[3] = bf16_hi(b2.y);
+            }
             float o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float x = acc[bi][bj][j] + bv[j];
+                float x = acc[t][4 * q + j] + bv[j];
                 if (act == 1) x = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
                 o[j] = x;
             }
@@ -417,46 +530,87 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
     }
 }
 
-// Test hook: per-group integer sums with the GEMM's operand widening and
-// int8 MFMA; one wave per 16 x 16 block of (n, m), operands read from memory.
+// Test hook: per-group integer sums with the GEMM's k split, operand
+// widening and int8 matrix instruction; one wave per 32 x 32 block of
+// (n, m), operands read from memory.
 __global__ void __launch_bounds__(64)
 group_sums_kernel(const uint8_t *__restrict__ qa, const uint8_t *__restrict__ qw, int64_t M,
                   int64_t N, int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
                   int32_t *__restrict__ S) {
     const int lane = threadIdx.x;
-    const int rl = lane & 15, ks = lane >> 4;
+    const int r32 = lane & 31, ks2 = lane >> 5;
     const int64_t nb = blockIdx.x, mb = blockIdx.y;
     const int64_t G = K / kGroup;
-    int64_t n = n0 + nb * 16 + rl, m = m0 + mb * 16 + rl;
+    int64_t n = n0 + nb * 32 + r32, m = m0 + mb * 32 + r32;
     if (n >= N) n = N - 1;
     if (m >= M) m = M - 1;
     for (int64_t g = 0; g < G; ++g) {
-        const i32x4 A = widen_nibbles(*reinterpret_cast<const u32x2 *>(qw + n * (K / 2) + g * 32 + 8 * ks));
-        const i32x4 B = widen_nibbles(*reinterpret_cast<const u32x2 *>(qa + m * (K / 2) + g * 32 + 8 * ks));
-        const i32x4 D = mfma_i8_16x16x64(A, B, i32x4{0, 0, 0, 0});
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(qw + n * (K / 2) + g * 32 + 16 * ks2);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(qa + m * (K / 2) + g * 32 + 16 * ks2);
+        i32x16 D = mfma_i8_32x32x32(widen_nibbles(u32x2{a.x, a.y}), widen_nibbles(u32x2{b.x, b.y}),
+                                    i32x16{});
+        D = mfma_i8_32x32x32(widen_nibbles(u32x2{a.z, a.w}), widen_nibbles(u32x2{b.z, b.w}), D);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t nl = nb * 16 + 4 * ks + j;
-            const int64_t ml = mb * 16 + rl;
-            if (nl < tn && ml < tm) S[(ml * tn + nl) * G + g] = D[j] >> 8;
+        for (int i = 0; i < 16; ++i) {
+            const int64_t nl = nb * 32 + 8 * (i / 4) + 4 * ks2 + (i % 4);
+            const int64_t ml = mb * 32 + r32;
+            if (nl < tn && ml < tm) S[(ml * tn + nl) * G + g] = D[i] >> 8;
         }
     }
 }
 
+static std::atomic<int> g_tile_policy{0};
+
+void set_tile_policy(int policy) { g_tile_policy.store(policy, std::memory_order_relaxed); }
+
+// Workgroup slots of the device (two 128 x 128 workgroups per compute
+// unit), cached per device.
+static int64_t wg_slots() {
+    static int64_t slots[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    if (slots[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        slots[dev] = 2 * (int64_t)cus;
+    }
+    return slots[dev];
+}
+
+// Full 128 x 128 tiles for whole rounds of the device's workgroup slots; if
+// a partial last round is left of at most three quarters of the slots, its
+// tiles run as 64 x 64 quarter tiles in a second launch (four times the
+// workgroups, a quarter of the work each).
 hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
                             const float *sw, const float *xl1, const uint16_t *L2,
                             const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
                             int r, uint16_t *Y, hipStream_t stream) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    w4a4_lr_gemm_kernel<<<(unsigned)tiles, NTHR, 0, stream>>>(qa, sa, qw, sw, xl1, L2, bias, act,
-                                                              M, N, K, r, Y);
+    const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
+    const int policy = g_tile_policy.load(std::memory_order_relaxed);
+    int64_t rest = 0;
+    if (policy == 2) {
+        rest = tiles;
+    } else if (policy == 0) {
+        const int64_t slots = wg_slots();
+        rest = tiles % slots;
+        if (rest * 4 > slots * 3) rest = 0;
+    }
+    const int64_t full = tiles - rest;
+    if (full > 0)
+        w4a4_lr_gemm_kernel<2><<<(unsigned)full, NTHR, 0, stream>>>(
+            qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, 0, full);
+    if (rest > 0)
+        w4a4_lr_gemm_kernel<1><<<(unsigned)(4 * rest), NTHR, 0, stream>>>(
+            qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, full, rest);
     return hipGetLastError();
 }
 
 hipError_t launch_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
                              int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
                              int32_t *S, hipStream_t stream) {
-    dim3 grid((unsigned)((tn + 15) / 16), (unsigned)((tm + 15) / 16));
+    dim3 grid((unsigned)((tn + 31) / 32), (unsigned)((tm + 31) / 32));
     group_sums_kernel<<<grid, 64, 0, stream>>>(qa, qw, M, N, K, m0, n0, tm, tn, S);
     return hipGetLastError();
 }

@@ -171,6 +171,22 @@ int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, i
                               int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
                               int32_t *S, void *stream);
 
+/*
+ * Test hook: how svdq_w4a4_lr_gemm (and svdq_linear) tile the output.
+ *   SVDQ_TILES_AUTO    128 x 128 tiles for whole rounds of the device's
+ *                      workgroup slots, 64 x 64 tiles for a partial last round
+ *                      of at most three quarters of them (the default)
+ *   SVDQ_TILES_FULL    128 x 128 tiles only
+ *   SVDQ_TILES_QUARTER 64 x 64 tiles only
+ * Process-wide; results are identical under every policy (it only moves
+ * tiles between two kernels that compute the same thing).  Returns
+ * SVDQ_ERR_INVALID_ARG for any other value.
+ */
+#define SVDQ_TILES_AUTO 0
+#define SVDQ_TILES_FULL 1
+#define SVDQ_TILES_QUARTER 2
+int32_t svdq_debug_set_tile_policy(int32_t policy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     decl = declared_functions()
-    assert len(decl) == 10, decl
+    assert len(decl) == 11, decl
     assert sorted(_binding.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -118,6 +118,14 @@ def test_pack_and_debug_reject(lib):
     assert lib.svdq_pack_weights(P(A), 8, 128, P(U), P(A), None) == MISALIGNED
     assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 128, 8, 0, 16, 16, P(A), None) == INVALID
     assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 100, 0, 0, 16, 16, P(A), None) == SHAPE
+    assert lib.svdq_debug_set_tile_policy(3) == INVALID
+    assert lib.svdq_debug_set_tile_policy(-1) == INVALID
+
+
+def test_tile_policy_values_accepted(lib):
+    # host-side setting only (no launch); restored to the default
+    for pol in (bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_AUTO):
+        assert lib.svdq_debug_set_tile_policy(pol) == OK
 
 
 def test_empty_inputs_are_noops(lib):

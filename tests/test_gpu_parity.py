@@ -72,7 +72,14 @@ def test_group_sums_bit_exact(case):
         assert np.array_equal(S, ref)
 
 
-def test_gemm_stagewise(case):
+@pytest.fixture(params=[bdt.TILES_FULL, bdt.TILES_QUARTER], ids=["full_tiles", "quarter_tiles"])
+def tiles(request):
+    bdt.svdq_debug_set_tile_policy(request.param)
+    yield request.param
+    bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
+
+
+def test_gemm_stagewise(case, tiles):
     # Same inputs on both sides: the oracle's codes/scales and its xl1 in fp32.
     L, r, K = case["L"], case["r"], case["K"]
     xl1_32 = case["xl1"].astype(np.float32) if r else None
@@ -85,7 +92,7 @@ def test_gemm_stagewise(case):
     assert_y_close(bf16_host(Y), y_or, "gemm")
 
 
-def test_linear_end_to_end(case):
+def test_linear_end_to_end(case, tiles):
     L, r = case["L"], case["r"]
     Y = bdt.linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
                    to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
@@ -101,3 +108,18 @@ def test_linear_is_deterministic(case):
     y1 = bf16_host(bdt.linear(*args))
     y2 = bf16_host(bdt.linear(*args))
     assert np.array_equal(y1, y2)
+
+
+def test_tile_policies_agree_bit_exact(case):
+    # Both tile shapes run the same per-output arithmetic in the same order.
+    L, r = case["L"], case["r"]
+    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
+            to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
+    out = []
+    try:
+        for pol in (bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_AUTO):
+            bdt.svdq_debug_set_tile_policy(pol)
+            out.append(bf16_host(bdt.linear(*args)))
+    finally:
+        bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
+    assert np.array_equal(out[0], out[1]) and np.array_equal(out[0], out[2])
