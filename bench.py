@@ -118,10 +118,10 @@ def main():
     carved = []
     for s_ in sets:
         carved.append(bdt.quantize_act_down(s_["X"], s_["lam"], s_["L1"] if r > 0 else None))
-        s_["ws_down"] = torch.empty(bdt.svdq_quantize_act_down_workspace_bytes(K, r),
+        s_["ws_down"] = torch.empty(max(bdt.svdq_quantize_act_down_workspace_bytes(M, K, r), 1),
                                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    down_ws = bdt.svdq_quantize_act_down_workspace_bytes(K, r)
+    down_ws = bdt.svdq_quantize_act_down_workspace_bytes(M, K, r)
 
     def quant(i):
         s, (qa, sa, xl1) = sets[i % nsets], carved[i % nsets]

@@ -57,7 +57,7 @@ def quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Ten
     qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     sa = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
     xl1 = torch.empty((M, r), dtype=torch.float32, device=dev) if r > 0 else None
-    ws_bytes = svdq_quantize_act_down_workspace_bytes(K, r)
+    ws_bytes = svdq_quantize_act_down_workspace_bytes(M, K, r)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     svdq_quantize_act_down(_bits(X), lam, _bits(L1) if r > 0 else None, M, K, r, qa, sa, xl1,
                            ws, ws_bytes)

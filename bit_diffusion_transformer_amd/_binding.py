@@ -59,7 +59,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_status_string": ([I32], ctypes.c_char_p),
         "svdq_last_error": ([], ctypes.c_char_p),
         "svdq_pack_weights": ([P, I64, I64, P, P, P], I32),
-        "svdq_quantize_act_down_workspace_bytes": ([I64, I32], SZ),
+        "svdq_quantize_act_down_workspace_bytes": ([I64, I64, I32], SZ),
         "svdq_quantize_act_down": ([P, P, P, I64, I64, I32, P, P, P, P, SZ, P], I32),
         "svdq_w4a4_lr_gemm": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P], I32),
         "svdq_linear_workspace_bytes": ([I64, I64, I32], SZ),
@@ -117,8 +117,8 @@ def svdq_pack_weights(R, N, K, qw, sw, stream=None):
            "svdq_pack_weights")
 
 
-def svdq_quantize_act_down_workspace_bytes(K, r) -> int:
-    return int(load_library().svdq_quantize_act_down_workspace_bytes(K, r))
+def svdq_quantize_act_down_workspace_bytes(M, K, r) -> int:
+    return int(load_library().svdq_quantize_act_down_workspace_bytes(M, K, r))
 
 
 def svdq_quantize_act_down(X, lam, L1, M, K, r, qa, sa, xl1, workspace, ws_bytes, stream=None):

@@ -9,141 +9,191 @@
 
 namespace svdq {
 
-// ------------------------------------------------------------------ prep
-// inv_lam[k] = fl32(1 / lambda[k]);  L1s = fl32(L1[k][i] * inv_lam[k]) split
-// into bf16 hi = rn(L1s), lo = rn(L1s - hi), stored transposed [r][K] so the
-// down-projection reads 8 consecutive k per lane.  X diag(lambda)^-1 L1 is
-// then computed as X (L1s_hi + L1s_lo) with X exact in bf16: every product
-// is exact in fp32 and the split keeps ~16 significant bits of L1s.
+// ------------------------------------------------------------------ K1
+// One workgroup = 64 rows of X (four waves of 16) and a chunk of KC groups
+// of K.  Everything the chunk needs is requested up front, in this order:
+// lambda and the chunk of L1 (small, read first so that their use does not
+// wait for the rest), then the X of all KC groups of the wave's rows, which
+// stays in flight while the workgroup computes fl32(1 / lambda) and stages
+// the chunk of L1 transposed in LDS ([column][k], 8 consecutive k = one
+// 16-byte read), shared by the four waves.  The loads have fixed counts
+// (addresses past the chunk or the rank are clamped and the data ignored),
+// so each group waits only for its own X.  (X is deliberately not declared
+// restrict: loads from a read-only restrict argument may be re-issued after
+// the barrier instead of being kept in registers.)
+//
+// Per group, lane l owns row l % 16 and the 16 consecutive elements at
+// 16 (l / 16): the four lanes of a group reduce the absmax with two lane
+// exchanges.  The down-projection uses the smoothed values x^ themselves,
+// split into bf16 hi + lo (x^ - hi), as the A operand of a bf16 MFMA
+// (16x16x32: lane l holds 8 consecutive k of row l % 16 in k-slot l / 16)
+// against the raw bf16 L1: every product is exact in fp32 and the split keeps
+// about 16 significant bits of x^.  A chunk's result is either xl1 itself
+// (one chunk) or a partial sum that xl1_reduce_kernel adds up in chunk order,
+// so the result does not depend on scheduling.
+constexpr int K1_ROWS = 64;
+
+// Chunk size for a tile count: the staged L1 chunk is 64 KC x 16 NT bf16.
+template <int NT> struct K1Chunk { static constexpr int KC = NT <= 2 ? 8 : (NT <= 4 ? 4 : 2); };
+
+template <int NT>
 __global__ void __launch_bounds__(256)
-prep_down_kernel(const float *__restrict__ lambda, const uint16_t *__restrict__ L1,
-                 int64_t K, int r, float *__restrict__ inv_lam,
-                 uint16_t *__restrict__ l1_hi, uint16_t *__restrict__ l1_lo) {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= K) return;
-    const float il = 1.0f / lambda[k];
-    if (blockIdx.y == 0) inv_lam[k] = il;
-    for (int i = blockIdx.y; i < r; i += gridDim.y) {
-        const float s = bf16_to_f32(L1[k * r + i]) * il;
-        const uint32_t hi_lo = pack_bf16x2(s, 0.0f);
-        const float hi = bf16_lo(hi_lo);
-        const uint32_t lo_pair = pack_bf16x2(s - hi, 0.0f);
-        l1_hi[(int64_t)i * K + k] = (uint16_t)(hi_lo & 0xFFFFu);
-        l1_lo[(int64_t)i * K + k] = (uint16_t)(lo_pair & 0xFFFFu);
+quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
+                  const uint16_t *__restrict__ L1, int64_t M, int64_t K, int r, int nc,
+                  uint8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ out,
+                  int64_t out_chunk_stride) {
+    constexpr int KC = K1Chunk<NT>::KC;
+    constexpr int S = KC * kGroup + 8;                 // LDS row of the L1 chunk, bf16
+    constexpr int NLAM = (KC * kGroup + 255) / 256;    // lambda loads per thread
+    constexpr int NL1 = NT > 0 ? KC * NT / 2 : 0;      // 16-byte L1 pieces per thread
+    __shared__ float inv[KC * kGroup];
+    __shared__ __align__(16) uint16_t l1t[NT > 0 ? 16 * NT * S : 8];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int rl = lane & 15;
+    const int ks = lane >> 4;
+    const int64_t c = blockIdx.x % nc;                 // chunk
+    const int64_t rb = blockIdx.x / nc;                // row block
+    const int64_t G = K / kGroup;
+    const int64_t g0 = c * KC;
+    const int gc = (int)((G - g0) < KC ? (G - g0) : KC);
+    const int64_t row = rb * K1_ROWS + wave * 16 + rl;
+    const bool row_ok = row < M;
+    const int64_t rowc = row_ok ? row : M - 1;
+    const int nt = r >> 4;
+    const int64_t kbase = g0 * kGroup;
+    const int kvalid = gc * kGroup;
+
+    // 1. lambda and the L1 chunk, then X, all in flight together
+    float lam[NLAM];
+#pragma unroll
+    for (int j = 0; j < NLAM; ++j) {
+        const int k = tid + 256 * j;
+        lam[j] = lambda[kbase + (k < kvalid ? k : kvalid - 1)];
+    }
+    u32x4 l1v[NL1 > 0 ? NL1 : 1];
+    int l1k[NL1 > 0 ? NL1 : 1], l1n[NL1 > 0 ? NL1 : 1];
+#pragma unroll
+    for (int j = 0; j < NL1; ++j) {
+        const int q = tid + 256 * j;                   // piece: k = q / (2 NT), columns 8 (q % 2NT)
+        constexpr int PR = NT > 0 ? 2 * NT : 1;        // pieces per k row
+        const int kk = q / PR;
+        const int n0 = 8 * (q - kk * PR);
+        l1k[j] = kk;
+        l1n[j] = n0;
+        const int kc_ = kk < kvalid ? kk : kvalid - 1;
+        const int nc_ = n0 < r ? n0 : 0;
+        l1v[j] = *reinterpret_cast<const u32x4 *>(L1 + (kbase + kc_) * r + nc_);
+    }
+    __builtin_amdgcn_sched_barrier(0);                 // keep the small loads first
+    u32x4 xa[KC], xb[KC];
+    const uint16_t *xrow = X + rowc * K + kbase + 16 * ks;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int ic = i < gc ? i : gc - 1;
+        xa[i] = *reinterpret_cast<const u32x4 *>(xrow + ic * kGroup);
+        xb[i] = *reinterpret_cast<const u32x4 *>(xrow + ic * kGroup + 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. 1/lambda and the transposed L1 chunk into LDS (X still in flight)
+#pragma unroll
+    for (int j = 0; j < NLAM; ++j) {
+        const int k = tid + 256 * j;
+        if (256 * (j + 1) <= KC * kGroup || k < KC * kGroup) inv[k] = 1.0f / lam[j];
+    }
+    // (columns past r hold copies that are never read; writing them keeps the
+    // loads above unconditional)
+#pragma unroll
+    for (int j = 0; j < NL1; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            l1t[(l1n[j] + 2 * e) * S + l1k[j]] = (uint16_t)(l1v[j][e] & 0xFFFFu);
+            l1t[(l1n[j] + 2 * e + 1) * S + l1k[j]] = (uint16_t)(l1v[j][e] >> 16);
+        }
+    }
+    // LDS writes done, then a barrier without a memory fence (the X loads
+    // stay outstanding across it)
+    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0); vmcnt, expcnt untouched
+    asm volatile("s_barrier" ::: "memory");
+
+    f32x4 acc[NT > 0 ? NT : 1];
+#pragma unroll
+    for (int t = 0; t < (NT > 0 ? NT : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        if (i < gc) {
+            const int64_t g = g0 + i;
+            const f32x4 *ip = reinterpret_cast<const f32x4 *>(inv + i * kGroup + 16 * ks);
+            const f32x4 i0 = ip[0], i1 = ip[1], i2 = ip[2], i3 = ip[3];
+            const u32x4 x0 = xa[i], x1 = xb[i];
+            float v[16];
+            v[0] = bf16_lo(x0.x) * i0.x;  v[1] = bf16_hi(x0.x) * i0.y;
+            v[2] = bf16_lo(x0.y) * i0.z;  v[3] = bf16_hi(x0.y) * i0.w;
+            v[4] = bf16_lo(x0.z) * i1.x;  v[5] = bf16_hi(x0.z) * i1.y;
+            v[6] = bf16_lo(x0.w) * i1.z;  v[7] = bf16_hi(x0.w) * i1.w;
+            v[8] = bf16_lo(x1.x) * i2.x;  v[9] = bf16_hi(x1.x) * i2.y;
+            v[10] = bf16_lo(x1.y) * i2.z; v[11] = bf16_hi(x1.y) * i2.w;
+            v[12] = bf16_lo(x1.z) * i3.x; v[13] = bf16_hi(x1.z) * i3.y;
+            v[14] = bf16_lo(x1.w) * i3.z; v[15] = bf16_hi(x1.w) * i3.w;
+            u32x2 packed;
+            const float s = quantize_group16(v, packed);
+            if (row_ok) {
+                *reinterpret_cast<u32x2 *>(qa + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
+                if (ks == 0) sa[row * G + g] = s;
+            }
+            if (NT > 0) {
+                u32x4 h[2], l[2];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t hp = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+                    h[e >> 2][e & 3] = hp;
+                    l[e >> 2][e & 3] = pack_bf16x2(v[2 * e] - bf16_lo(hp), v[2 * e + 1] - bf16_hi(hp));
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t < nt) {
+                        const uint16_t *bp = l1t + (16 * t + rl) * S + i * kGroup + 16 * ks;
+                        const u32x4 b0 = *reinterpret_cast<const u32x4 *>(bp);
+                        const u32x4 b1 = *reinterpret_cast<const u32x4 *>(bp + 8);
+                        acc[t] = mfma_bf16_16x16x32(h[0], b0, acc[t]);
+                        acc[t] = mfma_bf16_16x16x32(l[0], b0, acc[t]);
+                        acc[t] = mfma_bf16_16x16x32(h[1], b1, acc[t]);
+                        acc[t] = mfma_bf16_16x16x32(l[1], b1, acc[t]);
+                    }
+                }
+            }
+        }
+    }
+    if (NT == 0) return;
+
+    // This chunk's x^ L1: lane holds rows 4 ks + j, column 16 t + rl.
+    float *o = out + c * out_chunk_stride;
+#pragma unroll
+    for (int t = 0; t < (NT > 0 ? NT : 1); ++t) {
+        if (t < nt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t orow = rb * K1_ROWS + wave * 16 + 4 * ks + j;
+                if (orow < M) o[orow * r + 16 * t + rl] = acc[t][j];
+            }
+        }
     }
 }
 
-// ------------------------------------------------------------------ K1
-// One workgroup = 16 rows of X and KW waves that split the K groups between
-// them.  Lane l owns row l % 16 and, inside every group of 64, the 16
-// consecutive elements starting at 16 * (l / 16): the four lanes of a group
-// reduce the absmax with two lane exchanges.  The same registers feed the
-// bf16 MFMA of the down-projection as its A operand (16x16x32: lane l holds
-// 8 consecutive k of row l % 16 in k-slot l / 16), with the transposed hi/lo
-// factor as the B operand; the partial products of the KW waves are summed
-// in LDS in wave order, so the result does not depend on scheduling.
-template <int KW, int NTMAX>
-__global__ void __launch_bounds__(64 * KW)
-quant_down_kernel(const uint16_t *__restrict__ X, const float *__restrict__ inv_lam,
-                  const uint16_t *__restrict__ l1_hi, const uint16_t *__restrict__ l1_lo,
-                  int64_t M, int64_t K, int r, uint8_t *__restrict__ qa,
-                  float *__restrict__ sa, float *__restrict__ xl1) {
-    extern __shared__ float red[];   // [KW][16][r]
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int rl = lane & 15;
-    const int ks = lane >> 4;
-    const int64_t row = (int64_t)blockIdx.x * 16 + rl;
-    const bool row_ok = row < M;
-    const int64_t rowc = row_ok ? row : M - 1;
-    const int64_t G = K / kGroup;
-    const int64_t g_begin = G * wave / KW;
-    const int64_t g_end = G * (wave + 1) / KW;
-    const int nt = r >> 4;
-
-    f32x4 acc[NTMAX];
-#pragma unroll
-    for (int t = 0; t < NTMAX; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Software pipeline: the next group's X and 1/lambda are in flight while
-    // the current group is quantized; the current group's down-projection
-    // operands are issued before the quantizer math that hides their latency.
-    const uint16_t *xrow = X + rowc * K;
-    u32x4 nxa = u32x4{0u, 0u, 0u, 0u}, nxb = nxa;
-    f32x4 ni0 = f32x4{0.f, 0.f, 0.f, 0.f}, ni1 = ni0, ni2 = ni0, ni3 = ni0;
-    if (g_begin < g_end) {
-        const int64_t k0 = g_begin * kGroup + 16 * ks;
-        nxa = *reinterpret_cast<const u32x4 *>(xrow + k0);
-        nxb = *reinterpret_cast<const u32x4 *>(xrow + k0 + 8);
-        const f32x4 *il4 = reinterpret_cast<const f32x4 *>(inv_lam + k0);
-        ni0 = il4[0]; ni1 = il4[1]; ni2 = il4[2]; ni3 = il4[3];
+// xl1 = sum over chunks of the partial sums, added in chunk order.
+__global__ void __launch_bounds__(256)
+xl1_reduce_kernel(const float *__restrict__ part, int nc, int64_t total, float *__restrict__ xl1) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= total) return;
+    f32x4 s = *reinterpret_cast<const f32x4 *>(part + i);
+    for (int c = 1; c < nc; ++c) {
+        const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (int64_t)c * total + i);
+        s = f32x4{s.x + p.x, s.y + p.y, s.z + p.z, s.w + p.w};
     }
-    for (int64_t g = g_begin; g < g_end; ++g) {
-        const int64_t k0 = g * kGroup + 16 * ks;
-        const u32x4 xa = nxa, xb = nxb;
-        const f32x4 i0 = ni0, i1 = ni1, i2 = ni2, i3 = ni3;
-        if (g + 1 < g_end) {
-            nxa = *reinterpret_cast<const u32x4 *>(xrow + k0 + kGroup);
-            nxb = *reinterpret_cast<const u32x4 *>(xrow + k0 + kGroup + 8);
-            const f32x4 *il4 = reinterpret_cast<const f32x4 *>(inv_lam + k0 + kGroup);
-            ni0 = il4[0]; ni1 = il4[1]; ni2 = il4[2]; ni3 = il4[3];
-        }
-        u32x4 bh[NTMAX][2], bl[NTMAX][2];
-#pragma unroll
-        for (int t = 0; t < NTMAX; ++t) {
-            if (t < nt) {
-                const int64_t col = (int64_t)(16 * t + rl);
-                bh[t][0] = *reinterpret_cast<const u32x4 *>(l1_hi + col * K + k0);
-                bh[t][1] = *reinterpret_cast<const u32x4 *>(l1_hi + col * K + k0 + 8);
-                bl[t][0] = *reinterpret_cast<const u32x4 *>(l1_lo + col * K + k0);
-                bl[t][1] = *reinterpret_cast<const u32x4 *>(l1_lo + col * K + k0 + 8);
-            }
-        }
-        float v[16];
-        v[0] = bf16_lo(xa.x) * i0.x;  v[1] = bf16_hi(xa.x) * i0.y;
-        v[2] = bf16_lo(xa.y) * i0.z;  v[3] = bf16_hi(xa.y) * i0.w;
-        v[4] = bf16_lo(xa.z) * i1.x;  v[5] = bf16_hi(xa.z) * i1.y;
-        v[6] = bf16_lo(xa.w) * i1.z;  v[7] = bf16_hi(xa.w) * i1.w;
-        v[8] = bf16_lo(xb.x) * i2.x;  v[9] = bf16_hi(xb.x) * i2.y;
-        v[10] = bf16_lo(xb.y) * i2.z; v[11] = bf16_hi(xb.y) * i2.w;
-        v[12] = bf16_lo(xb.z) * i3.x; v[13] = bf16_hi(xb.z) * i3.y;
-        v[14] = bf16_lo(xb.w) * i3.z; v[15] = bf16_hi(xb.w) * i3.w;
-        u32x2 packed;
-        const float s = quantize_group16(v, packed);
-        if (row_ok) {
-            *reinterpret_cast<u32x2 *>(qa + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
-            if (ks == 0) sa[row * G + g] = s;
-        }
-#pragma unroll
-        for (int t = 0; t < NTMAX; ++t) {
-            if (t < nt) {
-                acc[t] = mfma_bf16_16x16x32(xa, bh[t][0], acc[t]);
-                acc[t] = mfma_bf16_16x16x32(xa, bl[t][0], acc[t]);
-                acc[t] = mfma_bf16_16x16x32(xb, bh[t][1], acc[t]);
-                acc[t] = mfma_bf16_16x16x32(xb, bl[t][1], acc[t]);
-            }
-        }
-    }
-    if (nt == 0) return;
-
-    // Partial XL1 of this wave: lane holds rows 4*ks + j, column 16 t + rl.
-#pragma unroll
-    for (int t = 0; t < NTMAX; ++t) {
-        if (t < nt) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                red[(wave * 16 + 4 * ks + j) * r + 16 * t + rl] = acc[t][j];
-        }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * r; idx += 64 * KW) {
-        const int rr = idx / r;
-        const int c = idx - rr * r;
-        float sum = 0.0f;
-        for (int w = 0; w < KW; ++w) sum += red[(w * 16 + rr) * r + c];
-        const int64_t orow = (int64_t)blockIdx.x * 16 + rr;
-        if (orow < M) xl1[orow * r + c] = sum;
-    }
+    *reinterpret_cast<f32x4 *>(xl1 + i) = s;
 }
 
 // ------------------------------------------------------------------ pack
@@ -180,49 +230,28 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_prep_down(const float *lambda, const uint16_t *L1, int64_t K, int r,
-                            const DownWorkspace &ws, hipStream_t stream) {
-    dim3 grid((unsigned)((K + 255) / 256), (unsigned)(r > 0 ? (r < 8 ? r : 8) : 1));
-    prep_down_kernel<<<grid, 256, 0, stream>>>(lambda, L1, K, r, ws.inv_lam, ws.l1_hi, ws.l1_lo);
-    return hipGetLastError();
-}
-
-int choose_kw(int64_t M, int64_t K, int r) {
-    const int64_t blocks = (M + 15) / 16;
-    const int64_t G = K / kGroup;
-    int kw = 1;
-    while (kw < 16 && blocks * kw < 2048 && 2 * kw <= G && 2 * kw * r <= 1024) kw *= 2;
-    return kw;
-}
-
-hipError_t launch_quant_down(const uint16_t *X, int64_t M, int64_t K, int r,
-                             const DownWorkspace &ws, uint8_t *qa, float *sa, float *xl1,
-                             hipStream_t stream) {
-    const int kw = choose_kw(M, K, r);
-    const unsigned blocks = (unsigned)((M + 15) / 16);
-    const size_t lds = (size_t)kw * 16 * (size_t)r * sizeof(float);
-#define SVDQ_K1(KWV, NTM)                                                                  \
-    quant_down_kernel<KWV, NTM><<<blocks, 64 * KWV, lds, stream>>>(                        \
-        X, ws.inv_lam, ws.l1_hi, ws.l1_lo, M, K, r, qa, sa, xl1)
-#define SVDQ_K1_KW(NTM)                                                                    \
-    switch (kw) {                                                                          \
-        case 1: SVDQ_K1(1, NTM); break;                                                    \
-        case 2: SVDQ_K1(2, NTM); break;                                                    \
-        case 4: SVDQ_K1(4, NTM); break;                                                    \
-        case 8: SVDQ_K1(8, NTM); break;                                                    \
-        case 16: SVDQ_K1(16, NTM); break;                                                  \
-        default: return hipErrorInvalidValue;                                              \
-    }
-    const int nt = r / 16;
-    if (nt <= 2) {
-        SVDQ_K1_KW(2)
-    } else if (nt <= 4) {
-        SVDQ_K1_KW(4)
-    } else {
-        SVDQ_K1_KW(8)
-    }
-#undef SVDQ_K1_KW
+hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                             int64_t M, int64_t K, int r, const DownWorkspace &ws, uint8_t *qa,
+                             float *sa, float *xl1, hipStream_t stream) {
+    const int nc = k1_chunks(K, r);
+    const int64_t rbs = (M + K1_ROWS - 1) / K1_ROWS;
+    const unsigned blocks = (unsigned)(rbs * nc);
+    const bool partial = r > 0 && nc > 1;
+    float *out = partial ? ws.part : xl1;
+    const int64_t stride = partial ? M * (int64_t)r : 0;
+#define SVDQ_K1(NTV)                                                                       \
+    quant_down_kernel<NTV><<<blocks, 256, 0, stream>>>(X, lambda, L1, M, K, r, nc, qa, sa,  \
+                                                      out, stride)
+    if (r == 0) SVDQ_K1(0);
+    else if (r <= 32) SVDQ_K1(2);
+    else if (r <= 64) SVDQ_K1(4);
+    else SVDQ_K1(8);
 #undef SVDQ_K1
+    if (partial) {
+        const int64_t total = M * (int64_t)r;
+        const unsigned rblocks = (unsigned)((total / 4 + 255) / 256);
+        xl1_reduce_kernel<<<rblocks, 256, 0, stream>>>(ws.part, nc, total, xl1);
+    }
     return hipGetLastError();
 }
 

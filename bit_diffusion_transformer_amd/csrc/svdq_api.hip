@@ -119,11 +119,11 @@ int32_t validate_down(const uint16_t *X, const float *lambda, const uint16_t *L1
     SVDQ_TRY(need_ptr(qa, "qa"));
     SVDQ_TRY(need_ptr(sa, "sa"));
     SVDQ_TRY(lr_ptrs(L1, "L1", xl1, "xl1", r));
-    const size_t need = svdq::down_workspace_bytes(K, r);
+    const size_t need = svdq::down_workspace_bytes(M, K, r);
     if (ws_bytes < need)
         return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed",
                     ws_bytes, need);
-    return need_ptr(ws, "workspace");
+    return need == 0 ? SVDQ_OK : need_ptr(ws, "workspace");
 }
 
 int32_t validate_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
@@ -166,7 +166,7 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r) {
     w.xl1 = r > 0 ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256((size_t)M * (size_t)r * 4);
     w.down = p + off;
-    off += svdq::down_workspace_bytes(K, r);
+    off += svdq::down_workspace_bytes(M, K, r);
     w.bytes = off;
     return w;
 }
@@ -206,9 +206,9 @@ int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, flo
                       "pack_weights launch");
 }
 
-size_t svdq_quantize_act_down_workspace_bytes(int64_t K, int32_t r) {
-    if (K < 0 || r < 0) return 0;
-    return svdq::down_workspace_bytes(K, r);
+size_t svdq_quantize_act_down_workspace_bytes(int64_t M, int64_t K, int32_t r) {
+    if (M < 0 || K < 0 || r < 0) return 0;
+    return svdq::down_workspace_bytes(M, K, r);
 }
 
 int32_t svdq_quantize_act_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
@@ -219,9 +219,8 @@ int32_t svdq_quantize_act_down(const uint16_t *X, const float *lambda, const uin
     if (M == 0) return SVDQ_OK;
     SVDQ_TRY(check_device());
     hipStream_t s = (hipStream_t)stream;
-    const svdq::DownWorkspace dw = svdq::carve_down_workspace(workspace, K, r);
-    SVDQ_TRY(hip_status(svdq::launch_prep_down(lambda, L1, K, r, dw, s), "prep launch"));
-    return hip_status(svdq::launch_quant_down(X, M, K, r, dw, qa, sa, xl1, s),
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(workspace, M, K, r);
+    return hip_status(svdq::launch_quant_down(X, lambda, L1, M, K, r, dw, qa, sa, xl1, s),
                       "quantize_act_down launch");
 }
 
@@ -270,9 +269,9 @@ int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
     SVDQ_TRY(check_device());
     hipStream_t s = (hipStream_t)stream;
     const LinearWorkspace w = carve_linear(workspace, M, K, r);
-    const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.down, K, r);
-    SVDQ_TRY(hip_status(svdq::launch_prep_down(lambda, L1, K, r, dw, s), "prep launch"));
-    SVDQ_TRY(hip_status(svdq::launch_quant_down(X, M, K, r, dw, w.qa, w.sa, w.xl1, s),
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.down, M, K, r);
+    SVDQ_TRY(hip_status(svdq::launch_quant_down(X, lambda, L1, M, K, r, dw, w.qa, w.sa, w.xl1,
+                                                s),
                         "quantize_act_down launch"));
     return hip_status(svdq::launch_w4a4_gemm(w.qa, w.sa, qw, sw, w.xl1, L2, bias, act, M, N, K,
                                              r, Y, s),

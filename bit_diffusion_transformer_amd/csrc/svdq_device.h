@@ -108,8 +108,17 @@ __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &p
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    // Max with the lanes l ^ 16 and l ^ 32: a permlane swap leaves, in the
+    // two registers, the lane's own value and its partner's (in either
+    // order), so their max is the pairwise max.
+    {
+        const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(amax),
+                                                          __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+        const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax),
+                                                          __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    }
     const float s = amax / 7.0f;
     float inv = 0.0f;
     if (s != 0.0f) {

@@ -8,37 +8,40 @@
 
 namespace svdq {
 
-// Scratch of svdq_quantize_act_down, carved from the caller's workspace.
-struct DownWorkspace {
-    float *inv_lam;     // [K]
-    uint16_t *l1_hi;    // [r][K]  bf16 hi part of L1[k][i] / lambda[k], transposed
-    uint16_t *l1_lo;    // [r][K]  bf16 lo part
-};
-
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// inv_lam is always needed; the L1 parts only when r > 0.
-inline size_t down_workspace_bytes(int64_t K, int r) {
-    return align256((size_t)K * 4) + 2 * align256((size_t)K * (size_t)r * 2);
+// svdq_quantize_act_down splits K into chunks of kc groups (one workgroup per
+// 64 rows and chunk); with more than one chunk and r > 0 the chunks' partial
+// x^ L1 sums go to the workspace and a second kernel adds them up.  kc keeps
+// the chunk of L1 staged in LDS (kc x 64 x r bf16, r rounded up to 32, 64 or
+// 128) at 32 KB; the last chunk may hold fewer groups.
+inline int k1_chunk_groups(int r) { return r <= 32 ? 8 : (r <= 64 ? 4 : 2); }
+inline int k1_chunks(int64_t K, int r) {
+    const int64_t G = K / 64;
+    const int kc = k1_chunk_groups(r);
+    return (int)((G + kc - 1) / kc);
 }
 
-inline DownWorkspace carve_down_workspace(void *base, int64_t K, int r) {
-    DownWorkspace w{nullptr, nullptr, nullptr};
-    char *p = static_cast<char *>(base);
-    w.inv_lam = reinterpret_cast<float *>(p);
-    p += align256((size_t)K * 4);
-    if (r == 0) return w;
-    w.l1_hi = reinterpret_cast<uint16_t *>(p);
-    p += align256((size_t)K * (size_t)r * 2);
-    w.l1_lo = reinterpret_cast<uint16_t *>(p);
+// Scratch of svdq_quantize_act_down, carved from the caller's workspace.
+struct DownWorkspace {
+    float *part;        // [chunks][M][r] partial sums (null when not needed)
+};
+
+inline size_t down_workspace_bytes(int64_t M, int64_t K, int r) {
+    if (r <= 0 || M <= 0 || K < 64) return 0;
+    const int nc = k1_chunks(K, r);
+    return nc > 1 ? align256((size_t)nc * (size_t)M * (size_t)r * 4) : 0;
+}
+
+inline DownWorkspace carve_down_workspace(void *base, int64_t M, int64_t K, int r) {
+    DownWorkspace w{nullptr};
+    if (down_workspace_bytes(M, K, r) > 0) w.part = static_cast<float *>(base);
     return w;
 }
 
-hipError_t launch_prep_down(const float *lambda, const uint16_t *L1, int64_t K, int r,
-                            const DownWorkspace &ws, hipStream_t stream);
-hipError_t launch_quant_down(const uint16_t *X, int64_t M, int64_t K, int r,
-                             const DownWorkspace &ws, uint8_t *qa, float *sa, float *xl1,
-                             hipStream_t stream);
+hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                             int64_t M, int64_t K, int r, const DownWorkspace &ws, uint8_t *qa,
+                             float *sa, float *xl1, hipStream_t stream);
 hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
                                hipStream_t stream);
 // 0 auto, 1 full tiles only, 2 quarter tiles only (process-wide test hook)

@@ -100,11 +100,11 @@ int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, flo
                           void *stream);
 
 /*
- * Workspace bytes svdq_quantize_act_down needs: the reciprocal smoothing
- * factors and the transposed, smoothed low-rank factor L1 diag(lambda)^-1 as
- * a bf16 hi/lo pair (rebuilt on every call from lambda and L1).
+ * Workspace bytes svdq_quantize_act_down needs: when K spans more than one
+ * chunk of groups and r > 0, the chunks' partial fp32 sums of the
+ * down-projection (chunks x M x r floats, 256-byte aligned); otherwise 0.
  */
-size_t svdq_quantize_act_down_workspace_bytes(int64_t K, int32_t r);
+size_t svdq_quantize_act_down_workspace_bytes(int64_t M, int64_t K, int32_t r);
 
 /*
  * Smoothing, activation quantization and low-rank down-projection in one
@@ -117,8 +117,8 @@ size_t svdq_quantize_act_down_workspace_bytes(int64_t K, int32_t r);
  *   sa      device fp32 [M, K/64] group scales (out)
  *   xl1     device fp32 [M, r]   (X diag(lambda)^-1) L1, fp32 (out; NULL iff r == 0)
  *   workspace / ws_bytes  device scratch of at least
- *           svdq_quantize_act_down_workspace_bytes(K, r) bytes (may be NULL
- *           when that is 0)
+ *           svdq_quantize_act_down_workspace_bytes(M, K, r) bytes (may be
+ *           NULL when that is 0)
  * M >= 0 (0: no-op), K % 64 == 0, r in {0, 16, 32, ..., 128}.
  * qa and sa are bit-exact with the definition above; xl1 is accurate to
  * about 2^-16 relative per term (bf16 hi/lo products, fp32 sums).

@@ -49,9 +49,12 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_sizes(lib):
     K, r, M = 3072, 32, 4608
-    down = lib.svdq_quantize_act_down_workspace_bytes(K, r)
-    assert down == 4 * K + 2 * 2 * K * r          # all 256-aligned here
-    assert lib.svdq_quantize_act_down_workspace_bytes(K, 0) == 4 * K
+    down = lib.svdq_quantize_act_down_workspace_bytes(M, K, r)
+    assert down == 6 * M * r * 4                  # six chunks of 8 groups; 256-aligned here
+    assert lib.svdq_quantize_act_down_workspace_bytes(M, K, 0) == 0
+    assert lib.svdq_quantize_act_down_workspace_bytes(M, 512, 32) == 0     # one chunk
+    assert lib.svdq_quantize_act_down_workspace_bytes(M, 512, 128) == 4 * M * 128 * 4
+    assert lib.svdq_quantize_act_down_workspace_bytes(0, K, r) == 0
     lin = lib.svdq_linear_workspace_bytes(M, K, r)
     assert lin == M * K // 2 + M * (K // 64) * 4 + M * r * 4 + down
     assert lib.svdq_linear_workspace_bytes(-1, K, r) == 0
@@ -60,7 +63,7 @@ def test_workspace_sizes(lib):
 P = ctypes.c_void_p
 
 
-def _down(lib, X=A, lam=A, L1=A, M=16, K=128, r=16, qa=A, sa=A, xl1=A, ws=A, ws_bytes=1 << 20):
+def _down(lib, X=A, lam=A, L1=A, M=16, K=1024, r=16, qa=A, sa=A, xl1=A, ws=A, ws_bytes=1 << 20):
     return lib.svdq_quantize_act_down(P(X), P(lam), P(L1), M, K, r, P(qa), P(sa), P(xl1),
                                       P(ws), ws_bytes, None)
 

@@ -83,8 +83,8 @@ def test_canaries_untouched():
     sa_b, sa = _padded(M * G, torch.float32, -123.0)
     x_b, x1 = _padded(M * r, torch.float32, -321.0)
     y_b, y = _padded(M * N, torch.int16, 0x5A5A)
-    ws_bytes = bdt.svdq_quantize_act_down_workspace_bytes(K, r)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    ws_bytes = bdt.svdq_quantize_act_down_workspace_bytes(M, K, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda:0")
     bdt.svdq_quantize_act_down(bdt._bits(to_dev(L.X)), to_dev(L.lam), bdt._bits(to_dev(L.L1)),
                                M, K, r, qa, sa, x1, ws, ws_bytes)
     qw, sw = bdt.pack_weights(to_dev(L.R))
