@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="qkv", choices=["tiny", "qkv", "mlp_up", "mlp_down"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of a known size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     return ap.parse_args()
@@ -54,8 +56,46 @@ def k2_bytes(M, N, K, r):
             + 2 * M * N)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_lr_gemm_qkv_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "bit_diffusion_transformer_amd", "csrc", "w4a4_gemm.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM call from the committed counter summary, if it was
+    taken on this workload with the current kernel source; else None."""
+    import hashlib
+    if workload != "qkv" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != src or "traffic_bytes_per_call" not in kv:
+        return None
+    return int(float(kv["traffic_bytes_per_call"]))
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of a known size, for scaling FETCH_SIZE and
+    WRITE_SIZE counter readings to bytes."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the layer has no multi-GPU path in this build "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -168,8 +208,9 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = None
-    roof["kernel"] = "w4a4_lr_gemm_kernel"
+    roof["traffic"] = measured_traffic(args.workload) if args.M is None else None
+    roof["kernel"] = ("svdq_w4a4_lr_gemm: w4a4_lr_gemm_kernel<2> (128x128 tiles) and, for a "
+                      "partial last round, w4a4_lr_gemm_kernel<1> (64x64 tiles)")
     roof["avg_launch_us"] = round(t_gemm * 1e6, 2)
     roof["algorithmic_ops"] = ops
     roof["algorithmic_bytes"] = k2_bytes(M, N, K, r)
