@@ -352,38 +352,18 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
 
 }  // namespace
 
-// Tile `tile0 + blockIdx.x` (WB = 2, with the XCD-aware order when `xcd`) or
-// quarter blockIdx.x % 4 of tile `tile0 + blockIdx.x / 4` (WB = 1) of the
-// 128 x 128 tile grid.
+namespace {
+
+// One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0).
 template <int WB>
-__global__ void __launch_bounds__(NTHR)
-w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
-                    const uint8_t *__restrict__ qw, const float *__restrict__ sw,
-                    const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
-                    const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N,
-                    int64_t K, int r, uint16_t *__restrict__ Y, int64_t tile0, int64_t ntiles) {
+__device__ __forceinline__ void
+tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
+          const uint8_t *__restrict__ qw, const float *__restrict__ sw,
+          const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
+          const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N, int64_t K, int r,
+          uint16_t *__restrict__ Y, Smem<WB> &sm, int64_t m0, int64_t n0) {
     using C = Cfg<WB>;
     constexpr int BT = C::BT, NB = C::NB;
-    __shared__ Smem<WB> sm;
-    const int64_t nbm = (M + TILE - 1) / TILE, nbn = (N + TILE - 1) / TILE;
-    int64_t m0, n0;
-    {
-        int64_t b = blockIdx.x, tm, tn;
-        if (WB == 2) {
-            // Consecutive workgroups go to different XCDs (round robin over
-            // 8); give each XCD a contiguous range of tiles so the tiles
-            // sharing operands share that XCD's L2.
-            if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
-            raster(tile0 + b, nbm, nbn, tm, tn);
-            m0 = tm * TILE;
-            n0 = tn * TILE;
-        } else {
-            raster(tile0 + b / 4, nbm, nbn, tm, tn);
-            m0 = tm * TILE + 64 * (b & 1);
-            n0 = tn * TILE + 64 * ((b >> 1) & 1);
-            if (m0 >= M || n0 >= N) return;   // quadrant outside a ragged edge
-        }
-    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -530,6 +510,44 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
     }
 }
 
+}  // namespace
+
+// One launch covers the whole output.  Workgroups [0, nq) are quarter tiles
+// (64 x 64): quadrant b % 4 of tile tq0 + b / 4 of the 128 x 128 tile grid,
+// used for the tiles of a partial last round.  They come first so that they
+// run alongside the first round of full tiles instead of alone after the
+// last one.  Workgroups [nq, nq + nfull) are full tiles 0 .. nfull - 1, each
+// XCD taking a contiguous range of them (consecutive workgroups go to
+// different XCDs, round robin over 8) so that tiles sharing operands share
+// that XCD's L2.
+__global__ void __launch_bounds__(NTHR)
+w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
+                    const uint8_t *__restrict__ qw, const float *__restrict__ sw,
+                    const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
+                    const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N,
+                    int64_t K, int r, uint16_t *__restrict__ Y, int64_t nq, int64_t tq0,
+                    int64_t nfull) {
+    __shared__ union {
+        Smem<2> full;
+        Smem<1> quarter;
+    } sm;
+    const int64_t nbm = (M + TILE - 1) / TILE, nbn = (N + TILE - 1) / TILE;
+    int64_t b = blockIdx.x, tm, tn;
+    if (b < nq) {
+        raster(tq0 + b / 4, nbm, nbn, tm, tn);
+        const int64_t m0 = tm * TILE + 64 * (b & 1);
+        const int64_t n0 = tn * TILE + 64 * ((b >> 1) & 1);
+        if (m0 >= M || n0 >= N) return;   // quadrant outside a ragged edge
+        tile_body<1>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm.quarter, m0, n0);
+    } else {
+        b -= nq;
+        if ((nfull & 7) == 0) b = (b & 7) * (nfull >> 3) + (b >> 3);
+        raster(b, nbm, nbn, tm, tn);
+        tile_body<2>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm.full, tm * TILE,
+                     tn * TILE);
+    }
+}
+
 // Test hook: per-group integer sums with the GEMM's k split, operand
 // widening and int8 matrix instruction; one wave per 32 x 32 block of
 // (n, m), operands read from memory.
@@ -581,8 +599,8 @@ static int64_t wg_slots() {
 
 // Full 128 x 128 tiles for whole rounds of the device's workgroup slots; if
 // a partial last round is left of at most three quarters of the slots, its
-// tiles run as 64 x 64 quarter tiles in a second launch (four times the
-// workgroups, a quarter of the work each).
+// tiles run as 64 x 64 quarter tiles (four times the workgroups, a quarter
+// of the work each) in the same launch.
 hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
                             const float *sw, const float *xl1, const uint16_t *L2,
                             const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
@@ -598,12 +616,9 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
         if (rest * 4 > slots * 3) rest = 0;
     }
     const int64_t full = tiles - rest;
-    if (full > 0)
-        w4a4_lr_gemm_kernel<2><<<(unsigned)full, NTHR, 0, stream>>>(
-            qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, 0, full);
-    if (rest > 0)
-        w4a4_lr_gemm_kernel<1><<<(unsigned)(4 * rest), NTHR, 0, stream>>>(
-            qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, full, rest);
+    const int64_t nq = 4 * rest;
+    w4a4_lr_gemm_kernel<<<(unsigned)(nq + full), NTHR, 0, stream>>>(
+        qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, nq, full, full);
     return hipGetLastError();
 }
 
