@@ -34,10 +34,12 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="qkv", choices=["tiny", "qkv", "mlp_up", "mlp_down"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rank-overhead", action="store_true",
+                    help="skip the r = 0 timing loops (cleaner kernel traces)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of a known size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -175,7 +177,8 @@ def main():
                               rank, bits(s["Y"]), stream)
 
     def time_loop(fn, n):
-        for i in range(min(n, 5)):
+        # enough untimed calls for the clocks to settle after the previous loop
+        for i in range(20):
             fn(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -187,7 +190,8 @@ def main():
 
     n_k = max(args.steps, 20)
     t_gemm = time_loop(lambda i: gemm(i, r), n_k)
-    t_gemm_r0 = time_loop(lambda i: gemm(i, 0), n_k) if r > 0 else t_gemm
+    rank_loops = r > 0 and not args.no_rank_overhead
+    t_gemm_r0 = time_loop(lambda i: gemm(i, 0), n_k) if rank_loops else None
 
     def linear_r0(i):
         s = sets[i % nsets]
@@ -196,7 +200,7 @@ def main():
 
     t_quant = time_loop(quant, n_k)
     t_lin = time_loop(lambda i: step(sets[i % nsets]), n_k)
-    t_lin_r0 = time_loop(linear_r0, n_k) if r > 0 else t_lin
+    t_lin_r0 = time_loop(linear_r0, n_k) if rank_loops else None
     torch.cuda.synchronize()
 
     gemm_tops = ops / t_gemm / 1e12
@@ -232,7 +236,7 @@ def main():
                                   L.bias is not None),
                    "global_batch": M, "input_sets_rotated": nsets},
         "roofline": roof,
-        "rank_branch_overhead": {
+        "rank_branch_overhead": None if t_gemm_r0 is None else {
             "gemm_r%d_us" % r: round(t_gemm * 1e6, 2), "gemm_r0_us": round(t_gemm_r0 * 1e6, 2),
             "gemm_frac": round(t_gemm / t_gemm_r0 - 1, 4),
             "linear_r%d_us" % r: round(t_lin * 1e6, 2), "linear_r0_us": round(t_lin_r0 * 1e6, 2),

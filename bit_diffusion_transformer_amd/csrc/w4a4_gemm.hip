@@ -428,6 +428,34 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
 
     // ---- epilogue: rank-r up-projection on the same tile (bf16 MFMA, the
     // fp32 xl1 split into a bf16 hi/lo pair), then bias, activation, store.
+    // Its global loads go out together so that their latencies overlap: the
+    // lane's xl1 for the first 32 ranks, the bias of its columns, and the L2
+    // rows the workgroup stages as L2^T in LDS.
+    f32x4 xp[WB][2][2];                        // [bj][16-rank chunk][half]
+    if (r > 0) {
+#pragma unroll
+        for (int bj = 0; bj < WB; ++bj) {
+            const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+            const int64_t mc = m < M ? m : M - 1;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                if (16 * c < r) {
+                    const f32x4 *p = reinterpret_cast<const f32x4 *>(xl1 + mc * r + 16 * c + 8 * ks2);
+                    xp[bj][c][0] = p[0];
+                    xp[bj][c][1] = p[1];
+                }
+            }
+        }
+    }
+    u32x2 bb[WB][4];
+#pragma unroll
+    for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+            bb[bi][q] = (bias && n < N) ? *reinterpret_cast<const u32x2 *>(bias + n) : u32x2{0u, 0u};
+        }
+    }
     if (r > 0) {
         const int lstr = r + 8;   // bf16 elements per LDS row of L2^T
         uint16_t *l2t = sm.u.l2t;
@@ -447,7 +475,8 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
             *reinterpret_cast<u32x4 *>(&l2t[n * lstr + 8 * c]) = u32x4{v[0], v[1], v[2], v[3]};
         }
         __syncthreads();
-        for (int c16 = 0; c16 < r; c16 += 16) {
+        // 16 ranks: L2^T rows from LDS (A), xl1 hi/lo of the lane's rows (B).
+        auto chunk = [&](int c16, const f32x4 (&x)[WB][2]) {
             const int i0 = c16 + 8 * ks2;
             u32x4 AL[WB];
 #pragma unroll
@@ -457,11 +486,8 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
             }
 #pragma unroll
             for (int bj = 0; bj < WB; ++bj) {
-                const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
-                const int64_t mc = m < M ? m : M - 1;
-                const f32x4 *p = reinterpret_cast<const f32x4 *>(xl1 + mc * r + i0);
-                const f32x4 x0 = p[0], x1 = p[1];
-                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                const float xs[8] = {x[bj][0].x, x[bj][0].y, x[bj][0].z, x[bj][0].w,
+                                     x[bj][1].x, x[bj][1].y, x[bj][1].z, x[bj][1].w};
                 u32x4 hi, lo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -475,6 +501,30 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
                     acc[bi * WB + bj] = mfma_bf16_32x32x16(AL[bi], lo, acc[bi * WB + bj]);
                 }
             }
+        };
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if (16 * c < r) {
+                f32x4 x[WB][2];
+#pragma unroll
+                for (int bj = 0; bj < WB; ++bj) {
+                    x[bj][0] = xp[bj][c][0];
+                    x[bj][1] = xp[bj][c][1];
+                }
+                chunk(16 * c, x);
+            }
+        }
+        for (int c16 = 32; c16 < r; c16 += 16) {
+            f32x4 x[WB][2];
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) {
+                const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+                const int64_t mc = m < M ? m : M - 1;
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(xl1 + mc * r + c16 + 8 * ks2);
+                x[bj][0] = p[0];
+                x[bj][1] = p[1];
+            }
+            chunk(c16, x);
         }
     }
 
@@ -489,12 +539,8 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
         for (int q = 0; q < 4; ++q) {
             const int64_t n = n0 + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
             if (n >= N) continue;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias) {
-                const u32x2 b2 = *reinterpret_cast<const u32x2 *>(bias + n);
-                bv[0] = bf16_lo(b2.x); bv[1] = bf16_hi(b2.x);
-                bv[2] = bf16_lo(b2.y); bv[3] = bf16_hi(b2.y);
-            }
+            const u32x2 b2 = bb[bi][q];
+            const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
             float o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
