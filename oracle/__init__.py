@@ -22,6 +22,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "svdq_oracle.c")
+_SRC_AWQ = os.path.join(_HERE, "awq_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -34,7 +35,7 @@ def build(force: bool = True) -> str:
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, _SRC_AWQ, "-o", tmp, "-lm"]
     subprocess.check_call(cmd)
     os.replace(tmp, _LIB)
     return _LIB
@@ -61,8 +62,12 @@ def _load():
     lib.oracle_group_sums.argtypes = [P, P, I64, I64, I64, I64, I64, I64, I64, P]
     lib.oracle_gemm_rows.argtypes = [P, P, P, P, P, P, P, I32, I64, I64, I64, I32,
                                      P, I64, P, P]
+    lib.oracle_awq_quantize.argtypes = [P, I64, I64, P, P, P]
+    lib.oracle_awq_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_awq_linear_rows.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, P, P]
     for f in ("oracle_smooth", "oracle_quantize_groups", "oracle_unpack",
-              "oracle_down_proj", "oracle_group_sums", "oracle_gemm_rows"):
+              "oracle_down_proj", "oracle_group_sums", "oracle_gemm_rows",
+              "oracle_awq_quantize", "oracle_awq_dequant", "oracle_awq_linear_rows"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -199,6 +204,58 @@ def linear(X, lam, L1, qw, sw, L2, bias, act: int, rows=None):
     r = 0 if L1 is None else L1.shape[1]
     xl1 = down_proj(xh, L1) if r > 0 else None
     return gemm_rows(qa, sa, qw, sw, xl1, L2, bias, act, K, rows)
+
+
+# ---------------------------------------------------------------- W4A16 (awq_w4a16)
+
+def awq_quantize(W: np.ndarray):
+    """Group-64 asymmetric INT4 weights -> (packed uint8 [N, K/2], scales f32 [N, K/64],
+    zero points uint8 [N, K/64]).  Readings in awq_oracle.c."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    assert K % GROUP == 0
+    packed = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, K // GROUP), np.float32)
+    zeros = np.empty((N, K // GROUP), np.uint8)
+    if N > 0:
+        _load().oracle_awq_quantize(_ptr(W), N, K, _ptr(packed), _ptr(scales), _ptr(zeros))
+    return packed, scales, zeros
+
+
+def awq_dequant(packed, scales, zeros, K: int) -> np.ndarray:
+    """(q - z) * s in fp64 -> float64 [N, K]."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    N = packed.shape[0]
+    out = np.empty((N, K), np.float64)
+    if N > 0:
+        _load().oracle_awq_dequant(_ptr(packed), _ptr(scales), _ptr(zeros), N, K, _ptr(out))
+    return out
+
+
+def awq_linear(X, packed, scales, zeros, bias, rows: Optional[Sequence[int]] = None):
+    """Y = X W^T + bias of the W4A16 layer -> (acc f64 [R, N], y bf16 bits [R, N])."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+    M, K = X.shape
+    N = packed.shape[0]
+    if rows is None:
+        rows_arr, nrows = None, M
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = len(rows_arr)
+    acc = np.empty((nrows, N), np.float64)
+    y = np.empty((nrows, N), np.uint16)
+    if nrows > 0 and N > 0:
+        _load().oracle_awq_linear_rows(_ptr(X), _ptr(packed), _ptr(scales), _ptr(zeros),
+                                       _ptr(bias), M, N, K, _ptr(rows_arr), nrows, _ptr(acc),
+                                       _ptr(y))
+    return acc, y
 
 
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
