@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="qkv", choices=["tiny", "qkv", "mlp_up", "mlp_down"])
+    ap.add_argument("--workload", default="qkv",
+                    choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-overhead", action="store_true",
@@ -93,10 +94,97 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
 
 
+def bench_awq(args):
+    """The W4A16 (awq_w4a16) modulation projection: one step = one svdq_awq_w4a16_linear
+    call; HBM-bound, so the metric is GB/s of its algorithmic bytes."""
+    import torch
+
+    import bit_diffusion_transformer_amd as bdt
+    from synth import AWQ_CONFIGS, make_awq_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    spec = AWQ_CONFIGS[args.workload]
+    L = make_awq_layer(spec, seed=0, M=args.M)
+    M, K, N = L.spec.M, L.spec.K, L.spec.N
+    G = K // 64
+    W = torch.from_numpy(L.W).to(dev)
+    qw, sc, zp = bdt.awq_pack_weights(W)
+    del W
+    X = torch.from_numpy(L.X.view(np.int16).copy()).to(dev)
+    bias = torch.from_numpy(L.bias.view(np.int16).copy()).to(dev) if L.bias is not None else None
+    nbytes = 2 * M * K + N * K // 2 + 4 * N * G + N * G + (2 * N if bias is not None else 0) \
+        + 2 * M * N
+    nsets = max(2, int(np.ceil(2 * CACHE_BYTES / nbytes)))
+    sets = [(X.clone(), qw.clone(), sc.clone(), zp.clone(),
+             bias.clone() if bias is not None else None,
+             torch.empty((M, N), dtype=torch.int16, device=dev)) for _ in range(nsets)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        x, q, s_, z, b, y = sets[i % nsets]
+        bdt.svdq_awq_w4a16_linear(x, q, s_, z, b, M, N, K, y, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    for i in range(20):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_k = max(args.steps, 50)
+    e0.record(stream)
+    for i in range(n_k):
+        step(i)
+    e1.record(stream)
+    e1.synchronize()
+    t_k = e0.elapsed_time(e1) / 1e3 / n_k
+    gbs = nbytes / t_step / 1e9
+    out = {
+        "metric": "GB/s (algorithmic bytes / t) of the W4A16 modulation projection",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded conditioning vectors and random weights of the stated shape)",
+        "config": {"workload": "%s: M=%d K=%d N=%d group=64 bias=%s"
+                               % (spec.name, M, K, N, bias is not None),
+                   "global_batch": M, "input_sets_rotated": nsets},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / t_k / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / t_k / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "awq_linear_kernel", "avg_launch_us": round(t_k * 1e6, 2),
+                     "algorithmic_bytes": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        oracle.set_threads(cores)
+        q, s_, z = oracle.awq_quantize(L.W)
+        t0 = time.perf_counter()
+        oracle.awq_linear(L.X, q, s_, z, L.bias)
+        tc = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(nbytes / tc / 1e9, 3), "unit": "GB/s",
+                               "cores": cores, "kind": "oracle",
+                               "sample": "the whole layer (all %d rows), %.2f s" % (M, tc)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.workload.startswith("awq"):
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only (--gpus %d requested)" % args.gpus,
+                  file=sys.stderr)
+            sys.exit(2)
+        bench_awq(args)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the layer has no multi-GPU path in this build "

@@ -17,7 +17,8 @@ import torch
 
 from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError,  # noqa: F401
                        TILES_AUTO, TILES_FULL, TILES_QUARTER,
-                       load_library, svdq_abi_version, svdq_debug_group_sums,
+                       load_library, svdq_abi_version, svdq_awq_pack_weights,
+                       svdq_awq_w4a16_linear, svdq_debug_group_sums,
                        svdq_debug_set_tile_policy,
                        svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
                        svdq_pack_weights, svdq_quantize_act_down,
@@ -47,6 +48,25 @@ def pack_weights(R: torch.Tensor):
     sw = torch.empty((N, K // GROUP), dtype=torch.float32, device=R.device)
     svdq_pack_weights(R, N, K, qw, sw)
     return qw, sw
+
+
+def awq_pack_weights(W: torch.Tensor):
+    """fp32 weight [N, K] -> (qw uint8 [N, K/2], scales fp32 [N, K/64], zeros uint8 [N, K/64])."""
+    N, K = W.shape
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, K // GROUP), dtype=torch.float32, device=W.device)
+    zeros = torch.empty((N, K // GROUP), dtype=torch.uint8, device=W.device)
+    svdq_awq_pack_weights(W, N, K, qw, scales, zeros)
+    return qw, scales, zeros
+
+
+def awq_linear(X: torch.Tensor, qw, scales, zeros, bias=None) -> torch.Tensor:
+    """W4A16 layer: X bf16 [M, K] -> Y bf16 [M, N]."""
+    M, K = X.shape
+    N = qw.shape[0]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    svdq_awq_w4a16_linear(_bits(X), qw, scales, zeros, _bits(bias), M, N, K, _bits(Y))
+    return Y
 
 
 def quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Tensor]):

@@ -29,7 +29,7 @@ EXPORTS = (
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_pack_weights",
     "svdq_quantize_act_down_workspace_bytes", "svdq_quantize_act_down", "svdq_w4a4_lr_gemm",
     "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
-    "svdq_debug_set_tile_policy",
+    "svdq_debug_set_tile_policy", "svdq_awq_pack_weights", "svdq_awq_w4a16_linear",
 )
 
 
@@ -66,6 +66,8 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_linear": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, SZ, P], I32),
         "svdq_debug_group_sums": ([P, P, I64, I64, I64, I64, I64, I64, I64, P, P], I32),
         "svdq_debug_set_tile_policy": ([I32], I32),
+        "svdq_awq_pack_weights": ([P, I64, I64, P, P, P, P], I32),
+        "svdq_awq_w4a16_linear": ([P, P, P, P, P, I64, I64, I64, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -155,3 +157,14 @@ TILES_AUTO, TILES_FULL, TILES_QUARTER = 0, 1, 2
 
 def svdq_debug_set_tile_policy(policy):
     _check(load_library().svdq_debug_set_tile_policy(policy), "svdq_debug_set_tile_policy")
+
+
+def svdq_awq_pack_weights(W, N, K, qw, scales, zeros, stream=None):
+    _check(load_library().svdq_awq_pack_weights(_p(W), N, K, _p(qw), _p(scales), _p(zeros),
+                                                _stream(stream)), "svdq_awq_pack_weights")
+
+
+def svdq_awq_w4a16_linear(X, qw, scales, zeros, bias, M, N, K, Y, stream=None):
+    _check(load_library().svdq_awq_w4a16_linear(_p(X), _p(qw), _p(scales), _p(zeros), _p(bias),
+                                                M, N, K, _p(Y), _stream(stream)),
+           "svdq_awq_w4a16_linear")

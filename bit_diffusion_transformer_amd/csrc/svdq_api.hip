@@ -297,7 +297,6 @@ int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, i
                       "group_sums launch");
 }
 
-}  // extern "C"
 
 int32_t svdq_debug_set_tile_policy(int32_t policy) {
     g_last_error[0] = 0;
@@ -306,3 +305,40 @@ int32_t svdq_debug_set_tile_policy(int32_t policy) {
     svdq::set_tile_policy(policy);
     return SVDQ_OK;
 }
+
+int32_t svdq_awq_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *qw, float *scales,
+                              uint8_t *zeros, void *stream) {
+    g_last_error[0] = 0;
+    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+    SVDQ_TRY(check_k(K));
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(W, "W"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(scales, "scales"));
+    SVDQ_TRY(need_ptr(zeros, "zeros"));
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_awq_pack(W, N, K, qw, scales, zeros, (hipStream_t)stream),
+                      "awq_pack launch");
+}
+
+int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *qw, const float *scales,
+                              const uint8_t *zeros, const uint16_t *bias, int64_t M, int64_t N,
+                              int64_t K, uint16_t *Y, void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_n(N));
+    SVDQ_TRY(check_k(K));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(X, "X"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(scales, "scales"));
+    SVDQ_TRY(need_ptr(zeros, "zeros"));
+    SVDQ_TRY(need_ptr(Y, "Y"));
+    if (bias && !aligned16(bias)) return fail(SVDQ_ERR_MISALIGNED, "bias is not 16-byte aligned");
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_awq_linear(X, qw, scales, zeros, bias, M, N, K, Y,
+                                              (hipStream_t)stream),
+                      "awq_w4a16_linear launch");
+}
+
+}  // extern "C"

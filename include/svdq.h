@@ -171,6 +171,44 @@ int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, i
                               int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
                               int32_t *S, void *stream);
 
+/* ------------------------------------------------------------------
+ * 4-bit weights, 16-bit activations (W4A16).  The blog "Bringing Nunchaku
+ * 4-bit inference to Diffusers", section "Introducing Nunchaku Lite", names
+ * this second layer kind (awq_w4a16) for the adaptive-normalization and
+ * modulation projections; its quantization_config gives int4 and group
+ * size 64.  The pages fix no more than that; the format here: asymmetric
+ * codes q in [0, 15] per group of 64 along K, an fp32 scale s and a u8
+ * zero point z per (row, group), weight = (q - z) s, over a range that
+ * always contains zero.
+ * ------------------------------------------------------------------ */
+
+/*
+ * Offline quantization of the fp32 weight W [N, K] (row n = output n):
+ *   qw      device u8   [N, K/2]  codes, element 2j in the low nibble of byte j (out)
+ *   scales  device fp32 [N, K/64] s = fl32(fl32(hi - lo) / 15) with
+ *                                 lo = min(0, min w), hi = max(0, max w) (out)
+ *   zeros   device u8   [N, K/64] z = clamp(rint(fl32(-lo fl32(1/s))), 0, 15) (out)
+ * Codes q = clamp(rint(fl32(w fl32(1/s))) + z, 0, 15), ties to even; a
+ * zero scale or a non-finite 1/s gives q = z = 0.  N >= 0 (0: no-op),
+ * K % 64 == 0.  Bit-exact with that definition.
+ */
+int32_t svdq_awq_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *qw, float *scales,
+                              uint8_t *zeros, void *stream);
+
+/*
+ * Y = X Wq^T + bias with Wq = (q - z) s from svdq_awq_pack_weights.
+ *   X       device bf16 [M, K]
+ *   qw, scales, zeros  as above
+ *   bias    device bf16 [N] or NULL
+ *   Y       device bf16 [M, N] (out)
+ * M >= 0 (0: no-op; made for small M, any M works), N % 8 == 0, K % 64 == 0.
+ * Products exact, fp32 sums; accurate to 1 bf16 ulp + 1e-3 rms of the
+ * fp64 result.
+ */
+int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *qw, const float *scales,
+                              const uint8_t *zeros, const uint16_t *bias, int64_t M, int64_t N,
+                              int64_t K, uint16_t *Y, void *stream);
+
 /*
  * Test hook: how svdq_w4a4_lr_gemm (and svdq_linear) tile the output.
  *   SVDQ_TILES_AUTO    128 x 128 tiles for whole rounds of the device's

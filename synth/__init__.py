@@ -49,6 +49,7 @@ import numpy as np
 __all__ = [
     "LayerSpec", "CONFIGS", "make_layer", "make_config_layers",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "DIT_CHAIN",
+    "AwqSpec", "AWQ_CONFIGS", "make_awq_layer",
 ]
 
 
@@ -223,3 +224,47 @@ def make_config_layers(name: str, seed: int = 0, M: Optional[int] = None):
     if name == "chain":
         return [make_layer(s, seed, M=M) for s in DIT_CHAIN]
     return [make_layer(CONFIGS[name], seed, M=M)]
+
+
+# ---------------------------------------------------------------- W4A16 (awq_w4a16)
+# The modulation projection of a DiT block (adaptive layer norm): a few
+# conditioning vectors (one per image in the batch; SiLU of a normal, as the
+# projection's input is the SiLU of the timestep / text embedding) against a
+# 3072 -> 6 x 3072 weight (shift, scale and gate for attention and MLP).
+
+@dataclass
+class AwqSpec:
+    name: str
+    M: int
+    K: int
+    N: int
+    bias: bool = True
+    cfg_id: int = 20
+
+
+AWQ_CONFIGS = {
+    "awq_mod": AwqSpec("awq_mod", 2, 3072, 18432, cfg_id=20),
+    "awq_mod_single": AwqSpec("awq_mod_single", 2, 3072, 9216, cfg_id=21),
+}
+
+
+@dataclass
+class AwqLayer:
+    spec: AwqSpec
+    X: np.ndarray               # uint16 [M, K] bf16 bits
+    W: np.ndarray               # float32 [N, K]
+    bias: Optional[np.ndarray]  # uint16 [N] or None
+
+
+def make_awq_layer(spec: AwqSpec, seed: int = 0, M: Optional[int] = None) -> AwqLayer:
+    """Seeded inputs of a W4A16 layer: X = SiLU(N(0,1)) in bf16; W rows N(0, 1/K)
+    with a per-row spread of 4x; bias N(0, 0.02)."""
+    M = spec.M if M is None else M
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, spec.cfg_id, 0])))
+    z = rng.standard_normal((M, spec.K))
+    X = _to_bf16(z / (1.0 + np.exp(-z)))
+    row = np.exp(rng.uniform(-np.log(2.0), np.log(2.0), size=(spec.N, 1)))
+    W = (rng.standard_normal((spec.N, spec.K)) * (row / np.sqrt(spec.K))).astype(np.float32)
+    bias = _to_bf16(0.02 * rng.standard_normal(spec.N)) if spec.bias else None
+    return AwqLayer(AwqSpec(spec.name, M, spec.K, spec.N, spec.bias, spec.cfg_id),
+                    np.ascontiguousarray(X), np.ascontiguousarray(W), bias)
