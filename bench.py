@@ -107,24 +107,21 @@ def bench_awq(args):
     spec = AWQ_CONFIGS[args.workload]
     L = make_awq_layer(spec, seed=0, M=args.M)
     M, K, N = L.spec.M, L.spec.K, L.spec.N
-    G = K // 64
     W = torch.from_numpy(L.W).to(dev)
-    qw, sc, zp = bdt.awq_pack_weights(W)
+    packed = bdt.awq_pack_weights(W)
     del W
     X = torch.from_numpy(L.X.view(np.int16).copy()).to(dev)
     bias = torch.from_numpy(L.bias.view(np.int16).copy()).to(dev) if L.bias is not None else None
-    nbytes = 2 * M * K + N * K // 2 + 4 * N * G + N * G + (2 * N if bias is not None else 0) \
-        + 2 * M * N
+    nbytes = 2 * M * K + packed.numel() + (2 * N if bias is not None else 0) + 2 * M * N
     nsets = max(2, int(np.ceil(2 * CACHE_BYTES / nbytes)))
-    sets = [(X.clone(), qw.clone(), sc.clone(), zp.clone(),
-             bias.clone() if bias is not None else None,
+    sets = [(X.clone(), packed.clone(), bias.clone() if bias is not None else None,
              torch.empty((M, N), dtype=torch.int16, device=dev)) for _ in range(nsets)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step(i):
-        x, q, s_, z, b, y = sets[i % nsets]
-        bdt.svdq_awq_w4a16_linear(x, q, s_, z, b, M, N, K, y, stream)
+        x, p, b, y = sets[i % nsets]
+        bdt.svdq_awq_w4a16_linear(x, p, b, M, N, K, y, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -151,8 +148,8 @@ def bench_awq(args):
         "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded conditioning vectors and random weights of the stated shape)",
-        "config": {"workload": "%s: M=%d K=%d N=%d group=64 bias=%s"
-                               % (spec.name, M, K, N, bias is not None),
+        "config": {"workload": "%s: M=%d K=%d N=%d group=64 bias=%s (W4A16 records, %d B)"
+                               % (spec.name, M, K, N, bias is not None, packed.numel()),
                    "global_batch": M, "input_sets_rotated": nsets},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / t_k / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -18,6 +18,7 @@ import torch
 from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError,  # noqa: F401
                        TILES_AUTO, TILES_FULL, TILES_QUARTER,
                        load_library, svdq_abi_version, svdq_awq_pack_weights,
+                       svdq_awq_packed_bytes, svdq_awq_repack,
                        svdq_awq_w4a16_linear, svdq_debug_group_sums,
                        svdq_debug_set_tile_policy,
                        svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
@@ -50,22 +51,27 @@ def pack_weights(R: torch.Tensor):
     return qw, sw
 
 
-def awq_pack_weights(W: torch.Tensor):
-    """fp32 weight [N, K] -> (qw uint8 [N, K/2], scales fp32 [N, K/64], zeros uint8 [N, K/64])."""
+def awq_pack_weights(W: torch.Tensor) -> torch.Tensor:
+    """fp32 weight [N, K] -> the W4A16 records (uint8, svdq_awq_packed_bytes(N, K) bytes)."""
     N, K = W.shape
-    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
-    scales = torch.empty((N, K // GROUP), dtype=torch.float32, device=W.device)
-    zeros = torch.empty((N, K // GROUP), dtype=torch.uint8, device=W.device)
-    svdq_awq_pack_weights(W, N, K, qw, scales, zeros)
-    return qw, scales, zeros
+    packed = torch.empty(svdq_awq_packed_bytes(N, K), dtype=torch.uint8, device=W.device)
+    svdq_awq_pack_weights(W, N, K, packed)
+    return packed
 
 
-def awq_linear(X: torch.Tensor, qw, scales, zeros, bias=None) -> torch.Tensor:
-    """W4A16 layer: X bf16 [M, K] -> Y bf16 [M, N]."""
+def awq_repack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor) -> torch.Tensor:
+    """Row-major codes uint8 [N, K/2], scales fp32 [N, K/64], zeros uint8 [N, K/64] -> records."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    packed = torch.empty(svdq_awq_packed_bytes(N, K), dtype=torch.uint8, device=codes.device)
+    svdq_awq_repack(codes, scales, zeros, N, K, packed)
+    return packed
+
+
+def awq_linear(X: torch.Tensor, packed: torch.Tensor, N: int, bias=None) -> torch.Tensor:
+    """W4A16 layer: X bf16 [M, K] -> Y bf16 [M, N] (packed from awq_pack_weights / awq_repack)."""
     M, K = X.shape
-    N = qw.shape[0]
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
-    svdq_awq_w4a16_linear(_bits(X), qw, scales, zeros, _bits(bias), M, N, K, _bits(Y))
+    svdq_awq_w4a16_linear(_bits(X), packed, _bits(bias), M, N, K, _bits(Y))
     return Y
 
 

@@ -29,7 +29,8 @@ EXPORTS = (
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_pack_weights",
     "svdq_quantize_act_down_workspace_bytes", "svdq_quantize_act_down", "svdq_w4a4_lr_gemm",
     "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
-    "svdq_debug_set_tile_policy", "svdq_awq_pack_weights", "svdq_awq_w4a16_linear",
+    "svdq_debug_set_tile_policy", "svdq_awq_packed_bytes", "svdq_awq_pack_weights",
+    "svdq_awq_repack", "svdq_awq_w4a16_linear",
 )
 
 
@@ -66,8 +67,10 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_linear": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, SZ, P], I32),
         "svdq_debug_group_sums": ([P, P, I64, I64, I64, I64, I64, I64, I64, P, P], I32),
         "svdq_debug_set_tile_policy": ([I32], I32),
-        "svdq_awq_pack_weights": ([P, I64, I64, P, P, P, P], I32),
-        "svdq_awq_w4a16_linear": ([P, P, P, P, P, I64, I64, I64, P, P], I32),
+        "svdq_awq_packed_bytes": ([I64, I64], I64),
+        "svdq_awq_pack_weights": ([P, I64, I64, P, P], I32),
+        "svdq_awq_repack": ([P, P, P, I64, I64, P, P], I32),
+        "svdq_awq_w4a16_linear": ([P, P, P, I64, I64, I64, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -159,12 +162,20 @@ def svdq_debug_set_tile_policy(policy):
     _check(load_library().svdq_debug_set_tile_policy(policy), "svdq_debug_set_tile_policy")
 
 
-def svdq_awq_pack_weights(W, N, K, qw, scales, zeros, stream=None):
-    _check(load_library().svdq_awq_pack_weights(_p(W), N, K, _p(qw), _p(scales), _p(zeros),
-                                                _stream(stream)), "svdq_awq_pack_weights")
+def svdq_awq_packed_bytes(N, K):
+    return int(load_library().svdq_awq_packed_bytes(N, K))
 
 
-def svdq_awq_w4a16_linear(X, qw, scales, zeros, bias, M, N, K, Y, stream=None):
-    _check(load_library().svdq_awq_w4a16_linear(_p(X), _p(qw), _p(scales), _p(zeros), _p(bias),
-                                                M, N, K, _p(Y), _stream(stream)),
-           "svdq_awq_w4a16_linear")
+def svdq_awq_pack_weights(W, N, K, packed, stream=None):
+    _check(load_library().svdq_awq_pack_weights(_p(W), N, K, _p(packed), _stream(stream)),
+           "svdq_awq_pack_weights")
+
+
+def svdq_awq_repack(codes, scales, zeros, N, K, packed, stream=None):
+    _check(load_library().svdq_awq_repack(_p(codes), _p(scales), _p(zeros), N, K, _p(packed),
+                                          _stream(stream)), "svdq_awq_repack")
+
+
+def svdq_awq_w4a16_linear(X, packed, bias, M, N, K, Y, stream=None):
+    _check(load_library().svdq_awq_w4a16_linear(_p(X), _p(packed), _p(bias), M, N, K, _p(Y),
+                                                _stream(stream)), "svdq_awq_w4a16_linear")

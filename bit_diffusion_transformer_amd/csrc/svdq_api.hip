@@ -173,6 +173,37 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r) {
 
 }  // namespace
 
+namespace {
+
+int32_t check_awq_pack_shape(int64_t N, int64_t K) {
+    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+    SVDQ_TRY(check_k(K));
+    if (N > 0) SVDQ_TRY(check_n(N));
+    return SVDQ_OK;
+}
+
+// Per-device cache of the per-workgroup LDS limit.
+std::atomic<int64_t> g_lds_limit[kMaxDevices];
+
+int32_t lds_limit(size_t *out) {
+    int dev = -1;
+    SVDQ_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SVDQ_ERR_HIP, "device index %d out of range", dev);
+    int64_t v = g_lds_limit[dev].load();
+    if (v <= 0) {
+        int bytes = 0;
+        SVDQ_TRY(hip_status(
+            hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev),
+            "hipDeviceGetAttribute(MaxSharedMemoryPerBlock)"));
+        v = bytes;
+        g_lds_limit[dev].store(v);
+    }
+    *out = (size_t)v;
+    return SVDQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
@@ -306,39 +337,60 @@ int32_t svdq_debug_set_tile_policy(int32_t policy) {
     return SVDQ_OK;
 }
 
-int32_t svdq_awq_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *qw, float *scales,
-                              uint8_t *zeros, void *stream) {
+int64_t svdq_awq_packed_bytes(int64_t N, int64_t K) {
+    if (N < 0 || K < SVDQ_GROUP || K % SVDQ_GROUP != 0) return 0;
+    return svdq::awq_packed_bytes(N, K);
+}
+
+
+int32_t svdq_awq_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *packed, void *stream) {
     g_last_error[0] = 0;
-    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
-    SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_awq_pack_shape(N, K));
     if (N == 0) return SVDQ_OK;
     SVDQ_TRY(need_ptr(W, "W"));
-    SVDQ_TRY(need_ptr(qw, "qw"));
-    SVDQ_TRY(need_ptr(scales, "scales"));
-    SVDQ_TRY(need_ptr(zeros, "zeros"));
+    SVDQ_TRY(need_ptr(packed, "packed"));
     SVDQ_TRY(check_device());
-    return hip_status(svdq::launch_awq_pack(W, N, K, qw, scales, zeros, (hipStream_t)stream),
+    return hip_status(svdq::launch_awq_pack(W, N, K, packed, (hipStream_t)stream),
                       "awq_pack launch");
 }
 
-int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *qw, const float *scales,
-                              const uint8_t *zeros, const uint16_t *bias, int64_t M, int64_t N,
-                              int64_t K, uint16_t *Y, void *stream) {
+int32_t svdq_awq_repack(const uint8_t *codes, const float *scales, const uint8_t *zeros,
+                        int64_t N, int64_t K, uint8_t *packed, void *stream) {
+    g_last_error[0] = 0;
+    SVDQ_TRY(check_awq_pack_shape(N, K));
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(codes, "codes"));
+    SVDQ_TRY(need_ptr(scales, "scales"));
+    if (!zeros) return fail(SVDQ_ERR_INVALID_ARG, "zeros must not be NULL");
+    SVDQ_TRY(need_ptr(packed, "packed"));
+    SVDQ_TRY(check_device());
+    return hip_status(
+        svdq::launch_awq_repack(codes, scales, zeros, N, K, packed, (hipStream_t)stream),
+        "awq_repack launch");
+}
+
+int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_t *bias,
+                              int64_t M, int64_t N, int64_t K, uint16_t *Y, void *stream) {
     g_last_error[0] = 0;
     if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
     SVDQ_TRY(check_n(N));
     SVDQ_TRY(check_k(K));
     if (M == 0) return SVDQ_OK;
     SVDQ_TRY(need_ptr(X, "X"));
-    SVDQ_TRY(need_ptr(qw, "qw"));
-    SVDQ_TRY(need_ptr(scales, "scales"));
-    SVDQ_TRY(need_ptr(zeros, "zeros"));
+    SVDQ_TRY(need_ptr(packed, "packed"));
     SVDQ_TRY(need_ptr(Y, "Y"));
     if (bias && !aligned16(bias)) return fail(SVDQ_ERR_MISALIGNED, "bias is not 16-byte aligned");
     SVDQ_TRY(check_device());
-    return hip_status(svdq::launch_awq_linear(X, qw, scales, zeros, bias, M, N, K, Y,
-                                              (hipStream_t)stream),
-                      "awq_w4a16_linear launch");
+    size_t limit = 0;
+    SVDQ_TRY(lds_limit(&limit));
+    const int MT = svdq::awq_rows_per_pass(K, limit);
+    if (MT < 1)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
+                    "K = %lld: one activation row does not fit the %zu-byte workgroup LDS",
+                    (long long)K, limit);
+    return hip_status(
+        svdq::launch_awq_linear(X, packed, bias, M, N, K, MT, Y, (hipStream_t)stream),
+        "awq_w4a16_linear launch");
 }
 
 }  // extern "C"

@@ -44,11 +44,15 @@ hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint1
                              float *sa, float *xl1, hipStream_t stream);
 hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
                                hipStream_t stream);
-hipError_t launch_awq_pack(const float *W, int64_t N, int64_t K, uint8_t *qw, float *scales,
-                           uint8_t *zeros, hipStream_t stream);
-hipError_t launch_awq_linear(const uint16_t *X, const uint8_t *qw, const float *scales,
-                             const uint8_t *zeros, const uint16_t *bias, int64_t M, int64_t N,
-                             int64_t K, uint16_t *Y, hipStream_t stream);
+// W4A16 records (16 columns x 4 groups each)
+int64_t awq_packed_bytes(int64_t N, int64_t K);
+int awq_rows_per_pass(int64_t K, size_t lds_limit);   // activation rows staged per workgroup
+hipError_t launch_awq_pack(const float *W, int64_t N, int64_t K, uint8_t *rec, hipStream_t stream);
+hipError_t launch_awq_repack(const uint8_t *codes, const float *scales, const uint8_t *zeros,
+                             int64_t N, int64_t K, uint8_t *rec, hipStream_t stream);
+hipError_t launch_awq_linear(const uint16_t *X, const uint8_t *rec, const uint16_t *bias,
+                             int64_t M, int64_t N, int64_t K, int MT, uint16_t *Y,
+                             hipStream_t stream);
 
 // 0 auto, 1 full tiles only, 2 quarter tiles only (process-wide test hook)
 void set_tile_policy(int policy);

@@ -183,31 +183,60 @@ int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, i
  * ------------------------------------------------------------------ */
 
 /*
- * Offline quantization of the fp32 weight W [N, K] (row n = output n):
- *   qw      device u8   [N, K/2]  codes, element 2j in the low nibble of byte j (out)
- *   scales  device fp32 [N, K/64] s = fl32(fl32(hi - lo) / 15) with
- *                                 lo = min(0, min w), hi = max(0, max w) (out)
- *   zeros   device u8   [N, K/64] z = clamp(rint(fl32(-lo fl32(1/s))), 0, 15) (out)
- * Codes q = clamp(rint(fl32(w fl32(1/s))) + z, 0, 15), ties to even; a
- * zero scale or a non-finite 1/s gives q = z = 0.  N >= 0 (0: no-op),
- * K % 64 == 0.  Bit-exact with that definition.
+ * The packed W4A16 weight ("records").  The columns are cut into NB =
+ * ceil(N/16) blocks of 16 and K into GQ = ceil(K/256) quads of 4 groups;
+ * block b, quad t is one 2368-byte record at byte (b * GQ + t) * 2368.  For
+ * column c = n - 16 b, group j = g - 4 t and k = 64 g + 16 s + 8 h + e
+ * (s, h, e in [0,4) x [0,2) x [0,8)):
+ *   code   in the 32-bit word at byte 1024 (j / 2) + 16 (c + 16 s)
+ *          + 8 (j % 2) + 4 h, nibble e / 2 + 4 (e % 2)
+ *   scale  fp32 at byte 2048 + 16 c + 4 j
+ *   zero   u8 at byte 2304 + 4 c + j
+ * Columns past N and groups past K/64 hold zero codes, scales and zeros.
+ * This is the order in which one 64-lane matrix-core pass consumes them, so
+ * every load of the linear is a contiguous run.
+ * Size in bytes of the records for an N x K weight (0 for bad shapes).
  */
-int32_t svdq_awq_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *qw, float *scales,
-                              uint8_t *zeros, void *stream);
+int64_t svdq_awq_packed_bytes(int64_t N, int64_t K);
 
 /*
- * Y = X Wq^T + bias with Wq = (q - z) s from svdq_awq_pack_weights.
+ * Offline quantization of the fp32 weight W [N, K] (row n = output n) into
+ * records (device, svdq_awq_packed_bytes(N, K) bytes, out), per group:
+ *   s = fl32(fl32(hi - lo) / 15) with lo = min(0, min w), hi = max(0, max w),
+ *   z = clamp(rint(fl32(-lo fl32(1/s))), 0, 15),
+ *   q = clamp(rint(fl32(w fl32(1/s))) + z, 0, 15), ties to even;
+ * a zero scale or a non-finite 1/s gives q = z = 0.  N >= 0 (0: no-op),
+ * N % 8 == 0, K % 64 == 0.  Bit-exact with that definition.
+ */
+int32_t svdq_awq_pack_weights(const float *W, int64_t N, int64_t K, uint8_t *packed,
+                              void *stream);
+
+/*
+ * Records from an already quantized weight in the common row-major form:
+ *   codes   device u8   [N, K/2]  element 2j in the low nibble of byte j
+ *   scales  device fp32 [N, K/64]
+ *   zeros   device u8   [N, K/64] in [0, 15] (not checked)
+ *   packed  device, svdq_awq_packed_bytes(N, K) bytes (out)
+ * Same shape rules as svdq_awq_pack_weights; a pure re-arrangement.
+ */
+int32_t svdq_awq_repack(const uint8_t *codes, const float *scales, const uint8_t *zeros,
+                        int64_t N, int64_t K, uint8_t *packed, void *stream);
+
+/*
+ * Y = X Wq^T + bias with Wq = (q - z) s from the records.
  *   X       device bf16 [M, K]
- *   qw, scales, zeros  as above
+ *   packed  device records of svdq_awq_pack_weights / svdq_awq_repack
  *   bias    device bf16 [N] or NULL
  *   Y       device bf16 [M, N] (out)
- * M >= 0 (0: no-op; made for small M, any M works), N % 8 == 0, K % 64 == 0.
- * Products exact, fp32 sums; accurate to 1 bf16 ulp + 1e-3 rms of the
- * fp64 result.
+ * M >= 0 (0: no-op; made for small M, where the weight stream dominates;
+ * rows are taken 16 at a time, each 16 re-reading the weight), N % 8 == 0,
+ * K % 64 == 0 with 16 activation rows of K fitting the device's
+ * per-workgroup LDS (fewer rows per pass otherwise; SVDQ_ERR_UNSUPPORTED_SHAPE
+ * when not even one fits).  Products exact, fp32 sums; accurate to 1 bf16
+ * ulp + 1e-3 rms of the fp64 result.  Deterministic.
  */
-int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *qw, const float *scales,
-                              const uint8_t *zeros, const uint16_t *bias, int64_t M, int64_t N,
-                              int64_t K, uint16_t *Y, void *stream);
+int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_t *bias,
+                              int64_t M, int64_t N, int64_t K, uint16_t *Y, void *stream);
 
 /*
  * Test hook: how svdq_w4a4_lr_gemm (and svdq_linear) tile the output.

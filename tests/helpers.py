@@ -59,3 +59,32 @@ def xl1_bound(xh: np.ndarray, L1_bits: np.ndarray) -> np.ndarray:
     K = xh.shape[1]
     mag = np.abs(xh.astype(np.float64)) @ np.abs(bf16_f64(L1_bits))
     return (2.0 ** -15 + K * 2.0 ** -24) * mag + 1e-30
+
+
+def awq_records(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, N: int, K: int) -> np.ndarray:
+    """The W4A16 records (the byte layout documented with svdq_awq_packed_bytes in svdq.h),
+    built on the host from row-major codes [N, K/2] (element 2j in the low nibble of byte j),
+    fp32 scales [N, K/64] and u8 zeros [N, K/64].  Written from that description alone."""
+    G = K // 64
+    GQ, NB = (G + 3) // 4, (N + 15) // 16
+    q = np.zeros((NB * 16, GQ * 256), np.uint32)
+    q[:N, 0:K:2] = codes & 0xF
+    q[:N, 1:K:2] = codes >> 4
+    s = np.zeros((NB * 16, GQ * 4), np.float32)
+    s[:N, :G] = scales
+    z = np.zeros((NB * 16, GQ * 4), np.uint8)
+    z[:N, :G] = zeros
+    # k = 256 t + 64 j + 16 sl + 8 h + e, column n = 16 b + c
+    q7 = q.reshape(NB, 16, GQ, 4, 4, 2, 8)                        # b c t j sl h e
+    shift = np.array([4 * (e // 2 + 4 * (e % 2)) for e in range(8)], np.uint32)
+    words = (q7 << shift).sum(axis=-1, dtype=np.uint64).astype(np.uint32)   # b c t j sl h
+    words = words.reshape(NB, 16, GQ, 2, 2, 4, 2)                 # b c t jhi jlo sl h
+    # dword 256 jhi + 64 sl + 4 c + 2 jlo + h of the record
+    code_dw = words.transpose(0, 2, 3, 5, 1, 4, 6).reshape(NB, GQ, 512)
+    scale_dw = s.reshape(NB, 16, GQ, 4).transpose(0, 2, 1, 3).reshape(NB, GQ, 64).view(np.uint32)
+    zero_b = z.reshape(NB, 16, GQ, 4).transpose(0, 2, 1, 3).reshape(NB, GQ, 64)
+    rec = np.zeros((NB, GQ, 2368), np.uint8)
+    rec[:, :, :2048] = code_dw.astype('<u4').view(np.uint8).reshape(NB, GQ, 2048)
+    rec[:, :, 2048:2304] = scale_dw.astype('<u4').view(np.uint8).reshape(NB, GQ, 256)
+    rec[:, :, 2304:] = zero_b
+    return rec.reshape(-1)

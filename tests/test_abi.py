@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     decl = declared_functions()
-    assert len(decl) == 13, decl
+    assert len(decl) == 15, decl
     assert sorted(_binding.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -121,18 +121,26 @@ def test_pack_and_debug_reject(lib):
     assert lib.svdq_pack_weights(P(A), 8, 128, P(U), P(A), None) == MISALIGNED
     assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 128, 8, 0, 16, 16, P(A), None) == INVALID
     assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 100, 0, 0, 16, 16, P(A), None) == SHAPE
-    assert lib.svdq_awq_pack_weights(P(A), -1, 128, P(A), P(A), P(A), None) == INVALID
-    assert lib.svdq_awq_pack_weights(P(A), 8, 96, P(A), P(A), P(A), None) == SHAPE
-    assert lib.svdq_awq_pack_weights(P(A), 8, 128, P(A), P(0), P(A), None) == INVALID
-    assert lib.svdq_awq_pack_weights(P(A), 8, 128, P(A), P(A), P(U), None) == MISALIGNED
+    ap = lib.svdq_awq_pack_weights
+    assert ap(P(A), -1, 128, P(A), None) == INVALID
+    assert ap(P(A), 8, 96, P(A), None) == SHAPE
+    assert ap(P(A), 12, 128, P(A), None) == SHAPE
+    assert ap(P(A), 8, 128, P(0), None) == INVALID
+    assert ap(P(U), 8, 128, P(A), None) == MISALIGNED
+    ar = lib.svdq_awq_repack
+    assert ar(P(A), P(A), P(A), -1, 128, P(A), None) == INVALID
+    assert ar(P(A), P(A), P(A), 8, 100, P(A), None) == SHAPE
+    assert ar(P(0), P(A), P(A), 8, 128, P(A), None) == INVALID
+    assert ar(P(A), P(A), P(0), 8, 128, P(A), None) == INVALID
+    assert ar(P(A), P(U), P(A), 8, 128, P(A), None) == MISALIGNED
     aw = lib.svdq_awq_w4a16_linear
-    assert aw(P(A), P(A), P(A), P(A), P(A), -1, 64, 128, P(A), None) == INVALID
-    assert aw(P(A), P(A), P(A), P(A), P(A), 2, 60, 128, P(A), None) == SHAPE
-    assert aw(P(A), P(A), P(A), P(A), P(A), 2, 64, 100, P(A), None) == SHAPE
-    assert aw(P(0), P(A), P(A), P(A), P(A), 2, 64, 128, P(A), None) == INVALID
-    assert aw(P(A), P(A), P(A), P(0), P(A), 2, 64, 128, P(A), None) == INVALID
-    assert aw(P(A), P(A), P(A), P(A), P(U), 2, 64, 128, P(A), None) == MISALIGNED
-    assert aw(P(A), P(A), P(A), P(A), P(A), 2, 64, 128, P(U), None) == MISALIGNED
+    assert aw(P(A), P(A), P(A), -1, 64, 128, P(A), None) == INVALID
+    assert aw(P(A), P(A), P(A), 2, 60, 128, P(A), None) == SHAPE
+    assert aw(P(A), P(A), P(A), 2, 64, 100, P(A), None) == SHAPE
+    assert aw(P(0), P(A), P(A), 2, 64, 128, P(A), None) == INVALID
+    assert aw(P(A), P(0), P(A), 2, 64, 128, P(A), None) == INVALID
+    assert aw(P(A), P(A), P(U), 2, 64, 128, P(A), None) == MISALIGNED
+    assert aw(P(A), P(A), P(A), 2, 64, 128, P(U), None) == MISALIGNED
     assert lib.svdq_debug_set_tile_policy(3) == INVALID
     assert lib.svdq_debug_set_tile_policy(-1) == INVALID
 
@@ -150,8 +158,19 @@ def test_empty_inputs_are_noops(lib):
     assert _lin(lib, X=0, lam=0, L1=0, qw=0, sw=0, L2=0, bias=0, Y=0, ws=0, M=0) == OK
     assert lib.svdq_pack_weights(P(0), 0, 128, P(0), P(0), None) == OK
     assert lib.svdq_debug_group_sums(P(0), P(0), 16, 16, 128, 0, 0, 0, 5, P(0), None) == OK
-    assert lib.svdq_awq_pack_weights(P(0), 0, 128, P(0), P(0), P(0), None) == OK
-    assert lib.svdq_awq_w4a16_linear(P(0), P(0), P(0), P(0), P(0), 0, 64, 128, P(0), None) == OK
+    assert lib.svdq_awq_pack_weights(P(0), 0, 128, P(0), None) == OK
+    assert lib.svdq_awq_repack(P(0), P(0), P(0), 0, 128, P(0), None) == OK
+    assert lib.svdq_awq_w4a16_linear(P(0), P(0), P(0), 0, 64, 128, P(0), None) == OK
+
+
+def test_awq_packed_bytes(lib):
+    # (N, K) -> ceil(N/16) * ceil(K/256) records of 2368 bytes; 0 for bad shapes
+    assert lib.svdq_awq_packed_bytes(18432, 3072) == 1152 * 12 * 2368
+    assert lib.svdq_awq_packed_bytes(8, 64) == 2368
+    assert lib.svdq_awq_packed_bytes(264, 320) == 17 * 2 * 2368
+    assert lib.svdq_awq_packed_bytes(0, 128) == 0
+    assert lib.svdq_awq_packed_bytes(8, 100) == 0
+    assert lib.svdq_awq_packed_bytes(-8, 128) == 0
 
 
 def test_refuses_without_a_gfx950_device(lib):
