@@ -63,18 +63,32 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_lr_gemm_qkv_traffic.txt")
 GEMM_SOURCE = os.path.join(ROOT, "bit_diffusion_transformer_amd", "csrc", "w4a4_gemm.hip")
 
 
+# workload -> (committed counter summary, kernel source it was taken with)
+TRAFFIC = {
+    "qkv": (None, None),
+    "awq_mod": (os.path.join(ROOT, "profiles", "awq_w4a16_linear_mod_traffic.txt"),
+                os.path.join(ROOT, "bit_diffusion_transformer_amd", "csrc", "awq_w4a16.hip")),
+}
+
+
 def measured_traffic(workload):
-    """HBM bytes per GEMM call from the committed counter summary, if it was
-    taken on this workload with the current kernel source; else None."""
+    """HBM bytes per call of the dominant kernel from the committed counter
+    summary, if it was taken on this workload with the current kernel source;
+    else None."""
     import hashlib
-    if workload != "qkv" or not os.path.exists(TRAFFIC_FILE):
+    if workload not in TRAFFIC:
+        return None
+    path, source = TRAFFIC[workload]
+    if path is None:
+        path, source = TRAFFIC_FILE, GEMM_SOURCE
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    src = hashlib.sha256(open(source, "rb").read()).hexdigest()
     if kv.get("kernel_source_sha256") != src or "traffic_bytes_per_call" not in kv:
         return None
     return int(float(kv["traffic_bytes_per_call"]))
@@ -153,7 +167,8 @@ def bench_awq(args):
                    "global_batch": M, "input_sets_rotated": nsets},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / t_k / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(nbytes / t_k / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(nbytes / t_k / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(args.workload),
                      "kernel": "awq_linear_kernel", "avg_launch_us": round(t_k * 1e6, 2),
                      "algorithmic_bytes": nbytes},
     }
@@ -162,12 +177,15 @@ def bench_awq(args):
         cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
         oracle.set_threads(cores)
         q, s_, z = oracle.awq_quantize(L.W)
-        t0 = time.perf_counter()
-        oracle.awq_linear(L.X, q, s_, z, L.bias)
-        tc = time.perf_counter() - t0
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < 2.0:    # whole layer, repeated ~2 s
+            oracle.awq_linear(L.X, q, s_, z, L.bias)
+            reps += 1
+        tc = (time.perf_counter() - t0) / reps
         out["cpu_baseline"] = {"value": round(nbytes / tc / 1e9, 3), "unit": "GB/s",
                                "cores": cores, "kind": "oracle",
-                               "sample": "the whole layer (all %d rows), %.2f s" % (M, tc)}
+                               "sample": "the whole layer (all %d rows) x %d, %.3f s each"
+                                         % (M, reps, tc)}
     print(json.dumps(out), flush=True)
 
 
