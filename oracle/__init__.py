@@ -23,6 +23,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "svdq_oracle.c")
 _SRC_AWQ = os.path.join(_HERE, "awq_oracle.c")
+_SRC_QKV = os.path.join(_HERE, "qkv_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -35,7 +36,7 @@ def build(force: bool = True) -> str:
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, _SRC_AWQ, "-o", tmp, "-lm"]
+           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, _SRC_AWQ, _SRC_QKV, "-o", tmp, "-lm"]
     subprocess.check_call(cmd)
     os.replace(tmp, _LIB)
     return _LIB
@@ -65,9 +66,12 @@ def _load():
     lib.oracle_awq_quantize.argtypes = [P, I64, I64, P, P, P]
     lib.oracle_awq_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.oracle_awq_linear_rows.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, P, P]
+    lib.oracle_qkv_epilogue.argtypes = [P, P, I64, I64, I64, I64, P, P, ctypes.c_double, P, P,
+                                        P, P, P, P, P, P, P]
     for f in ("oracle_smooth", "oracle_quantize_groups", "oracle_unpack",
               "oracle_down_proj", "oracle_group_sums", "oracle_gemm_rows",
-              "oracle_awq_quantize", "oracle_awq_dequant", "oracle_awq_linear_rows"):
+              "oracle_awq_quantize", "oracle_awq_dequant", "oracle_awq_linear_rows",
+              "oracle_qkv_epilogue"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -267,4 +271,33 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     e = np.floor(np.log2(a[nz]))
     e = np.maximum(e, -126.0)
     out[nz] = np.exp2(e - 7.0)
+    return out
+
+
+# ---------------------------------------------------------------- fused QKV epilogue
+
+def qkv_epilogue(acc: np.ndarray, H: int, D: int, S: int, gamma_q: np.ndarray,
+                 gamma_k: np.ndarray, eps: float, cos_t: np.ndarray, sin_t: np.ndarray,
+                 rows: Optional[Sequence[int]] = None):
+    """Per-head RMS norm + rotary embedding of Q and K, V re-laid out (readings in
+    qkv_oracle.c).  acc: fp64 [R, 3 H D], the exact projection output of tokens
+    ``rows`` (token i if None).  Returns dict with q, k (fp64 [R, H, D]), qb, kb, vb
+    (bf16 bits [R, H, D]) and rho_q, rho_k (fp64 [R, H])."""
+    acc = np.ascontiguousarray(acc, dtype=np.float64)
+    R = acc.shape[0]
+    assert acc.shape[1] == 3 * H * D and D % 2 == 0
+    gq = np.ascontiguousarray(gamma_q, dtype=np.uint16)
+    gk = np.ascontiguousarray(gamma_k, dtype=np.uint16)
+    ct = np.ascontiguousarray(cos_t, dtype=np.float32)
+    st = np.ascontiguousarray(sin_t, dtype=np.float32)
+    assert ct.shape == (S, D // 2) and st.shape == (S, D // 2)
+    rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = dict(q=np.empty((R, H, D)), k=np.empty((R, H, D)),
+               qb=np.empty((R, H, D), np.uint16), kb=np.empty((R, H, D), np.uint16),
+               vb=np.empty((R, H, D), np.uint16), rho_q=np.empty((R, H)), rho_k=np.empty((R, H)))
+    if R > 0:
+        _load().oracle_qkv_epilogue(_ptr(acc), _ptr(rows_arr), R, H, D, S, _ptr(gq), _ptr(gk),
+                                    float(eps), _ptr(ct), _ptr(st), _ptr(out["q"]),
+                                    _ptr(out["k"]), _ptr(out["qb"]), _ptr(out["kb"]),
+                                    _ptr(out["vb"]), _ptr(out["rho_q"]), _ptr(out["rho_k"]))
     return out
