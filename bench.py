@@ -36,7 +36,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="qkv",
-                    choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single"])
+                    choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single",
+                             "qkv_fused"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-overhead", action="store_true",
@@ -189,17 +190,131 @@ def bench_awq(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_qkv_fused(args):
+    """The qkv projection with the fused QKV epilogue (per-head RMS norm + rotary turn of Q
+    and K, [B, H, S, D] outputs): one step = one svdq_linear_qkv call.  Same metric as the
+    default line (2MNK/t); the plain svdq_linear on the same inputs is timed beside it."""
+    import torch
+
+    import bit_diffusion_transformer_amd as bdt
+    from synth import CONFIGS, make_layer, make_qkv_epilogue
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    spec = CONFIGS["qkv"]
+    L = make_layer(spec, seed=0, M=args.M)
+    M, K, N, r = L.spec.M, L.spec.K, L.spec.N, L.spec.r
+    H, D = 24, 128
+    assert N == 3 * H * D
+    S = M                                   # one sequence of M tokens
+    E = make_qkv_epilogue(H, D, S, cfg_id=40)
+
+    def d(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    qw, sw = bdt.pack_weights(d(L.R))
+    base = dict(X=d(L.X), lam=d(L.lam), L1=d(L.L1), L2=d(L.L2), bias=d(L.bias), qw=qw, sw=sw,
+                gq=d(E.gamma_q), gk=d(E.gamma_k), cos=d(E.cos_t), sin=d(E.sin_t))
+    ws_bytes = bdt.svdq_linear_workspace_bytes(M, K, r)
+    set_bytes = (2 * M * K + qw.numel() + sw.numel() * 4 + 2 * M * N + ws_bytes
+                 + 4 * K + 2 * K * r + 2 * r * N + 2 * N + 8 * S * (D // 2))
+    nsets = max(2, int(np.ceil(2 * CACHE_BYTES / set_bytes)))
+    bits = bdt._bits
+    sets = []
+    for _ in range(nsets):
+        st = {k: v.clone() for k, v in base.items()}
+        st["Q"], st["K"], st["V"] = (torch.empty((M // S, H, S, D), dtype=torch.bfloat16,
+                                                 device=dev) for _ in range(3))
+        st["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        st["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        st["epi"] = bdt.qkv_epilogue(H, D, S, bits(st["gq"]), bits(st["gk"]), E.eps, st["cos"],
+                                     st["sin"], bits(st["Q"]), bits(st["K"]), bits(st["V"]))
+        sets.append(st)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        st = sets[i % nsets]
+        bdt.svdq_linear_qkv(bits(st["X"]), st["lam"], bits(st["L1"]), st["qw"], st["sw"],
+                            bits(st["L2"]), bits(st["bias"]), M, K, r, st["epi"], st["ws"],
+                            ws_bytes, stream)
+
+    def plain(i):
+        st = sets[i % nsets]
+        bdt.svdq_linear(bits(st["X"]), st["lam"], bits(st["L1"]), st["qw"], st["sw"],
+                        bits(st["L2"]), bits(st["bias"]), 0, M, N, K, r, bits(st["Y"]),
+                        st["ws"], ws_bytes, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    ops = 2.0 * M * N * K
+
+    carved = [bdt.quantize_act_down(st["X"], st["lam"], st["L1"]) for st in sets]
+    torch.cuda.synchronize()
+
+    def gemm_qkv(i):
+        st, (qa, sa, xl1) = sets[i % nsets], carved[i % nsets]
+        bdt.svdq_w4a4_lr_gemm_qkv(qa, sa, st["qw"], st["sw"], xl1, bits(st["L2"]),
+                                  bits(st["bias"]), M, K, r, st["epi"], stream)
+
+    def time_loop(fn, n):
+        for i in range(20):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    n_k = max(args.steps, 20)
+    t_gq = time_loop(gemm_qkv, n_k)
+    t_lin = time_loop(step, n_k)
+    t_plain = time_loop(plain, n_k)
+    gemm_tops = ops / t_gq / 1e12
+    out = {
+        "metric": METRIC, "value": round(ops / t_step / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
+        "config": {"workload": "qkv_fused: M=%d K=%d N=%d r=%d group=64 heads=%d head_dim=%d "
+                               "seq=%d, Q/K RMS norm + rotary, [B,H,S,D] bf16 out"
+                               % (M, K, N, r, H, D, S),
+                   "global_batch": M, "input_sets_rotated": nsets},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": None,
+                     "kernel": "w4a4_lr_gemm_qkv_kernel (one launch per svdq_w4a4_lr_gemm_qkv call)",
+                     "avg_launch_us": round(t_gq * 1e6, 2), "algorithmic_ops": ops},
+        "fused_vs_plain": {"linear_qkv_us": round(t_lin * 1e6, 2),
+                           "linear_plain_us": round(t_plain * 1e6, 2),
+                           "epilogue_overhead": round(t_lin / t_plain - 1.0, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.workload.startswith("awq"):
+    if args.workload.startswith("awq") or args.workload == "qkv_fused":
         if args.gpus != 1:
             print("bench.py runs on one GPU only (--gpus %d requested)" % args.gpus,
                   file=sys.stderr)
             sys.exit(2)
-        bench_awq(args)
+        (bench_awq if args.workload.startswith("awq") else bench_qkv_fused)(args)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the layer has no multi-GPU path in this build "

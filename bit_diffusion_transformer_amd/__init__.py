@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError,  # noqa: F401
-                       TILES_AUTO, TILES_FULL, TILES_QUARTER,
+                       QkvEpilogue, TILES_AUTO, TILES_FULL, TILES_QUARTER, qkv_epilogue,
                        load_library, svdq_abi_version, svdq_awq_pack_weights,
                        svdq_awq_packed_bytes, svdq_awq_repack,
                        svdq_awq_w4a16_linear, svdq_debug_group_sums,
@@ -24,7 +24,7 @@ from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError, 
                        svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
                        svdq_pack_weights, svdq_quantize_act_down,
                        svdq_quantize_act_down_workspace_bytes, svdq_status_string,
-                       svdq_w4a4_lr_gemm)
+                       svdq_w4a4_lr_gemm, svdq_w4a4_lr_gemm_qkv, svdq_linear_qkv)
 
 
 def _bits(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
@@ -116,6 +116,40 @@ def linear(X, lam, L1, qw, sw, L2, bias, act: int = ACT_NONE,
                 _bits(L2) if r > 0 else None, _bits(bias), act, M, N, K, r, _bits(Y),
                 workspace, need)
     return Y
+
+
+def _qkv_out(M, heads, head_dim, seq, device):
+    shape = (M // seq, heads, seq, head_dim)
+    return tuple(torch.empty(shape, dtype=torch.bfloat16, device=device) for _ in range(3))
+
+
+def w4a4_lr_gemm_qkv(qa, sa, qw, sw, xl1, L2, bias, heads: int, head_dim: int, seq: int,
+                     gamma_q, gamma_k, eps: float, cos_t, sin_t):
+    """The GEMM with the fused QKV epilogue -> (Q, K, V) bf16 [M/seq, heads, seq, head_dim]."""
+    M, K = qa.shape[0], qa.shape[1] * 2
+    r = _rank(L2, 0)
+    Q, Kt, V = _qkv_out(M, heads, head_dim, seq, qa.device)
+    epi = qkv_epilogue(heads, head_dim, seq, _bits(gamma_q), _bits(gamma_k), eps, cos_t, sin_t,
+                       _bits(Q), _bits(Kt), _bits(V))
+    svdq_w4a4_lr_gemm_qkv(qa, sa, qw, sw, xl1 if r > 0 else None, _bits(L2) if r > 0 else None,
+                          _bits(bias), M, K, r, epi)
+    return Q, Kt, V
+
+
+def linear_qkv(X, lam, L1, qw, sw, L2, bias, heads: int, head_dim: int, seq: int, gamma_q,
+               gamma_k, eps: float, cos_t, sin_t, workspace: Optional[torch.Tensor] = None):
+    """The whole fused QKV layer (svdq_linear_qkv) -> (Q, K, V) bf16 [M/seq, heads, seq, D]."""
+    M, K = X.shape
+    r = _rank(L1, 1)
+    need = svdq_linear_workspace_bytes(M, K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    Q, Kt, V = _qkv_out(M, heads, head_dim, seq, X.device)
+    epi = qkv_epilogue(heads, head_dim, seq, _bits(gamma_q), _bits(gamma_k), eps, cos_t, sin_t,
+                       _bits(Q), _bits(Kt), _bits(V))
+    svdq_linear_qkv(_bits(X), lam, _bits(L1) if r > 0 else None, qw, sw,
+                    _bits(L2) if r > 0 else None, _bits(bias), M, K, r, epi, workspace, need)
+    return Q, Kt, V
 
 
 def group_sums(qa, qw, m0: int, n0: int, tm: int, tn: int) -> torch.Tensor:

@@ -30,8 +30,30 @@ EXPORTS = (
     "svdq_quantize_act_down_workspace_bytes", "svdq_quantize_act_down", "svdq_w4a4_lr_gemm",
     "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
     "svdq_debug_set_tile_policy", "svdq_awq_packed_bytes", "svdq_awq_pack_weights",
-    "svdq_awq_repack", "svdq_awq_w4a16_linear",
+    "svdq_awq_repack", "svdq_awq_w4a16_linear", "svdq_w4a4_lr_gemm_qkv", "svdq_linear_qkv",
 )
+
+
+class QkvEpilogue(ctypes.Structure):
+    """struct svdq_qkv_epilogue of include/svdq.h (device pointers as integers)."""
+    _fields_ = [
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("seq", ctypes.c_int64),
+        ("gamma_q", ctypes.c_void_p), ("gamma_k", ctypes.c_void_p), ("eps", ctypes.c_float),
+        ("cos_t", ctypes.c_void_p), ("sin_t", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+    ]
+
+
+def qkv_epilogue(heads, head_dim, seq, gamma_q, gamma_k, eps, cos_t, sin_t, q, k, v):
+    """Fill a QkvEpilogue from tensors (kept alive by the caller)."""
+    def a(t):
+        if t is None:
+            return None
+        if not t.is_contiguous():
+            raise ValueError("tensors passed to libsvdq must be contiguous")
+        return t.data_ptr()
+    return QkvEpilogue(int(heads), int(head_dim), int(seq), a(gamma_q), a(gamma_k), float(eps),
+                       a(cos_t), a(sin_t), a(q), a(k), a(v))
 
 
 class SVDQError(RuntimeError):
@@ -71,6 +93,10 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_awq_pack_weights": ([P, I64, I64, P, P], I32),
         "svdq_awq_repack": ([P, P, P, I64, I64, P, P], I32),
         "svdq_awq_w4a16_linear": ([P, P, P, I64, I64, I64, P, P], I32),
+        "svdq_w4a4_lr_gemm_qkv": ([P, P, P, P, P, P, P, I64, I64, I32,
+                                   ctypes.POINTER(QkvEpilogue), P], I32),
+        "svdq_linear_qkv": ([P, P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(QkvEpilogue),
+                             P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -179,3 +205,16 @@ def svdq_awq_repack(codes, scales, zeros, N, K, packed, stream=None):
 def svdq_awq_w4a16_linear(X, packed, bias, M, N, K, Y, stream=None):
     _check(load_library().svdq_awq_w4a16_linear(_p(X), _p(packed), _p(bias), M, N, K, _p(Y),
                                                 _stream(stream)), "svdq_awq_w4a16_linear")
+
+
+def svdq_w4a4_lr_gemm_qkv(qa, sa, qw, sw, xl1, L2, bias, M, K, r, epi: QkvEpilogue, stream=None):
+    _check(load_library().svdq_w4a4_lr_gemm_qkv(_p(qa), _p(sa), _p(qw), _p(sw), _p(xl1), _p(L2),
+                                                _p(bias), M, K, r, ctypes.byref(epi),
+                                                _stream(stream)), "svdq_w4a4_lr_gemm_qkv")
+
+
+def svdq_linear_qkv(X, lam, L1, qw, sw, L2, bias, M, K, r, epi: QkvEpilogue, workspace,
+                    ws_bytes, stream=None):
+    _check(load_library().svdq_linear_qkv(_p(X), _p(lam), _p(L1), _p(qw), _p(sw), _p(L2),
+                                          _p(bias), M, K, r, ctypes.byref(epi), _p(workspace),
+                                          ws_bytes, _stream(stream)), "svdq_linear_qkv")

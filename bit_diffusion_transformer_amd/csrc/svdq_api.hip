@@ -146,6 +146,46 @@ int32_t validate_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw, con
     return SVDQ_OK;
 }
 
+int32_t validate_qkv(const svdq_qkv_epilogue *e, int64_t M) {
+    if (!e) return fail(SVDQ_ERR_INVALID_ARG, "epi must not be NULL");
+    if (e->heads < 1) return fail(SVDQ_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", e->heads);
+    if (e->head_dim != 64 && e->head_dim != 128)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "head_dim must be 64 or 128 (got %d)",
+                    e->head_dim);
+    if (((int64_t)e->heads * e->head_dim) % 128 != 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "heads * head_dim must be a multiple of 128");
+    if (e->seq < 1) return fail(SVDQ_ERR_INVALID_ARG, "seq must be >= 1");
+    if (M % e->seq != 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "M = %lld is not a multiple of seq = %lld",
+                    (long long)M, (long long)e->seq);
+    if (!(e->eps >= 0.0f) || e->eps > 3.0e38f)
+        return fail(SVDQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(e->gamma_q, "gamma_q"));
+    SVDQ_TRY(need_ptr(e->gamma_k, "gamma_k"));
+    SVDQ_TRY(need_ptr(e->cos_t, "cos_t"));
+    SVDQ_TRY(need_ptr(e->sin_t, "sin_t"));
+    SVDQ_TRY(need_ptr(e->q, "q"));
+    SVDQ_TRY(need_ptr(e->k, "k"));
+    return need_ptr(e->v, "v");
+}
+
+svdq::QkvArgs qkv_args(const svdq_qkv_epilogue *e) {
+    svdq::QkvArgs a;
+    a.H = e->heads;
+    a.D = e->head_dim;
+    a.S = e->seq;
+    a.gq = e->gamma_q;
+    a.gk = e->gamma_k;
+    a.eps = e->eps;
+    a.cos_t = e->cos_t;
+    a.sin_t = e->sin_t;
+    a.Q = e->q;
+    a.K = e->k;
+    a.V = e->v;
+    return a;
+}
+
 struct LinearWorkspace {
     uint8_t *qa;
     float *sa;
@@ -268,6 +308,23 @@ int32_t svdq_w4a4_lr_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
                       "w4a4_lr_gemm launch");
 }
 
+int32_t svdq_w4a4_lr_gemm_qkv(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                              const float *sw, const float *xl1, const uint16_t *L2,
+                              const uint16_t *bias, int64_t M, int64_t K, int32_t r,
+                              const svdq_qkv_epilogue *epi, void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(validate_qkv(epi, M));
+    const int64_t N = 3 * (int64_t)epi->heads * epi->head_dim;
+    // the plain GEMM's checks, with a stand-in for the [M, N] output
+    SVDQ_TRY(validate_gemm(qa, sa, qw, sw, xl1, L2, bias, SVDQ_ACT_NONE, M, N, K, r, epi->q));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_w4a4_gemm_qkv(qa, sa, qw, sw, xl1, L2, bias, M, K, r,
+                                                 qkv_args(epi), (hipStream_t)stream),
+                      "w4a4_lr_gemm_qkv launch");
+}
+
 size_t svdq_linear_workspace_bytes(int64_t M, int64_t K, int32_t r) {
     if (M < 0 || K < 0 || r < 0) return 0;
     return carve_linear(nullptr, M, K, r).bytes;
@@ -307,6 +364,40 @@ int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
     return hip_status(svdq::launch_w4a4_gemm(w.qa, w.sa, qw, sw, w.xl1, L2, bias, act, M, N, K,
                                              r, Y, s),
                       "w4a4_lr_gemm launch");
+}
+
+int32_t svdq_linear_qkv(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                        const uint8_t *qw, const float *sw, const uint16_t *L2,
+                        const uint16_t *bias, int64_t M, int64_t K, int32_t r,
+                        const svdq_qkv_epilogue *epi, void *workspace, size_t ws_bytes,
+                        void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(validate_qkv(epi, M));
+    SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_r(r));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(X, "X"));
+    SVDQ_TRY(need_ptr(lambda, "lambda"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
+    SVDQ_TRY(lr_ptrs(L1, "L1", L2, "L2", r));
+    if (bias && !aligned16(bias)) return fail(SVDQ_ERR_MISALIGNED, "bias is not 16-byte aligned");
+    const size_t need = carve_linear(nullptr, M, K, r).bytes;
+    if (ws_bytes < need)
+        return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed", ws_bytes,
+                    need);
+    SVDQ_TRY(need_ptr(workspace, "workspace"));
+    SVDQ_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    const LinearWorkspace w = carve_linear(workspace, M, K, r);
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.down, M, K, r);
+    SVDQ_TRY(hip_status(svdq::launch_quant_down(X, lambda, L1, M, K, r, dw, w.qa, w.sa, w.xl1,
+                                                s),
+                        "quantize_act_down launch"));
+    return hip_status(svdq::launch_w4a4_gemm_qkv(w.qa, w.sa, qw, sw, w.xl1, L2, bias, M, K, r,
+                                                 qkv_args(epi), s),
+                      "w4a4_lr_gemm_qkv launch");
 }
 
 int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,

@@ -54,6 +54,20 @@ hipError_t launch_awq_linear(const uint16_t *X, const uint8_t *rec, const uint16
                              int64_t M, int64_t N, int64_t K, int MT, uint16_t *Y,
                              hipStream_t stream);
 
+// Fused QKV epilogue: the GEMM's columns are [Q | K | V], each H heads of D.
+struct QkvArgs {
+    int H, D;                      // heads, head_dim (64 or 128; H D % 128 == 0)
+    int64_t S;                     // tokens per sequence; M = B S
+    const uint16_t *gq, *gk;       // bf16 [D] RMS-norm weights
+    float eps;
+    const float *cos_t, *sin_t;    // fp32 [S, D/2]
+    uint16_t *Q, *K, *V;           // bf16 [B, H, S, D]
+};
+hipError_t launch_w4a4_gemm_qkv(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                                const float *sw, const float *xl1, const uint16_t *L2,
+                                const uint16_t *bias, int64_t M, int64_t K, int r,
+                                const QkvArgs &qk, hipStream_t stream);
+
 // 0 auto, 1 full tiles only, 2 quarter tiles only (process-wide test hook)
 void set_tile_policy(int policy);
 

@@ -354,14 +354,158 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
 
 namespace {
 
-// One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0).
+// Fused QKV epilogue of a 128 x 128 tile (the "Bringing Nunchaku 4-bit
+// inference to Diffusers" blog, the fused_qkv_norm_rottary listing: Q, K and
+// V from one projection, norm_q / norm_k, then the rotary embedding, in one
+// operator).  The tile lies in one section of [Q | K | V] (H D % 128 == 0).
+// For Q and K: per token and head, rho = sqrt(mean(x^2) + eps) over the head's
+// D columns (D = 128: the whole tile width, the two column-half waves swap
+// their partial sums through LDS and both add them in the same order; D = 64:
+// the wave's own 64 columns), v = x gamma / rho, then each adjacent pair
+// (2p, 2p + 1) -- two consecutive values of the same lane -- turns by the
+// caller's (cos, sin) of position s = m mod S.  V is only re-laid out.  The
+// stores go to [B, H, S, D] as 8-byte writes of four consecutive d.
 template <int WB>
+__device__ __forceinline__ void
+qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk,
+             Smem<WB> &sm, int64_t M, int64_t m0, int64_t n0, int wn, int wm, int r32,
+             int ks2) {
+    constexpr int NB = WB * WB;
+    const int D = qk.D;
+    const int64_t HD = (int64_t)qk.H * D;
+    const int sec = (int)(n0 / HD);
+    const int64_t nsec = n0 - sec * HD;        // section column of the tile's left edge
+    const int64_t S = qk.S;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        const int bi = t / WB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 b2 = bb[bi][q];
+            acc[t][4 * q + 0] += bf16_lo(b2.x);
+            acc[t][4 * q + 1] += bf16_hi(b2.x);
+            acc[t][4 * q + 2] += bf16_lo(b2.y);
+            acc[t][4 * q + 3] += bf16_hi(b2.y);
+        }
+    }
+    // token of the lane in each column block bj: row offset in [B, H, S, D]
+    int64_t tok[WB];
+    int64_t spos[WB];
+    bool live[WB];
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) {
+        const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+        live[bj] = m < M;
+        const int64_t mc = m < M ? m : M - 1;
+        const int64_t b = mc / S;
+        spos[bj] = mc - b * S;
+        tok[bj] = (b * qk.H * S + spos[bj]) * D;
+    }
+    if (sec == 2) {
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t nl = nsec + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+                const int64_t h = nl / D, d = nl - h * D;
+#pragma unroll
+                for (int bj = 0; bj < WB; ++bj) {
+                    if (!live[bj]) continue;
+                    const int t = bi * WB + bj;
+                    u32x2 out;
+                    out.x = pack_bf16x2(acc[t][4 * q], acc[t][4 * q + 1]);
+                    out.y = pack_bf16x2(acc[t][4 * q + 2], acc[t][4 * q + 3]);
+                    *reinterpret_cast<u32x2 *>(qk.V + tok[bj] + h * S * D + d) = out;
+                }
+            }
+        }
+        return;
+    }
+    // sum of squares of each token over this wave's columns (and the partner
+    // lane l ^ 32, which holds the other half of every 8-column group)
+    float ss[WB];
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) {
+        float a = 0.0f;
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a = fmaf(acc[bi * WB + bj][i], acc[bi * WB + bj][i], a);
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
+                                                        false, false);
+        ss[bj] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    if (D == 128) {
+        __syncthreads();   // every wave is past its reads of the L2^T staging
+        float *xs = reinterpret_cast<float *>(&sm.u);   // [wn][wm][bj][32]
+        if (ks2 == 0) {
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) xs[((wn * 2 + wm) * WB + bj) * 32 + r32] = ss[bj];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int bj = 0; bj < WB; ++bj)
+            ss[bj] = xs[((0 * 2 + wm) * WB + bj) * 32 + r32] + xs[((1 * 2 + wm) * WB + bj) * 32 + r32];
+    }
+    float inv[WB];
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) inv[bj] = 1.0f / sqrtf(ss[bj] / (float)D + qk.eps);
+    const uint16_t *gam = sec == 0 ? qk.gq : qk.gk;
+    uint16_t *dst = sec == 0 ? qk.Q : qk.K;
+    const int half = D / 2;
+#pragma unroll
+    for (int bi = 0; bi < WB; ++bi) {
+        u32x2 g4[4];
+        f32x2 cs[4][WB], sn[4][WB];
+        int64_t hoff[4], dd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t nl = nsec + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+            const int64_t h = nl / D;
+            dd[q] = nl - h * D;
+            hoff[q] = h * S * D;
+            g4[q] = *reinterpret_cast<const u32x2 *>(gam + dd[q]);
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) {
+                const int64_t at = spos[bj] * half + dd[q] / 2;
+                cs[q][bj] = *reinterpret_cast<const f32x2 *>(qk.cos_t + at);
+                sn[q][bj] = *reinterpret_cast<const f32x2 *>(qk.sin_t + at);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float gv[4] = {bf16_lo(g4[q].x), bf16_hi(g4[q].x), bf16_lo(g4[q].y),
+                                 bf16_hi(g4[q].y)};
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) {
+                if (!live[bj]) continue;
+                const int t = bi * WB + bj;
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = acc[t][4 * q + j] * inv[bj] * gv[j];
+                const float o0 = v[0] * cs[q][bj].x - v[1] * sn[q][bj].x;
+                const float o1 = v[0] * sn[q][bj].x + v[1] * cs[q][bj].x;
+                const float o2 = v[2] * cs[q][bj].y - v[3] * sn[q][bj].y;
+                const float o3 = v[2] * sn[q][bj].y + v[3] * cs[q][bj].y;
+                u32x2 out;
+                out.x = pack_bf16x2(o0, o1);
+                out.y = pack_bf16x2(o2, o3);
+                *reinterpret_cast<u32x2 *>(dst + tok[bj] + hoff[q] + dd[q]) = out;
+            }
+        }
+    }
+}
+
+// One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0);
+// QKV: the fused QKV epilogue instead of the plain store (WB = 2 only).
+template <int WB, bool QKV = false>
 __device__ __forceinline__ void
 tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
           const uint8_t *__restrict__ qw, const float *__restrict__ sw,
           const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
           const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N, int64_t K, int r,
-          uint16_t *__restrict__ Y, Smem<WB> &sm, int64_t m0, int64_t n0) {
+          uint16_t *__restrict__ Y, Smem<WB> &sm, int64_t m0, int64_t n0,
+          const QkvArgs *qk = nullptr) {
     using C = Cfg<WB>;
     constexpr int BT = C::BT, NB = C::NB;
     const int tid = threadIdx.x;
@@ -528,6 +672,10 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
         }
     }
 
+    if constexpr (QKV) {
+        qkv_epilogue<WB>(acc, bb, *qk, sm, M, m0, n0, wn, wm, r32, ks2);
+        return;
+    }
     // Block (bi, bj); element i of the lane is n = base + 8 (i / 4) +
     // 4 (lane / 32) + i % 4, m = base + lane % 32.
 #pragma unroll
@@ -592,6 +740,23 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
         tile_body<2>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm.full, tm * TILE,
                      tn * TILE);
     }
+}
+
+// The GEMM with the fused QKV epilogue: full 128 x 128 tiles only (a head
+// of 128 columns is one tile), each XCD taking a contiguous range.
+__global__ void __launch_bounds__(NTHR)
+w4a4_lr_gemm_qkv_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
+                        const uint8_t *__restrict__ qw, const float *__restrict__ sw,
+                        const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
+                        const uint16_t *__restrict__ bias, int64_t M, int64_t N, int64_t K,
+                        int r, QkvArgs qk, int64_t nfull) {
+    __shared__ Smem<2> sm;
+    const int64_t nbm = (M + TILE - 1) / TILE, nbn = (N + TILE - 1) / TILE;
+    int64_t b = blockIdx.x, tm, tn;
+    if ((nfull & 7) == 0) b = (b & 7) * (nfull >> 3) + (b >> 3);
+    raster(b, nbm, nbn, tm, tn);
+    tile_body<2, true>(qa, sa, qw, sw, xl1, L2, bias, 0, M, N, K, r, nullptr, sm, tm * TILE,
+                       tn * TILE, &qk);
 }
 
 // Test hook: per-group integer sums with the GEMM's k split, operand
@@ -665,6 +830,17 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
     const int64_t nq = 4 * rest;
     w4a4_lr_gemm_kernel<<<(unsigned)(nq + full), NTHR, 0, stream>>>(
         qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, nq, full, full);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a4_gemm_qkv(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                                const float *sw, const float *xl1, const uint16_t *L2,
+                                const uint16_t *bias, int64_t M, int64_t K, int r,
+                                const QkvArgs &qk, hipStream_t stream) {
+    const int64_t N = 3 * (int64_t)qk.H * qk.D;
+    const int64_t tiles = ((M + TILE - 1) / TILE) * (N / TILE);
+    w4a4_lr_gemm_qkv_kernel<<<(unsigned)tiles, NTHR, 0, stream>>>(qa, sa, qw, sw, xl1, L2, bias,
+                                                                  M, N, K, r, qk, tiles);
     return hipGetLastError();
 }
 

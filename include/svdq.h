@@ -161,6 +161,60 @@ int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
                     const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
                     int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------
+ * Fused QKV epilogue.  The blog "Bringing Nunchaku 4-bit inference to
+ * Diffusers" (its section on the structural rewrites, the to_q / to_k /
+ * to_v and fused_qkv_norm_rottary listings) fuses the Q, K and V
+ * projections into one SVDQuant layer whose operator also applies norm_q /
+ * norm_k and the rotary embedding.  The pages fix neither the norm nor the
+ * rotary convention; here:
+ *   - the projection's N = 3 H D columns are [Q | K | V], head h of a
+ *     section being its columns h D .. h D + D - 1;
+ *   - Q and K: per token m and head, v_d = x_d gamma_d / sqrt(mean(x^2) + eps)
+ *     (RMS norm over the head, bias included in x), then every adjacent pair
+ *     (2p, 2p + 1) turns: (a, b) -> (a cos - b sin, a sin + b cos) with
+ *     cos_t / sin_t [s][p] of the token's position s = m mod S;
+ *   - outputs are bf16 in the attention layout [B, H, S, D], M = B S.
+ * The norm and the turn act on the fp32 tile before its one bf16 rounding.
+ * ------------------------------------------------------------------ */
+typedef struct svdq_qkv_epilogue {
+    int32_t heads;            /* H >= 1 */
+    int32_t head_dim;         /* D: 64 or 128, with H D % 128 == 0 */
+    int64_t seq;              /* S >= 1 tokens per sequence, M % S == 0 */
+    const uint16_t *gamma_q;  /* device bf16 [D] */
+    const uint16_t *gamma_k;  /* device bf16 [D] */
+    float eps;                /* >= 0, finite */
+    const float *cos_t;       /* device fp32 [S, D/2] */
+    const float *sin_t;       /* device fp32 [S, D/2] */
+    uint16_t *q;              /* device bf16 [M/S, H, S, D] (out) */
+    uint16_t *k;              /* device bf16 [M/S, H, S, D] (out) */
+    uint16_t *v;              /* device bf16 [M/S, H, S, D] (out) */
+} svdq_qkv_epilogue;
+
+/*
+ * The W4A4 GEMM of svdq_w4a4_lr_gemm (N = 3 H D, no activation) with the
+ * fused QKV epilogue instead of the [M, N] store.  epi is a host pointer,
+ * read during the call only; its device pointers must be 16-byte aligned.
+ * Errors as svdq_w4a4_lr_gemm, plus SVDQ_ERR_INVALID_ARG / _UNSUPPORTED_SHAPE
+ * for a bad epilogue.  Q and K within 1 bf16 ulp plus the propagated GEMM
+ * error (the GEMM tolerance divided by the head's rms); V as Y.
+ */
+int32_t svdq_w4a4_lr_gemm_qkv(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                              const float *sw, const float *xl1, const uint16_t *L2,
+                              const uint16_t *bias, int64_t M, int64_t K, int32_t r,
+                              const svdq_qkv_epilogue *epi, void *stream);
+
+/*
+ * The whole fused QKV layer: svdq_quantize_act_down then
+ * svdq_w4a4_lr_gemm_qkv on one stream, intermediates in the caller's
+ * workspace of svdq_linear_workspace_bytes(M, K, r) bytes.
+ */
+int32_t svdq_linear_qkv(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                        const uint8_t *qw, const float *sw, const uint16_t *L2,
+                        const uint16_t *bias, int64_t M, int64_t K, int32_t r,
+                        const svdq_qkv_epilogue *epi, void *workspace, size_t ws_bytes,
+                        void *stream);
+
 /*
  * Test hook: the exact per-group integer sums of a block, computed with the
  * same operand unpacking and int8 matrix instructions as the GEMM.

@@ -49,7 +49,7 @@ import numpy as np
 __all__ = [
     "LayerSpec", "CONFIGS", "make_layer", "make_config_layers",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "DIT_CHAIN",
-    "AwqSpec", "AWQ_CONFIGS", "make_awq_layer",
+    "AwqSpec", "AWQ_CONFIGS", "make_awq_layer", "QkvEpi", "make_qkv_epilogue",
 ]
 
 
@@ -268,3 +268,32 @@ def make_awq_layer(spec: AwqSpec, seed: int = 0, M: Optional[int] = None) -> Awq
     bias = _to_bf16(0.02 * rng.standard_normal(spec.N)) if spec.bias else None
     return AwqLayer(AwqSpec(spec.name, M, spec.K, spec.N, spec.bias, spec.cfg_id),
                     np.ascontiguousarray(X), np.ascontiguousarray(W), bias)
+
+
+# ---------------------------------------------------------------- fused QKV epilogue inputs
+
+@dataclass
+class QkvEpi:
+    heads: int
+    head_dim: int
+    seq: int
+    gamma_q: np.ndarray     # uint16 [D] bf16 bits
+    gamma_k: np.ndarray     # uint16 [D] bf16 bits
+    eps: float
+    cos_t: np.ndarray       # float32 [S, D/2]
+    sin_t: np.ndarray       # float32 [S, D/2]
+
+
+def make_qkv_epilogue(heads: int, head_dim: int, seq: int, seed: int = 0, cfg_id: int = 40,
+                      theta: float = 10000.0, eps: float = 1e-6) -> QkvEpi:
+    """Seeded inputs of the fused QKV epilogue: norm weights bf16(U(0.5, 1.5)) and the
+    rotary tables of positions s = 0 .. S-1 with frequencies theta^(-2p/D) (the standard
+    one-axis table, standing in for a model's multi-axis one: the tables are caller
+    inputs), angles in fp64, cos / sin rounded to fp32."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, cfg_id, 7])))
+    gq = _to_bf16(rng.uniform(0.5, 1.5, head_dim))
+    gk = _to_bf16(rng.uniform(0.5, 1.5, head_dim))
+    freq = theta ** (-2.0 * np.arange(head_dim // 2) / head_dim)
+    ang = np.arange(seq, dtype=np.float64)[:, None] * freq[None, :]
+    return QkvEpi(heads, head_dim, seq, gq, gk, eps, np.cos(ang).astype(np.float32),
+                  np.sin(ang).astype(np.float32))

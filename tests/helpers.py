@@ -88,3 +88,17 @@ def awq_records(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, N: int
     rec[:, :, 2048:2304] = scale_dw.astype('<u4').view(np.uint8).reshape(NB, GQ, 256)
     rec[:, :, 2304:] = zero_b
     return rec.reshape(-1)
+
+
+def qkv_tolerance(ob: dict, x: np.ndarray, gamma_bits: np.ndarray, eps_y: float) -> np.ndarray:
+    """Per-element bound for Q or K of the fused QKV epilogue, from the oracle's values.
+
+    ob: oracle output for one section (fp64 values "o" [R, H, D] and "rho" [R, H]);
+    x: the section's exact pre-norm values [R, H, D]; eps_y: the bound on the GPU's
+    fp32 pre-norm error (the GEMM tolerance, 1e-3 rms of the projection).  Perturbing x
+    by |e| <= eps_y moves x / rho by at most eps_y / rho (1 + |x_d| / rho) per element;
+    gamma scales it and the pair turn mixes two elements (sqrt 2); plus 1 bf16 ulp."""
+    rho = ob["rho"][..., None]
+    xmax = np.abs(x).max(axis=-1, keepdims=True)
+    g = np.abs(bf16_f64(gamma_bits)).max()
+    return oracle.bf16_ulp(ob["o"]) + 2.0 * np.sqrt(2.0) * g * eps_y / rho * (1.0 + xmax / rho)

@@ -8,6 +8,7 @@ any launch.
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -34,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     decl = declared_functions()
-    assert len(decl) == 15, decl
+    assert len(decl) == 17, decl
     assert sorted(_binding.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -179,3 +180,69 @@ def test_refuses_without_a_gfx950_device(lib):
         pytest.skip("a GPU is present; the device check is exercised by the GPU tests")
     assert _gemm(lib) == NODEV
     assert "device" in lib.svdq_last_error().decode()
+
+
+def _epi(**kw):
+    e = dict(heads=2, head_dim=128, seq=4, gamma_q=A, gamma_k=A, eps=1e-6, cos_t=A, sin_t=A,
+             q=A, k=A, v=A)
+    e.update(kw)
+    return _binding.QkvEpilogue(**e)
+
+
+def _gq(lib, epi, M=8, K=128, r=16, **kw):
+    a = dict(qa=A, sa=A, qw=A, sw=A, xl1=A, L2=A, bias=A)
+    a.update(kw)
+    e = None if epi is None else ctypes.byref(epi)
+    return lib.svdq_w4a4_lr_gemm_qkv(P(a["qa"]), P(a["sa"]), P(a["qw"]), P(a["sw"]),
+                                     P(a["xl1"]), P(a["L2"]), P(a["bias"]), M, K, r, e, None)
+
+
+def _lq(lib, epi, M=8, K=128, r=16, ws_bytes=1 << 30, **kw):
+    a = dict(X=A, lam=A, L1=A, qw=A, sw=A, L2=A, bias=A, ws=A)
+    a.update(kw)
+    return lib.svdq_linear_qkv(P(a["X"]), P(a["lam"]), P(a["L1"]), P(a["qw"]), P(a["sw"]),
+                               P(a["L2"]), P(a["bias"]), M, K, r, ctypes.byref(epi), P(a["ws"]),
+                               ws_bytes, None)
+
+
+@pytest.mark.parametrize("epi_kw,code", [
+    (dict(head_dim=96), SHAPE), (dict(heads=1, head_dim=64), SHAPE), (dict(heads=0), INVALID),
+    (dict(seq=3), SHAPE), (dict(seq=0), INVALID), (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(gamma_q=None), INVALID), (dict(cos_t=U), MISALIGNED), (dict(v=U), MISALIGNED),
+    (dict(k=None), INVALID),
+])
+def test_qkv_rejects(lib, epi_kw, code):
+    assert _gq(lib, _epi(**epi_kw)) == code
+    assert _lq(lib, _epi(**epi_kw)) == code
+
+
+def test_qkv_rejects_operands(lib):
+    assert _gq(lib, None) == INVALID
+    assert _gq(lib, _epi(), K=100) == SHAPE
+    assert _gq(lib, _epi(), r=17) == SHAPE
+    assert _gq(lib, _epi(), qa=0) == INVALID
+    assert _gq(lib, _epi(), bias=U) == MISALIGNED
+    assert _gq(lib, _epi(), r=0) == INVALID          # xl1 / L2 must be NULL at r == 0
+    assert _lq(lib, _epi(), ws_bytes=10) == WS_SMALL
+    assert _lq(lib, _epi(), X=0) == INVALID
+    # M == 0: no-op; the epilogue's shape rules still apply
+    assert _gq(lib, _epi(q=0, k=0, v=0, gamma_q=0, gamma_k=0, cos_t=0, sin_t=0), M=0,
+               qa=0, sa=0, qw=0, sw=0, xl1=0, L2=0, bias=0) == OK
+    assert _gq(lib, _epi(head_dim=96), M=0) == SHAPE
+
+
+def test_qkv_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of svdq_qkv_epilogue has the C compiler's size and offsets."""
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "svdq.h"\n'
+                   "int main(void) { printf(\"%zu\", sizeof(svdq_qkv_epilogue));\n"
+                   + "".join('printf(" %%zu", offsetof(svdq_qkv_epilogue, %s));\n' % f
+                             for f, _ in _binding.QkvEpilogue._fields_)
+                   + "return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(_binding.QkvEpilogue)] + [getattr(_binding.QkvEpilogue, f).offset
+                                                    for f, _ in _binding.QkvEpilogue._fields_]
+    assert got == want
