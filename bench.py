@@ -61,22 +61,31 @@ def k2_bytes(M, N, K, r):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_lr_gemm_qkv_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "bit_diffusion_transformer_amd", "csrc", "w4a4_gemm.hip")
+_CSRC = os.path.join(ROOT, "bit_diffusion_transformer_amd", "csrc")
+GEMM_SOURCE = (os.path.join(_CSRC, "w4a4_tile.h"), os.path.join(_CSRC, "w4a4_gemm.hip"))
 
 
 # workload -> (committed counter summary, kernel source it was taken with)
 TRAFFIC = {
     "qkv": (None, None),
     "awq_mod": (os.path.join(ROOT, "profiles", "awq_w4a16_linear_mod_traffic.txt"),
-                os.path.join(ROOT, "bit_diffusion_transformer_amd", "csrc", "awq_w4a16.hip")),
+                (os.path.join(_CSRC, "awq_w4a16.hip"),)),
 }
+
+
+def source_sha256(paths):
+    """SHA-256 of the kernel's source files, concatenated in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
     """HBM bytes per call of the dominant kernel from the committed counter
     summary, if it was taken on this workload with the current kernel source;
     else None."""
-    import hashlib
     if workload not in TRAFFIC:
         return None
     path, source = TRAFFIC[workload]
@@ -89,8 +98,7 @@ def measured_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = hashlib.sha256(open(source, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != src or "traffic_bytes_per_call" not in kv:
+    if kv.get("kernel_source_sha256") != source_sha256(source) or "traffic_bytes_per_call" not in kv:
         return None
     return int(float(kv["traffic_bytes_per_call"]))
 

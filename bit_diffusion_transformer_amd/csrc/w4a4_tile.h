@@ -1,0 +1,714 @@
+// w4a4_tile.h -- the tile code of the SVDQuant W4A4 GEMM on gfx950 (internal;
+// not part of the ABI): operand staging, the K loop, the rank-r epilogue and
+// the two output epilogues (plain [M, N] store; fused QKV).  Included by the
+// plain GEMM and the fused-QKV GEMM, each in its own translation unit, so that
+// each kernel is scheduled on its own.
+#pragma once
+
+// The W4A4 GEMM of the SVDQuant layer on gfx950 with the
+// rank-r up-projection, bias and GELU applied to the same output tile before
+// its single bf16 store (the "Nunchaku engine design" section of the
+// svdq-int4-flux.1-canny-dev model card fuses the up-projection with the
+// 4-bit compute because both produce the same output).
+//
+// Output tiles are computed transposed, D[n][m] = Y[m][n]: the weight codes
+// are the MFMA A operand and the activation codes the B operand, so that an
+// output lane holds four consecutive n of one token row and stores them as
+// one 8-byte write.
+//
+// Per group of 64 along K and per 32 x 32 output block the wave issues
+//   - two v_mfma_i32_32x32x32_i8 on the widened codes (the two k halves of
+//     the group, accumulated in the matrix unit): S, exact int32;
+//   - one v_mfma_f32_32x32x8_bf16 that forms the scale products
+//     P[n][m] = sw[n] sa[m] as an outer product of bf16 hi/lo pairs
+//     ((sw_hi + sw_lo)(sa_hi + sa_lo), exact bf16 products, fp32 sums,
+//     ~2^-16 relative to the fp32 product) in the same output layout;
+// and the VALU does only acc = fma(float(S), P, acc).  Formed on the VALU,
+// the scale product would be a third VALU op per output and group; the
+// rescale is what bounds this kernel on this chip (one group of 64 MACs per
+// output costs 1/16 of a 32x32x32 MFMA but 2 wave-wide VALU ops), so it is
+// kept to the minimum.
+//
+// Data movement: packed 4-bit codes and raw fp32 scales go from global
+// memory straight into a four-stage LDS ring with global_load_lds (no
+// registers, no LDS write instructions), up to three stages ahead of the one
+// being read; each wave reads its fragments with 16-byte LDS reads
+// (XOR-swizzled rows, no bank conflicts) and widens the codes to int8 in
+// registers.
+#include "svdq_device.h"
+#include "svdq_internal.h"
+
+#define SVDQ_MAX_RANK_DEV 128
+
+namespace svdq {
+
+namespace {
+
+// Tiles are BT x BT outputs with BT = 64 WB, four waves in a 2 x 2 grid,
+// each wave WB x WB blocks of 32 x 32.  WB = 2 (128 x 128 tiles) is the main
+// shape; WB = 1 (64 x 64 quarter tiles) serves the tiles of a partial last
+// round, so that they spread over four times as many workgroups.
+constexpr int GC = 2;              // K groups per stage
+constexpr int ROWP = GC * 32;      // packed bytes of one row per stage (4 x 16)
+constexpr int NBUF = 4;            // stages in the LDS ring
+constexpr int NTHR = 256;          // 4 waves
+constexpr int TILE = 128;          // the tile grid (a quarter tile is a quadrant of one)
+constexpr int GROUP_M = 8;         // m-tiles per raster group (L2 reuse of weights)
+
+template <int WB>
+struct Cfg {
+    static constexpr int BT = 64 * WB;
+    static constexpr int NB = WB * WB;                 // blocks per wave
+    // One stage in LDS: codes of the BT weight rows, then of the BT token
+    // rows (64 bytes per row; 16-byte segment s of tile row R sits at slot
+    // s ^ swz(R)), then the raw fp32 scales [row][group] of both.
+    static constexpr int A_OFF = 0;
+    static constexpr int B_OFF = A_OFF + BT * ROWP;
+    static constexpr int SA_OFF = B_OFF + BT * ROWP;
+    static constexpr int SB_OFF = SA_OFF + BT * GC * 4;
+    static constexpr int STAGE = SB_OFF + BT * GC * 4;
+    // global_load_lds instructions per wave per stage: WB code transfers per
+    // operand, and one scale transfer per operand (WB = 2) or one in total
+    static constexpr int LOADS = 2 * WB + (WB == 2 ? 2 : 1);
+};
+
+// Row swizzle of the 16-byte segments.  A 16-byte LDS read by 8 consecutive
+// lanes (rows R..R+7 of one segment) or by 16 consecutive lanes touches 8
+// (16) distinct 16-byte bank groups of 128 (256) bytes with this mapping.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+template <int WB>
+struct __align__(16) Smem {
+    union {
+        uint8_t ring[NBUF][Cfg<WB>::STAGE];
+        uint16_t l2t[Cfg<WB>::BT * (SVDQ_MAX_RANK_DEV + 8)];
+    } u;
+};
+static_assert(sizeof(Smem<2>) <= 80 * 1024, "two workgroups per CU");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Linear tile index -> (tm, tn) on the 128 x 128 grid: GROUP_M m-tiles per
+// raster group, so that consecutive tiles share weight rows in L2.
+__device__ __forceinline__ void raster(int64_t id, int64_t nbm, int64_t nbn, int64_t &tm,
+                                       int64_t &tn) {
+    const int64_t per_group = (int64_t)GROUP_M * nbn;
+    const int64_t grp = id / per_group;
+    const int64_t first_m = grp * GROUP_M;
+    const int64_t gsize = (nbm - first_m) < GROUP_M ? (nbm - first_m) : GROUP_M;
+    const int64_t in_grp = id - grp * per_group;
+    tm = first_m + in_grp % gsize;
+    tn = in_grp / gsize;
+}
+
+// Loop-invariant plan of one wave's global -> LDS copies of a stage.  Code
+// transfers: 1 KB each, lane l carries row 16 WB w + 16 i + l / 4 of its
+// operand into LDS slot l % 4.  Scale transfers: 256 bytes, lane l carries
+// row 32 j + l / 2, group l % 2 (WB = 2: block j = w of both operands;
+// WB = 1: waves 0, 1 the weight rows, waves 2, 3 the token rows).  Rows past
+// the matrix re-read its last row (never stored); a stage that holds only
+// one group (odd group count) re-reads that group for the second.  Offsets
+// are unsigned bytes from the tile's first row, so each copy is a uniform
+// (scalar) base plus a per-lane 32-bit offset.
+template <int WB>
+struct CopyPlan {
+    uint32_t a_off[WB], b_off[WB];   // code transfers
+    uint32_t a_tail[WB], b_tail[WB]; // same for a one-group stage
+    uint32_t s_off[2], s_tail[2];    // scale transfers (weights, tokens)
+    int wave;                        // wave index (uniform)
+};
+
+struct Operands {
+    const uint8_t *qw0, *qa0;      // first row of the tile
+    const uint8_t *sw0, *sa0;      // (scales, as bytes)
+};
+
+template <int WB>
+__device__ __forceinline__ void issue_copies(uint8_t *st, const Operands &op, int c, int wave,
+                                             const uint32_t (&ao)[WB], const uint32_t (&bo)[WB],
+                                             const uint32_t (&so)[2]) {
+    using C = Cfg<WB>;
+    const uint8_t *qws = op.qw0 + c * ROWP;
+    const uint8_t *qas = op.qa0 + c * ROWP;
+#pragma unroll
+    for (int i = 0; i < WB; ++i) {
+        const int row = 16 * WB * wave + 16 * i;
+        __builtin_amdgcn_global_load_lds(qws + ao[i], (lds_void *)(st + C::A_OFF + row * ROWP), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qas + bo[i], (lds_void *)(st + C::B_OFF + row * ROWP), 16, 0, 0);
+    }
+    if (WB == 2) {
+        __builtin_amdgcn_global_load_lds(op.sw0 + c * GC * 4 + so[0],
+                                         (lds_void *)(st + C::SA_OFF + 32 * wave * GC * 4), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(op.sa0 + c * GC * 4 + so[1],
+                                         (lds_void *)(st + C::SB_OFF + 32 * wave * GC * 4), 4, 0, 0);
+    } else if (wave < 2) {
+        __builtin_amdgcn_global_load_lds(op.sw0 + c * GC * 4 + so[0],
+                                         (lds_void *)(st + C::SA_OFF + 32 * wave * GC * 4), 4, 0, 0);
+    } else {
+        __builtin_amdgcn_global_load_lds(op.sa0 + c * GC * 4 + so[1],
+                                         (lds_void *)(st + C::SB_OFF + 32 * (wave - 2) * GC * 4), 4, 0, 0);
+    }
+}
+
+template <int WB>
+__device__ __forceinline__ void issue_stage(uint8_t *st, const CopyPlan<WB> &cp,
+                                            const Operands &op, int c, bool one_group) {
+    if (one_group)
+        issue_copies<WB>(st, op, c, cp.wave, cp.a_tail, cp.b_tail, cp.s_tail);
+    else
+        issue_copies<WB>(st, op, c, cp.wave, cp.a_off, cp.b_off, cp.s_off);
+}
+
+// Wait until at most `n` stages of this wave's copies are in flight (in the
+// main loop the only outstanding vector-memory instructions are these) and
+// this wave's LDS reads have returned (the barrier that follows releases the
+// buffer they read for refilling).
+template <int L>
+__device__ __forceinline__ void wait_stages(int n) {
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    constexpr int kNoExp = (0x7 << 4);
+    constexpr int v1 = L, v2 = 2 * L, v3 = 3 * L;
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(kNoExp); break;
+    case 1: __builtin_amdgcn_s_waitcnt((v1 & 0xF) | ((v1 >> 4) << 14) | kNoExp); break;
+    case 2: __builtin_amdgcn_s_waitcnt((v2 & 0xF) | ((v2 >> 4) << 14) | kNoExp); break;
+    default: __builtin_amdgcn_s_waitcnt((v3 & 0xF) | ((v3 >> 4) << 14) | kNoExp); break;
+    }
+}
+
+// Workgroup barrier without a memory fence: the copies of the other stages
+// stay in flight across it.  The clobber keeps the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Loop-invariant LDS offsets of one lane's fragment reads.
+struct ReadPlan {
+    int a_code[GC], b_code[GC];    // block 0; block j is 32 j rows further
+    int a_scale, b_scale;          // group 0 of block 0
+    bool keep_b;                   // k-slot 0 lanes carry the token scale
+};
+
+template <int WB>
+struct Raw {
+    u32x4 a[WB], b[WB];
+    float sa[WB], sb[WB];
+};
+template <int WB>
+struct Frags {
+    i32x4 A[WB][2], B[WB][2];      // [block][k half]
+    u32x2 AS[WB], BS[WB];
+};
+
+template <int WB>
+__device__ __forceinline__ void read_raw(Raw<WB> &rw, const uint8_t *st, const ReadPlan &rp,
+                                         int gi) {
+#pragma unroll
+    for (int blk = 0; blk < WB; ++blk) {
+        rw.a[blk] = *reinterpret_cast<const u32x4 *>(st + rp.a_code[gi] + blk * 32 * ROWP);
+        rw.b[blk] = *reinterpret_cast<const u32x4 *>(st + rp.b_code[gi] + blk * 32 * ROWP);
+        rw.sa[blk] = *reinterpret_cast<const float *>(st + rp.a_scale + blk * 32 * GC * 4 + 4 * gi);
+        rw.sb[blk] = *reinterpret_cast<const float *>(st + rp.b_scale + blk * 32 * GC * 4 + 4 * gi);
+    }
+}
+
+// Widen the codes and build the scale operands.  A lane holds 32 codes of
+// its row: k half h of the group takes codes [16 h, 16 h + 16) of them in
+// both operands, so the pairing of k is the same on both sides.  Weight scale
+// operand: bf16 (hi, hi, lo, lo) of sw * 2^-8 (the 2^-8 undoes the x16 of
+// both widened operands; exact).  Token operand: (hi, lo, hi, lo) of sa on
+// k-slot 0 lanes and zero elsewhere; `keep` false also zeroes a group past K,
+// which then adds exactly nothing.
+template <int WB>
+__device__ __forceinline__ void make_frags(Frags<WB> &f, const Raw<WB> &rw, bool keep) {
+#pragma unroll
+    for (int blk = 0; blk < WB; ++blk) {
+        f.A[blk][0] = widen_nibbles(u32x2{rw.a[blk].x, rw.a[blk].y});
+        f.A[blk][1] = widen_nibbles(u32x2{rw.a[blk].z, rw.a[blk].w});
+        f.B[blk][0] = widen_nibbles(u32x2{rw.b[blk].x, rw.b[blk].y});
+        f.B[blk][1] = widen_nibbles(u32x2{rw.b[blk].z, rw.b[blk].w});
+        const float va = rw.sa[blk] * 0.00390625f;
+        const uint32_t ha = pack_bf16x2(va, va);
+        const float la = va - bf16_lo(ha);
+        f.AS[blk] = u32x2{ha, pack_bf16x2(la, la)};
+        const float vb = keep ? rw.sb[blk] : 0.0f;
+        const uint32_t hb = pack_bf16x2(vb, 0.0f);
+        const uint32_t hl = pack_bf16x2(vb, vb - bf16_lo(hb));
+        f.BS[blk] = u32x2{hl, hl};
+    }
+}
+
+// The MFMA -> VALU pipeline of a wave.  The blocks of the two groups of a
+// stage form one stream j = 0 .. 2 NB - 1 (block j % NB, result slot j & 1):
+// the three MFMAs of block j go out while the VALU converts and accumulates
+// block j - 1, so the matrix unit and the VALU work side by side, also
+// across the group boundary.
+struct Pipe {
+    i32x16 S[2];
+    f32x16 P[2];
+};
+
+template <int WB>
+__device__ __forceinline__ void issue_block(Pipe &p, const Frags<WB> &f, int t, int k) {
+    const int bi = t / WB, bj = t % WB;
+    p.S[k] = mfma_i8_32x32x32(f.A[bi][0], f.B[bj][0], i32x16{});
+    p.S[k] = mfma_i8_32x32x32(f.A[bi][1], f.B[bj][1], p.S[k]);
+    p.P[k] = mfma_bf16_32x32x8(f.AS[bi], f.BS[bj], f32x16{});
+}
+
+template <int NB>
+__device__ __forceinline__ void valu_block(f32x16 (&acc)[NB], const Pipe &p, int t, int k) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        acc[t][i] = __builtin_fmaf((float)p.S[k][i], p.P[k][i], acc[t][i]);
+}
+
+// Issue stream element j while the VALU finishes element j - 1: one MFMA,
+// then about a third of the VALU work, three times.  The empty asm pins the
+// updated accumulator so later passes cannot sink the VALU work below the
+// following MFMAs.
+template <int WB>
+__device__ __forceinline__ void pair(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f, int j) {
+    constexpr int NB = WB * WB;
+    issue_block<WB>(p, f, j % NB, j & 1);
+    valu_block<NB>(acc, p, (j - 1) % NB, (j - 1) & 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+    asm volatile("" : "+v"(acc[(j - 1) % NB]));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int WB>
+__device__ __forceinline__ void group_first(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f) {
+    issue_block<WB>(p, f, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 1; j < WB * WB; ++j) pair<WB>(acc, p, f, j);
+}
+template <int WB>
+__device__ __forceinline__ void group_second(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f) {
+#pragma unroll
+    for (int j = WB * WB; j < 2 * WB * WB; ++j) pair<WB>(acc, p, f, j);
+}
+template <int WB>
+__device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p) {
+    constexpr int NB = WB * WB;
+    valu_block<NB>(acc, p, NB - 1, 1);
+    asm volatile("" : "+v"(acc[NB - 1]));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The K loop.  The four ring buffers are separate restrict pointers so that
+// the compiler can tell a read of one stage from the copies still landing in
+// the others (otherwise every LDS read would wait for all copies).
+template <int WB>
+__device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__restrict__ b1,
+                                       uint8_t *__restrict__ b2, uint8_t *__restrict__ b3,
+                                       const CopyPlan<WB> &cp, const ReadPlan &rp,
+                                       const Operands &op, int ns, bool odd,
+                                       f32x16 (&acc)[WB * WB]) {
+    constexpr int L = Cfg<WB>::LOADS;
+    // prologue: stages 0..3 in flight, stage 0 visible, group 0 in registers
+    issue_stage<WB>(b0, cp, op, 0, odd && ns == 1);
+    if (ns > 1) issue_stage<WB>(b1, cp, op, 1, odd && ns == 2);
+    if (ns > 2) issue_stage<WB>(b2, cp, op, 2, odd && ns == 3);
+    if (ns > 3) issue_stage<WB>(b3, cp, op, 3, odd && ns == 4);
+    wait_stages<L>(ns < 4 ? ns - 1 : 3);
+    barrier();
+    Raw<WB> raw;
+    Frags<WB> f;
+    read_raw<WB>(raw, b0, rp, 0);
+    make_frags<WB>(f, raw, rp.keep_b);
+
+    // Stage s: group 2s computes while group 2s + 1 is read; then stage
+    // s + 1 is published and stage s's buffer (read by every wave before
+    // the barrier) is refilled with stage s + 4; group 2s + 1 computes
+    // while the first group of stage s + 1 is read.
+    auto step = [&](int s, uint8_t *cur, uint8_t *nxt) {
+        Pipe p;
+        read_raw<WB>(raw, cur, rp, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        group_first<WB>(acc, p, f);
+        make_frags<WB>(f, raw, rp.keep_b && !(odd && s == ns - 1));
+        wait_stages<L>(s + 1 < ns ? (ns - 2 - s < 2 ? ns - 2 - s : 2) : 0);
+        barrier();
+        if (s + 4 < ns) issue_stage<WB>(cur, cp, op, s + 4, odd && s + 4 == ns - 1);
+        // (after the last stage this reads a stale, unused buffer: no branch,
+        // so the fragments carry no merge of old and new values)
+        read_raw<WB>(raw, nxt, rp, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        group_second<WB>(acc, p, f);
+        make_frags<WB>(f, raw, rp.keep_b);
+        group_drain<WB>(acc, p);
+    };
+    for (int s = 0; s < ns; s += 4) {
+        step(s, b0, b1);
+        if (s + 1 >= ns) break;
+        step(s + 1, b1, b2);
+        if (s + 2 >= ns) break;
+        step(s + 2, b2, b3);
+        if (s + 3 >= ns) break;
+        step(s + 3, b3, b0);
+    }
+}
+
+}  // namespace
+
+namespace {
+
+// Fused QKV epilogue of a 128 x 128 tile (the "Bringing Nunchaku 4-bit
+// inference to Diffusers" blog, the fused_qkv_norm_rottary listing: Q, K and
+// V from one projection, norm_q / norm_k, then the rotary embedding, in one
+// operator).  The tile lies in one section of [Q | K | V] (H D % 128 == 0).
+// For Q and K: per token and head, rho = sqrt(mean(x^2) + eps) over the head's
+// D columns (D = 128: the whole tile width, the two column-half waves swap
+// their partial sums through LDS and both add them in the same order; D = 64:
+// the wave's own 64 columns), v = x gamma / rho, then each adjacent pair
+// (2p, 2p + 1) -- two consecutive values of the same lane -- turns by the
+// caller's (cos, sin) of position s = m mod S.  V is only re-laid out.  The
+// stores go to [B, H, S, D] as 8-byte writes of four consecutive d.
+template <int WB>
+__device__ __forceinline__ void
+qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk,
+             Smem<WB> &sm, int64_t M, int64_t m0, int64_t n0, int wn, int wm, int r32,
+             int ks2) {
+    constexpr int NB = WB * WB;
+    const int D = qk.D;
+    const int64_t HD = (int64_t)qk.H * D;
+    const int sec = (int)(n0 / HD);
+    const int64_t nsec = n0 - sec * HD;        // section column of the tile's left edge
+    const int64_t S = qk.S;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        const int bi = t / WB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2 b2 = bb[bi][q];
+            acc[t][4 * q + 0] += bf16_lo(b2.x);
+            acc[t][4 * q + 1] += bf16_hi(b2.x);
+            acc[t][4 * q + 2] += bf16_lo(b2.y);
+            acc[t][4 * q + 3] += bf16_hi(b2.y);
+        }
+    }
+    // token of the lane in each column block bj: row offset in [B, H, S, D]
+    int64_t tok[WB];
+    int64_t spos[WB];
+    bool live[WB];
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) {
+        const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+        live[bj] = m < M;
+        const int64_t mc = m < M ? m : M - 1;
+        const int64_t b = mc / S;
+        spos[bj] = mc - b * S;
+        tok[bj] = (b * qk.H * S + spos[bj]) * D;
+    }
+    if (sec == 2) {
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t nl = nsec + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+                const int64_t h = nl / D, d = nl - h * D;
+#pragma unroll
+                for (int bj = 0; bj < WB; ++bj) {
+                    if (!live[bj]) continue;
+                    const int t = bi * WB + bj;
+                    u32x2 out;
+                    out.x = pack_bf16x2(acc[t][4 * q], acc[t][4 * q + 1]);
+                    out.y = pack_bf16x2(acc[t][4 * q + 2], acc[t][4 * q + 3]);
+                    *reinterpret_cast<u32x2 *>(qk.V + tok[bj] + h * S * D + d) = out;
+                }
+            }
+        }
+        return;
+    }
+    // sum of squares of each token over this wave's columns (and the partner
+    // lane l ^ 32, which holds the other half of every 8-column group)
+    float ss[WB];
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) {
+        float a = 0.0f;
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a = fmaf(acc[bi * WB + bj][i], acc[bi * WB + bj][i], a);
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a),
+                                                        false, false);
+        ss[bj] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    if (D == 128) {
+        __syncthreads();   // every wave is past its reads of the L2^T staging
+        float *xs = reinterpret_cast<float *>(&sm.u);   // [wn][wm][bj][32]
+        if (ks2 == 0) {
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) xs[((wn * 2 + wm) * WB + bj) * 32 + r32] = ss[bj];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int bj = 0; bj < WB; ++bj)
+            ss[bj] = xs[((0 * 2 + wm) * WB + bj) * 32 + r32] + xs[((1 * 2 + wm) * WB + bj) * 32 + r32];
+    }
+    float inv[WB];
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) inv[bj] = 1.0f / sqrtf(ss[bj] / (float)D + qk.eps);
+    const uint16_t *gam = sec == 0 ? qk.gq : qk.gk;
+    uint16_t *dst = sec == 0 ? qk.Q : qk.K;
+    const int half = D / 2;
+#pragma unroll
+    for (int bi = 0; bi < WB; ++bi) {
+        u32x2 g4[4];
+        f32x2 cs[4][WB], sn[4][WB];
+        int64_t hoff[4], dd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t nl = nsec + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+            const int64_t h = nl / D;
+            dd[q] = nl - h * D;
+            hoff[q] = h * S * D;
+            g4[q] = *reinterpret_cast<const u32x2 *>(gam + dd[q]);
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) {
+                const int64_t at = spos[bj] * half + dd[q] / 2;
+                cs[q][bj] = *reinterpret_cast<const f32x2 *>(qk.cos_t + at);
+                sn[q][bj] = *reinterpret_cast<const f32x2 *>(qk.sin_t + at);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float gv[4] = {bf16_lo(g4[q].x), bf16_hi(g4[q].x), bf16_lo(g4[q].y),
+                                 bf16_hi(g4[q].y)};
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) {
+                if (!live[bj]) continue;
+                const int t = bi * WB + bj;
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = acc[t][4 * q + j] * inv[bj] * gv[j];
+                const float o0 = v[0] * cs[q][bj].x - v[1] * sn[q][bj].x;
+                const float o1 = v[0] * sn[q][bj].x + v[1] * cs[q][bj].x;
+                const float o2 = v[2] * cs[q][bj].y - v[3] * sn[q][bj].y;
+                const float o3 = v[2] * sn[q][bj].y + v[3] * cs[q][bj].y;
+                u32x2 out;
+                out.x = pack_bf16x2(o0, o1);
+                out.y = pack_bf16x2(o2, o3);
+                *reinterpret_cast<u32x2 *>(dst + tok[bj] + hoff[q] + dd[q]) = out;
+            }
+        }
+    }
+}
+
+// One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0);
+// QKV: the fused QKV epilogue instead of the plain store (WB = 2 only).
+template <int WB, bool QKV = false>
+__device__ __forceinline__ void
+tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
+          const uint8_t *__restrict__ qw, const float *__restrict__ sw,
+          const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
+          const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N, int64_t K, int r,
+          uint16_t *__restrict__ Y, Smem<WB> &sm, int64_t m0, int64_t n0,
+          const QkvArgs *qk = nullptr) {
+    using C = Cfg<WB>;
+    constexpr int BT = C::BT, NB = C::NB;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave >> 1, wm = wave & 1;
+    const int r32 = lane & 31, ks2 = lane >> 5;
+    const int G = (int)(K / kGroup);
+    const int kb = (int)(K / 2);
+    const int ns = (G + GC - 1) / GC;          // stages; only the last may hold one group
+    const bool odd = (G & 1) != 0;
+    const int nlast = (int)((N - n0 < BT ? N - n0 : BT) - 1);
+    const int mlast = (int)((M - m0 < BT ? M - m0 : BT) - 1);
+
+    Operands op;
+    op.qw0 = qw + n0 * (int64_t)kb;
+    op.qa0 = qa + m0 * (int64_t)kb;
+    op.sw0 = reinterpret_cast<const uint8_t *>(sw + n0 * (int64_t)G);
+    op.sa0 = reinterpret_cast<const uint8_t *>(sa + m0 * (int64_t)G);
+
+    CopyPlan<WB> cp;
+    cp.wave = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int i = 0; i < WB; ++i) {
+        const int row = 16 * WB * wave + 16 * i + (lane >> 2);
+        const int seg = (lane & 3) ^ swz(row);     // global segment landing in this lane's slot
+        const int ra = min(row, nlast), rb = min(row, mlast);
+        cp.a_off[i] = (uint32_t)(ra * kb + 16 * seg);
+        cp.b_off[i] = (uint32_t)(rb * kb + 16 * seg);
+        cp.a_tail[i] = (uint32_t)(ra * kb + 16 * (seg & 1));
+        cp.b_tail[i] = (uint32_t)(rb * kb + 16 * (seg & 1));
+    }
+    {
+        const int blk = WB == 2 ? wave : (wave & 1);
+        const int row = 32 * blk + (lane >> 1);
+        const int g = lane & 1;
+        cp.s_off[0] = (uint32_t)(4 * (min(row, nlast) * G + g));
+        cp.s_off[1] = (uint32_t)(4 * (min(row, mlast) * G + g));
+        cp.s_tail[0] = (uint32_t)(4 * min(row, nlast) * G);
+        cp.s_tail[1] = (uint32_t)(4 * min(row, mlast) * G);
+    }
+
+    ReadPlan rp;
+    {
+        // rows wn * 32 WB + 32 blk + r32 (and wm ...) all share swz(r32)
+        const int x = swz(r32);
+#pragma unroll
+        for (int gi = 0; gi < GC; ++gi) {
+            const int slot = (2 * gi + ks2) ^ x;
+            rp.a_code[gi] = C::A_OFF + (wn * 32 * WB + r32) * ROWP + 16 * slot;
+            rp.b_code[gi] = C::B_OFF + (wm * 32 * WB + r32) * ROWP + 16 * slot;
+        }
+        rp.a_scale = C::SA_OFF + (wn * 32 * WB + r32) * GC * 4;
+        rp.b_scale = C::SB_OFF + (wm * 32 * WB + r32) * GC * 4;
+        rp.keep_b = ks2 == 0;
+    }
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) acc[t] = f32x16{};
+
+    k_loop<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, odd, acc);
+    __syncthreads();
+
+    // ---- epilogue: rank-r up-projection on the same tile (bf16 MFMA, the
+    // fp32 xl1 split into a bf16 hi/lo pair), then bias, activation, store.
+    // Its global loads go out together so that their latencies overlap: the
+    // lane's xl1 for the first 32 ranks, the bias of its columns, and the L2
+    // rows the workgroup stages as L2^T in LDS.
+    f32x4 xp[WB][2][2];                        // [bj][16-rank chunk][half]
+    if (r > 0) {
+#pragma unroll
+        for (int bj = 0; bj < WB; ++bj) {
+            const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+            const int64_t mc = m < M ? m : M - 1;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                if (16 * c < r) {
+                    const f32x4 *p = reinterpret_cast<const f32x4 *>(xl1 + mc * r + 16 * c + 8 * ks2);
+                    xp[bj][c][0] = p[0];
+                    xp[bj][c][1] = p[1];
+                }
+            }
+        }
+    }
+    u32x2 bb[WB][4];
+#pragma unroll
+    for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+            bb[bi][q] = (bias && n < N) ? *reinterpret_cast<const u32x2 *>(bias + n) : u32x2{0u, 0u};
+        }
+    }
+    if (r > 0) {
+        const int lstr = r + 8;   // bf16 elements per LDS row of L2^T
+        uint16_t *l2t = sm.u.l2t;
+        // Thread q stages rank rows [8 c, 8 c + 8) of column n = q % BT as one
+        // 16-byte row segment of L2^T (consecutive lanes: consecutive n, so
+        // both the global reads and the LDS writes are conflict-free).
+        for (int q = tid; q < r * (BT / 8); q += NTHR) {
+            const int n = q % BT;
+            const int c = q / BT;
+            uint32_t v[4] = {0u, 0u, 0u, 0u};
+            if (n0 + n < N) {
+                const uint16_t *src = L2 + (int64_t)(8 * c) * N + n0 + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = (uint32_t)src[(2 * e) * N] | ((uint32_t)src[(2 * e + 1) * N] << 16);
+            }
+            *reinterpret_cast<u32x4 *>(&l2t[n * lstr + 8 * c]) = u32x4{v[0], v[1], v[2], v[3]};
+        }
+        __syncthreads();
+        // 16 ranks: L2^T rows from LDS (A), xl1 hi/lo of the lane's rows (B).
+        auto chunk = [&](int c16, const f32x4 (&x)[WB][2]) {
+            const int i0 = c16 + 8 * ks2;
+            u32x4 AL[WB];
+#pragma unroll
+            for (int bi = 0; bi < WB; ++bi) {
+                const int row = wn * 32 * WB + 32 * bi + r32;
+                AL[bi] = *reinterpret_cast<const u32x4 *>(&l2t[row * lstr + i0]);
+            }
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) {
+                const float xs[8] = {x[bj][0].x, x[bj][0].y, x[bj][0].z, x[bj][0].w,
+                                     x[bj][1].x, x[bj][1].y, x[bj][1].z, x[bj][1].w};
+                u32x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t h = pack_bf16x2(xs[2 * e], xs[2 * e + 1]);
+                    hi[e] = h;
+                    lo[e] = pack_bf16x2(xs[2 * e] - bf16_lo(h), xs[2 * e + 1] - bf16_hi(h));
+                }
+#pragma unroll
+                for (int bi = 0; bi < WB; ++bi) {
+                    acc[bi * WB + bj] = mfma_bf16_32x32x16(AL[bi], hi, acc[bi * WB + bj]);
+                    acc[bi * WB + bj] = mfma_bf16_32x32x16(AL[bi], lo, acc[bi * WB + bj]);
+                }
+            }
+        };
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if (16 * c < r) {
+                f32x4 x[WB][2];
+#pragma unroll
+                for (int bj = 0; bj < WB; ++bj) {
+                    x[bj][0] = xp[bj][c][0];
+                    x[bj][1] = xp[bj][c][1];
+                }
+                chunk(16 * c, x);
+            }
+        }
+        for (int c16 = 32; c16 < r; c16 += 16) {
+            f32x4 x[WB][2];
+#pragma unroll
+            for (int bj = 0; bj < WB; ++bj) {
+                const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+                const int64_t mc = m < M ? m : M - 1;
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(xl1 + mc * r + c16 + 8 * ks2);
+                x[bj][0] = p[0];
+                x[bj][1] = p[1];
+            }
+            chunk(c16, x);
+        }
+    }
+
+    if constexpr (QKV) {
+        qkv_epilogue<WB>(acc, bb, *qk, sm, M, m0, n0, wn, wm, r32, ks2);
+        return;
+    }
+    // Block (bi, bj); element i of the lane is n = base + 8 (i / 4) +
+    // 4 (lane / 32) + i % 4, m = base + lane % 32.
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        const int bi = t / WB, bj = t % WB;
+        const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+            if (n >= N) continue;
+            const u32x2 b2 = bb[bi][q];
+            const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x = acc[t][4 * q + j] + bv[j];
+                if (act == 1) x = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+                o[j] = x;
+            }
+            u32x2 out;
+            out.x = pack_bf16x2(o[0], o[1]);
+            out.y = pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<u32x2 *>(Y + m * N + n) = out;
+        }
+    }
+}
+
+}  // namespace
+
+}  // namespace svdq
