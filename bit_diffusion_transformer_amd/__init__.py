@@ -24,7 +24,10 @@ from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError, 
                        svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
                        svdq_pack_weights, svdq_quantize_act_down,
                        svdq_quantize_act_down_workspace_bytes, svdq_status_string,
-                       svdq_w4a4_lr_gemm, svdq_w4a4_lr_gemm_qkv, svdq_linear_qkv)
+                       svdq_w4a4_lr_gemm, svdq_w4a4_lr_gemm_qkv, svdq_linear_qkv,
+                       svdq_w4a4_lr_gemm_quant_down,
+                       svdq_w4a4_lr_gemm_quant_down_workspace_bytes, svdq_mlp,
+                       svdq_mlp_workspace_bytes)
 
 
 def _bits(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
@@ -150,6 +153,43 @@ def linear_qkv(X, lam, L1, qw, sw, L2, bias, heads: int, head_dim: int, seq: int
     svdq_linear_qkv(_bits(X), lam, _bits(L1) if r > 0 else None, qw, sw,
                     _bits(L2) if r > 0 else None, _bits(bias), M, K, r, epi, workspace, need)
     return Q, Kt, V
+
+
+def w4a4_lr_gemm_quant_down(qa, sa, qw, sw, xl1, L2, bias, act, lambda_next, L1_next):
+    """The GEMM whose output feeds the next layer -> that layer's (qa, sa, xl1)."""
+    M, K = qa.shape[0], qa.shape[1] * 2
+    N = qw.shape[0]
+    r = _rank(L2, 0)
+    rn = _rank(L1_next, 1)
+    dev = qa.device
+    qa_n = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    sa_n = torch.empty((M, N // GROUP), dtype=torch.float32, device=dev)
+    xl1_n = torch.empty((M, rn), dtype=torch.float32, device=dev) if rn > 0 else None
+    need = svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, rn)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    svdq_w4a4_lr_gemm_quant_down(qa, sa, qw, sw, xl1 if r > 0 else None,
+                                 _bits(L2) if r > 0 else None, _bits(bias), act, M, N, K, r,
+                                 lambda_next, _bits(L1_next) if rn > 0 else None, rn, qa_n, sa_n,
+                                 xl1_n, ws, need)
+    return qa_n, sa_n, xl1_n
+
+
+def mlp(X, up: dict, down: dict, act: int = ACT_GELU,
+        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = down(act(up(X))) through svdq_mlp; up / down: dicts with lam, L1, qw, sw, L2, bias."""
+    M, K = X.shape
+    Nh = up["qw"].shape[0]
+    ru, rd = _rank(up["L1"], 1), _rank(down["L1"], 1)
+    need = svdq_mlp_workspace_bytes(M, K, Nh, ru, rd)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    svdq_mlp(_bits(X), up["lam"], _bits(up["L1"]) if ru else None, up["qw"], up["sw"],
+             _bits(up["L2"]) if ru else None, _bits(up.get("bias")), down["lam"],
+             _bits(down["L1"]) if rd else None, down["qw"], down["sw"],
+             _bits(down["L2"]) if rd else None, _bits(down.get("bias")), act, M, K, Nh, ru, rd,
+             _bits(Y), workspace, need)
+    return Y
 
 
 def group_sums(qa, qw, m0: int, n0: int, tm: int, tn: int) -> torch.Tensor:

@@ -31,6 +31,8 @@ EXPORTS = (
     "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
     "svdq_debug_set_tile_policy", "svdq_awq_packed_bytes", "svdq_awq_pack_weights",
     "svdq_awq_repack", "svdq_awq_w4a16_linear", "svdq_w4a4_lr_gemm_qkv", "svdq_linear_qkv",
+    "svdq_w4a4_lr_gemm_quant_down_workspace_bytes", "svdq_w4a4_lr_gemm_quant_down",
+    "svdq_mlp_workspace_bytes", "svdq_mlp",
 )
 
 
@@ -97,6 +99,12 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
                                    ctypes.POINTER(QkvEpilogue), P], I32),
         "svdq_linear_qkv": ([P, P, P, P, P, P, P, I64, I64, I32, ctypes.POINTER(QkvEpilogue),
                              P, SZ, P], I32),
+        "svdq_w4a4_lr_gemm_quant_down_workspace_bytes": ([I64, I64, I32], SZ),
+        "svdq_w4a4_lr_gemm_quant_down": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, I32,
+                                          P, P, P, P, SZ, P], I32),
+        "svdq_mlp_workspace_bytes": ([I64, I64, I64, I32, I32], SZ),
+        "svdq_mlp": ([P, P, P, P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, I32, I32, P, P,
+                      SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -218,3 +226,30 @@ def svdq_linear_qkv(X, lam, L1, qw, sw, L2, bias, M, K, r, epi: QkvEpilogue, wor
     _check(load_library().svdq_linear_qkv(_p(X), _p(lam), _p(L1), _p(qw), _p(sw), _p(L2),
                                           _p(bias), M, K, r, ctypes.byref(epi), _p(workspace),
                                           ws_bytes, _stream(stream)), "svdq_linear_qkv")
+
+
+def svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, r_next) -> int:
+    return int(load_library().svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, r_next))
+
+
+def svdq_w4a4_lr_gemm_quant_down(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, lambda_next,
+                                 L1_next, r_next, qa_next, sa_next, xl1_next, workspace,
+                                 ws_bytes, stream=None):
+    _check(load_library().svdq_w4a4_lr_gemm_quant_down(
+        _p(qa), _p(sa), _p(qw), _p(sw), _p(xl1), _p(L2), _p(bias), act, M, N, K, r,
+        _p(lambda_next), _p(L1_next), r_next, _p(qa_next), _p(sa_next), _p(xl1_next),
+        _p(workspace), ws_bytes, _stream(stream)), "svdq_w4a4_lr_gemm_quant_down")
+
+
+def svdq_mlp_workspace_bytes(M, K, N_hidden, r_up, r_down) -> int:
+    return int(load_library().svdq_mlp_workspace_bytes(M, K, N_hidden, r_up, r_down))
+
+
+def svdq_mlp(X, lambda_up, L1_up, qw_up, sw_up, L2_up, bias_up, lambda_down, L1_down, qw_down,
+             sw_down, L2_down, bias_down, act, M, K, N_hidden, r_up, r_down, Y, workspace,
+             ws_bytes, stream=None):
+    _check(load_library().svdq_mlp(
+        _p(X), _p(lambda_up), _p(L1_up), _p(qw_up), _p(sw_up), _p(L2_up), _p(bias_up),
+        _p(lambda_down), _p(L1_down), _p(qw_down), _p(sw_down), _p(L2_down), _p(bias_down),
+        act, M, K, N_hidden, r_up, r_down, _p(Y), _p(workspace), ws_bytes, _stream(stream)),
+        "svdq_mlp")

@@ -255,6 +255,13 @@ hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint1
     return hipGetLastError();
 }
 
+hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl1,
+                             hipStream_t stream) {
+    const unsigned rblocks = (unsigned)((total / 4 + 255) / 256);
+    xl1_reduce_kernel<<<rblocks, 256, 0, stream>>>(part, nc, total, xl1);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
                                hipStream_t stream) {
     const int64_t waves = (N + 15) / 16;

@@ -244,6 +244,52 @@ int32_t lds_limit(size_t *out) {
 
 }  // namespace
 
+namespace {
+
+size_t mlp_part_bytes(int64_t M, int64_t N, int32_t rn) {
+    return rn > 0 ? svdq::align256((size_t)(N / 128) * (size_t)M * (size_t)rn * 4) : 0;
+}
+
+int32_t check_next_shape(int64_t N, int32_t rn) {
+    if (N % 128 != 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
+                    "N must be a multiple of 128 for the fused activation step (got %lld)",
+                    (long long)N);
+    if (rn != 0 && rn != 16 && rn != 32)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
+                    "the fused activation step takes a next-layer rank of 0, 16 or 32 (got %d)", rn);
+    return SVDQ_OK;
+}
+
+struct MlpWorkspace {
+    LinearWorkspace up;
+    uint8_t *qa_h;
+    float *sa_h;
+    float *xl1_h;
+    float *part;
+    size_t bytes;
+};
+
+MlpWorkspace carve_mlp(void *base, int64_t M, int64_t K, int64_t Nh, int32_t r_up, int32_t r_down) {
+    using svdq::align256;
+    MlpWorkspace w{};
+    w.up = carve_linear(base, M, K, r_up);
+    char *p = static_cast<char *>(base);
+    size_t off = w.up.bytes;
+    w.qa_h = reinterpret_cast<uint8_t *>(p + off);
+    off += align256((size_t)M * (size_t)(Nh / 2));
+    w.sa_h = reinterpret_cast<float *>(p + off);
+    off += align256((size_t)M * (size_t)(Nh / SVDQ_GROUP) * 4);
+    w.xl1_h = r_down > 0 ? reinterpret_cast<float *>(p + off) : nullptr;
+    off += align256((size_t)M * (size_t)r_down * 4);
+    w.part = reinterpret_cast<float *>(p + off);
+    off += mlp_part_bytes(M, Nh, r_down);
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
@@ -398,6 +444,112 @@ int32_t svdq_linear_qkv(const uint16_t *X, const float *lambda, const uint16_t *
     return hip_status(svdq::launch_w4a4_gemm_qkv(w.qa, w.sa, qw, sw, w.xl1, L2, bias, M, K, r,
                                                  qkv_args(epi), s),
                       "w4a4_lr_gemm_qkv launch");
+}
+
+size_t svdq_w4a4_lr_gemm_quant_down_workspace_bytes(int64_t M, int64_t N, int32_t r_next) {
+    if (M < 0 || N < 0 || r_next < 0) return 0;
+    return mlp_part_bytes(M, N, r_next);
+}
+
+int32_t svdq_w4a4_lr_gemm_quant_down(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                                     const float *sw, const float *xl1, const uint16_t *L2,
+                                     const uint16_t *bias, int32_t act, int64_t M, int64_t N,
+                                     int64_t K, int32_t r, const float *lambda_next,
+                                     const uint16_t *L1_next, int32_t r_next, uint8_t *qa_next,
+                                     float *sa_next, float *xl1_next, void *workspace,
+                                     size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_n(N));
+    SVDQ_TRY(check_next_shape(N, r_next));
+    // the plain GEMM's checks, with the next layer's codes standing in for Y
+    SVDQ_TRY(validate_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r,
+                           reinterpret_cast<const uint16_t *>(qa_next)));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(lambda_next, "lambda_next"));
+    SVDQ_TRY(need_ptr(sa_next, "sa_next"));
+    SVDQ_TRY(lr_ptrs(L1_next, "L1_next", xl1_next, "xl1_next", r_next));
+    const size_t need = mlp_part_bytes(M, N, r_next);
+    if (ws_bytes < need)
+        return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed", ws_bytes,
+                    need);
+    if (need > 0) SVDQ_TRY(need_ptr(workspace, "workspace"));
+    SVDQ_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    svdq::MlpArgs ma{lambda_next, L1_next, r_next, qa_next, sa_next,
+                     static_cast<float *>(workspace)};
+    SVDQ_TRY(hip_status(svdq::launch_w4a4_gemm_mlp(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r,
+                                                   ma, s),
+                        "w4a4_lr_gemm_mlp launch"));
+    if (r_next == 0) return SVDQ_OK;
+    return hip_status(svdq::launch_xl1_reduce(ma.part, (int)(N / 128), M * (int64_t)r_next,
+                                              xl1_next, s),
+                      "xl1 reduce launch");
+}
+
+size_t svdq_mlp_workspace_bytes(int64_t M, int64_t K, int64_t N_hidden, int32_t r_up,
+                                int32_t r_down) {
+    if (M < 0 || K < 0 || N_hidden < 0 || r_up < 0 || r_down < 0) return 0;
+    return carve_mlp(nullptr, M, K, N_hidden, r_up, r_down).bytes;
+}
+
+int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_up,
+                 const uint8_t *qw_up, const float *sw_up, const uint16_t *L2_up,
+                 const uint16_t *bias_up, const float *lambda_down, const uint16_t *L1_down,
+                 const uint8_t *qw_down, const float *sw_down, const uint16_t *L2_down,
+                 const uint16_t *bias_down, int32_t act, int64_t M, int64_t K, int64_t N_hidden,
+                 int32_t r_up, int32_t r_down, uint16_t *Y, void *workspace, size_t ws_bytes,
+                 void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
+        return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
+    SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_n(K));            // the down layer's N
+    SVDQ_TRY(check_k(N_hidden));
+    SVDQ_TRY(check_n(N_hidden));
+    SVDQ_TRY(check_r(r_up));
+    SVDQ_TRY(check_r(r_down));
+    SVDQ_TRY(check_next_shape(N_hidden, r_down));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(X, "X"));
+    SVDQ_TRY(need_ptr(lambda_up, "lambda_up"));
+    SVDQ_TRY(need_ptr(qw_up, "qw_up"));
+    SVDQ_TRY(need_ptr(sw_up, "sw_up"));
+    SVDQ_TRY(lr_ptrs(L1_up, "L1_up", L2_up, "L2_up", r_up));
+    SVDQ_TRY(need_ptr(lambda_down, "lambda_down"));
+    SVDQ_TRY(need_ptr(qw_down, "qw_down"));
+    SVDQ_TRY(need_ptr(sw_down, "sw_down"));
+    SVDQ_TRY(lr_ptrs(L1_down, "L1_down", L2_down, "L2_down", r_down));
+    SVDQ_TRY(need_ptr(Y, "Y"));
+    if (bias_up && !aligned16(bias_up))
+        return fail(SVDQ_ERR_MISALIGNED, "bias_up is not 16-byte aligned");
+    if (bias_down && !aligned16(bias_down))
+        return fail(SVDQ_ERR_MISALIGNED, "bias_down is not 16-byte aligned");
+    const size_t need = carve_mlp(nullptr, M, K, N_hidden, r_up, r_down).bytes;
+    if (ws_bytes < need)
+        return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed", ws_bytes,
+                    need);
+    SVDQ_TRY(need_ptr(workspace, "workspace"));
+    SVDQ_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    const MlpWorkspace w = carve_mlp(workspace, M, K, N_hidden, r_up, r_down);
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.up.down, M, K, r_up);
+    SVDQ_TRY(hip_status(svdq::launch_quant_down(X, lambda_up, L1_up, M, K, r_up, dw, w.up.qa,
+                                                w.up.sa, w.up.xl1, s),
+                        "quantize_act_down launch"));
+    svdq::MlpArgs ma{lambda_down, L1_down, r_down, w.qa_h, w.sa_h, w.part};
+    SVDQ_TRY(hip_status(svdq::launch_w4a4_gemm_mlp(w.up.qa, w.up.sa, qw_up, sw_up, w.up.xl1, L2_up,
+                                                   bias_up, act, M, N_hidden, K, r_up, ma, s),
+                        "w4a4_lr_gemm_mlp launch"));
+    if (r_down > 0)
+        SVDQ_TRY(hip_status(svdq::launch_xl1_reduce(w.part, (int)(N_hidden / 128),
+                                                    M * (int64_t)r_down, w.xl1_h, s),
+                            "xl1 reduce launch"));
+    return hip_status(svdq::launch_w4a4_gemm(w.qa_h, w.sa_h, qw_down, sw_down, w.xl1_h, L2_down,
+                                             bias_down, SVDQ_ACT_NONE, M, K, N_hidden, r_down, Y,
+                                             s),
+                      "w4a4_lr_gemm launch");
 }
 
 int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,

@@ -68,6 +68,23 @@ hipError_t launch_w4a4_gemm_qkv(const uint8_t *qa, const float *sa, const uint8_
                                 const uint16_t *bias, int64_t M, int64_t K, int r,
                                 const QkvArgs &qk, hipStream_t stream);
 
+// MLP chain: the next SVDQuant layer's activation step (smoothing, INT4
+// codes and scales, partial down-projections) from this GEMM's output tiles.
+struct MlpArgs {
+    const float *lam;       // fp32 [N]: the next layer's smoothing factors
+    const uint16_t *L1;     // bf16 [N, rn]: its down-projection (NULL when rn == 0)
+    int rn;                 // 0, 16 or 32
+    uint8_t *qa;            // [M, N/2] codes (out)
+    float *sa;              // [M, N/64] scales (out)
+    float *part;            // [N/128, M, rn] partial down-projections (out, rn > 0)
+};
+hipError_t launch_w4a4_gemm_mlp(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                                const float *sw, const float *xl1, const uint16_t *L2,
+                                const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
+                                int r, const MlpArgs &ma, hipStream_t stream);
+hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl1,
+                             hipStream_t stream);
+
 // 0 auto, 1 full tiles only, 2 quarter tiles only (process-wide test hook)
 void set_tile_policy(int policy);
 

@@ -19,7 +19,7 @@ w4a4_lr_gemm_qkv_kernel(const uint8_t *__restrict__ qa, const float *__restrict_
     int64_t b = blockIdx.x, tm, tn;
     if ((nfull & 7) == 0) b = (b & 7) * (nfull >> 3) + (b >> 3);
     raster(b, nbm, nbn, tm, tn);
-    tile_body<2, true>(qa, sa, qw, sw, xl1, L2, bias, 0, M, N, K, r, nullptr, sm, tm * TILE,
+    tile_body<2, EPI_QKV>(qa, sa, qw, sw, xl1, L2, bias, 0, M, N, K, r, nullptr, sm, tm * TILE,
                        tn * TILE, &qk);
 }
 

@@ -501,16 +501,175 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
     }
 }
 
-// One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0);
-// QKV: the fused QKV epilogue instead of the plain store (WB = 2 only).
-template <int WB, bool QKV = false>
+// MLP chain epilogue of a 128 x 128 tile (the "Bringing Nunchaku 4-bit
+// inference to Diffusers" blog credits fused GELU/MLP paths for native speed;
+// the model card's Nunchaku engine design fuses a layer's down-projection
+// with its quantizer because both read the same input).  The tile is the
+// MLP-up output; instead of storing it, the epilogue runs the next layer's
+// activation step on it, so the [M, N] intermediate never reaches memory:
+//   h  = bf16(act(acc + bias))              (the value the plain GEMM stores)
+//   x^ = fl32(h fl32(1 / lambda[n]))        (smoothing of the next layer)
+//   per token and group of 64 columns -- exactly one wave's columns, the
+//   lane's 32 values and those of its v_permlane32_swap partner --
+//   s = max|x^| / 7, code = rint(clamp(x^ fl32(1/s), -7, 7)): the same
+//   quantizer as K1, stored as the next layer's codes and scales;
+//   the tile's share of x^ L1 over its 128 columns: x^ as a bf16 hi/lo pair
+//   on v_mfma_f32_32x32x16_bf16 (rows: the lane's tokens, which is the
+//   operand layout the tile already has) against L1^T staged in LDS; the two
+//   column-half waves add their partials in LDS in a fixed order and the sum
+//   goes to the partial buffer [N/128][M][rn], reduced in column order later.
+template <int WB>
+__device__ __forceinline__ void
+mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma, int act,
+             Smem<WB> &sm, int64_t M, int64_t N, int64_t m0, int64_t n0, int wn, int wm,
+             int r32, int ks2, int tid) {
+    static_assert(WB == 2, "the MLP epilogue works on 128 x 128 tiles");
+    constexpr int NB = WB * WB;
+    const int64_t nw = n0 + 64 * wn;   // the wave's group of 64 columns
+    // bias, activation, bf16 rounding, smoothing (x^ kept in acc)
+#pragma unroll
+    for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 lam4 = *reinterpret_cast<const f32x4 *>(ma.lam + nw + 32 * bi + 8 * q + 4 * ks2);
+            const u32x2 b2 = bb[bi][q];
+            const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float inv = 1.0f / lam4[j];
+#pragma unroll
+                for (int bj = 0; bj < WB; ++bj) {
+                    float x = acc[bi * WB + bj][4 * q + j] + bv[j];
+                    if (act == 1) x = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+                    const float h = bf16_lo(pack_bf16x2(x, 0.0f));
+                    acc[bi * WB + bj][4 * q + j] = h * inv;
+                }
+            }
+        }
+    }
+    // quantize each token's group; store codes and scales
+    const int64_t kb = N / 2, G = N / kGroup;
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) {
+        const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
+        float amax = 0.0f;
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[bi * WB + bj][i]));
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax),
+                                                        false, false);
+        amax = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        const float s = amax / 7.0f;
+        float inv = 0.0f;
+        if (s != 0.0f) {
+            const float t = 1.0f / s;
+            inv = __builtin_isfinite(t) ? t : 0.0f;
+        }
+        if (m < M) {
+#pragma unroll
+            for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float y = __builtin_amdgcn_fmed3f(acc[bi * WB + bj][4 * q + j] * inv, -7.0f, 7.0f);
+                        w |= (__float_as_uint(y + 12582912.0f) & 15u) << (4 * j);
+                    }
+                    *reinterpret_cast<uint16_t *>(ma.qa + m * kb + (nw + 32 * bi + 8 * q + 4 * ks2) / 2) =
+                        (uint16_t)w;
+                }
+            }
+            if (ks2 == 0) ma.sa[m * G + nw / kGroup] = s;
+        }
+    }
+    if (ma.rn == 0) return;
+    // the tile's partial down-projection
+    constexpr int LS = 128 + 4;                     // bf16 per staged L1^T row
+    uint16_t *l1t = reinterpret_cast<uint16_t *>(&sm.u);                       // [32][LS]
+    float *pl = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&sm.u) + 16384);  // [8][32][33]
+    __syncthreads();   // every wave is past the rank-r staging of this tile
+    {
+        const int n = tid & 127, c = tid >> 7;      // column, 16-rank half
+        uint32_t v[8];
+        if (16 * c < ma.rn) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(ma.L1 + (n0 + n) * (int64_t)ma.rn + 16 * c);
+            const u32x4 a = src[0], b = src[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            l1t[(16 * c + 2 * e) * LS + n] = (uint16_t)(v[e] & 0xFFFFu);
+            l1t[(16 * c + 2 * e + 1) * LS + n] = (uint16_t)(v[e] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj) {
+        f32x16 P = f32x16{};
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                // columns 16c + 4 ks2 + 0..3 and 16c + 8 + 4 ks2 + 0..3 of block bi
+                float xs[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xs[e] = acc[bi * WB + bj][8 * c + e];
+                u32x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t h = pack_bf16x2(xs[2 * e], xs[2 * e + 1]);
+                    hi[e] = h;
+                    lo[e] = pack_bf16x2(xs[2 * e] - bf16_lo(h), xs[2 * e + 1] - bf16_hi(h));
+                }
+                const int nl = 64 * wn + 32 * bi + 16 * c + 4 * ks2;
+                const u32x2 b0 = *reinterpret_cast<const u32x2 *>(&l1t[r32 * LS + nl]);
+                const u32x2 b1 = *reinterpret_cast<const u32x2 *>(&l1t[r32 * LS + nl + 8]);
+                const u32x4 B = u32x4{b0.x, b0.y, b1.x, b1.y};
+                P = mfma_bf16_32x32x16(hi, B, P);
+                P = mfma_bf16_32x32x16(lo, B, P);
+            }
+        }
+        float *dst = pl + ((wn * 2 + wm) * 2 + bj) * (32 * 33);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dst[(8 * (j / 4) + 4 * ks2 + (j % 4)) * 33 + r32] = P[j];
+    }
+    __syncthreads();
+    {
+        const int tl = tid >> 1, half = tid & 1;      // token of the tile, 16-rank half
+        const int wmi = tl >> 6, bji = (tl >> 5) & 1, row = tl & 31;
+        const int64_t m = m0 + tl;
+        if (m < M && 16 * half < ma.rn) {
+            const float *a = pl + ((0 * 2 + wmi) * 2 + bji) * (32 * 33) + row * 33 + 16 * half;
+            const float *b = pl + ((1 * 2 + wmi) * 2 + bji) * (32 * 33) + row * 33 + 16 * half;
+            f32x4 *out = reinterpret_cast<f32x4 *>(ma.part + ((n0 / 128) * M + m) * ma.rn + 16 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = f32x4{a[4 * e] + b[4 * e], a[4 * e + 1] + b[4 * e + 1],
+                               a[4 * e + 2] + b[4 * e + 2], a[4 * e + 3] + b[4 * e + 3]};
+        }
+    }
+}
+
+// Output epilogues of a tile.
+enum { EPI_STORE = 0, EPI_QKV = 1, EPI_MLP = 2 };
+
+// One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0).
+// EPI_STORE: bias, activation, the [M, N] bf16 store; EPI_QKV: the fused QKV
+// epilogue (epi -> QkvArgs); EPI_MLP: the next layer's activation step
+// (epi -> MlpArgs).  The last two need WB = 2.
+template <int WB, int EPI = EPI_STORE>
 __device__ __forceinline__ void
 tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
           const uint8_t *__restrict__ qw, const float *__restrict__ sw,
           const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
           const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N, int64_t K, int r,
           uint16_t *__restrict__ Y, Smem<WB> &sm, int64_t m0, int64_t n0,
-          const QkvArgs *qk = nullptr) {
+          const void *epi = nullptr) {
     using C = Cfg<WB>;
     constexpr int BT = C::BT, NB = C::NB;
     const int tid = threadIdx.x;
@@ -677,8 +836,14 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
         }
     }
 
-    if constexpr (QKV) {
-        qkv_epilogue<WB>(acc, bb, *qk, sm, M, m0, n0, wn, wm, r32, ks2);
+    if constexpr (EPI == EPI_QKV) {
+        qkv_epilogue<WB>(acc, bb, *static_cast<const QkvArgs *>(epi), sm, M, m0, n0, wn, wm, r32,
+                         ks2);
+        return;
+    }
+    if constexpr (EPI == EPI_MLP) {
+        mlp_epilogue<WB>(acc, bb, *static_cast<const MlpArgs *>(epi), act, sm, M, N, m0, n0, wn,
+                         wm, r32, ks2, tid);
         return;
     }
     // Block (bi, bj); element i of the lane is n = base + 8 (i / 4) +

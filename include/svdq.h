@@ -215,6 +215,61 @@ int32_t svdq_linear_qkv(const uint16_t *X, const float *lambda, const uint16_t *
                         const svdq_qkv_epilogue *epi, void *workspace, size_t ws_bytes,
                         void *stream);
 
+/* ------------------------------------------------------------------
+ * MLP chain.  The blog "Bringing Nunchaku 4-bit inference to Diffusers"
+ * (section "Background: SVDQuant and Nunchaku") credits fused GELU/MLP paths
+ * for Nunchaku's native speed, and the model card's "Nunchaku engine design"
+ * fuses a layer's down-projection with its quantizer because both read the
+ * same input.  Here the MLP-up GEMM runs the MLP-down layer's activation step
+ * (svdq_quantize_act_down's smoothing, INT4 codes, scales and X L1) on its
+ * own output tiles, so the [M, N] intermediate is never written: the codes,
+ * scales and xl1 are bit-identical to (xl1: within the bound of)
+ * svdq_quantize_act_down applied to what svdq_w4a4_lr_gemm would have stored.
+ * ------------------------------------------------------------------ */
+
+/* Workspace (partial down-projections) of svdq_w4a4_lr_gemm_quant_down. */
+size_t svdq_w4a4_lr_gemm_quant_down_workspace_bytes(int64_t M, int64_t N, int32_t r_next);
+
+/*
+ * The GEMM of svdq_w4a4_lr_gemm (arguments as there, Y omitted) followed by
+ * the next layer's activation step on Y:
+ *   lambda_next  device fp32 [N]          the next layer's smoothing factors
+ *   L1_next      device bf16 [N, r_next]  its down-projection (NULL if r_next == 0)
+ *   qa_next      device u8   [M, N/2]     its codes (out)
+ *   sa_next      device fp32 [M, N/64]    its scales (out)
+ *   xl1_next     device fp32 [M, r_next]  its down-projection (out; NULL if r_next == 0)
+ *   workspace    device, svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, r_next)
+ * Needs N % 128 == 0 and r_next in {0, 16, 32}; otherwise as svdq_w4a4_lr_gemm.
+ */
+int32_t svdq_w4a4_lr_gemm_quant_down(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                                     const float *sw, const float *xl1, const uint16_t *L2,
+                                     const uint16_t *bias, int32_t act, int64_t M, int64_t N,
+                                     int64_t K, int32_t r, const float *lambda_next,
+                                     const uint16_t *L1_next, int32_t r_next, uint8_t *qa_next,
+                                     float *sa_next, float *xl1_next, void *workspace,
+                                     size_t ws_bytes, void *stream);
+
+/* Workspace of svdq_mlp. */
+size_t svdq_mlp_workspace_bytes(int64_t M, int64_t K, int64_t N_hidden, int32_t r_up,
+                                int32_t r_down);
+
+/*
+ * A whole MLP of two SVDQuant layers: Y = down(act(up(X))), up: K -> N_hidden
+ * (activation act, bias_up), down: N_hidden -> K (no activation, bias_down).
+ * Three launches on one stream (plus the reduce launches of the
+ * down-projections): K1 of the up layer, the up GEMM with the down layer's
+ * activation step in its epilogue, the down GEMM.  Arguments per layer as in
+ * svdq_linear; Y device bf16 [M, K] (out).  Needs N_hidden % 128 == 0 and
+ * r_down in {0, 16, 32}.
+ */
+int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_up,
+                 const uint8_t *qw_up, const float *sw_up, const uint16_t *L2_up,
+                 const uint16_t *bias_up, const float *lambda_down, const uint16_t *L1_down,
+                 const uint8_t *qw_down, const float *sw_down, const uint16_t *L2_down,
+                 const uint16_t *bias_down, int32_t act, int64_t M, int64_t K, int64_t N_hidden,
+                 int32_t r_up, int32_t r_down, uint16_t *Y, void *workspace, size_t ws_bytes,
+                 void *stream);
+
 /*
  * Test hook: the exact per-group integer sums of a block, computed with the
  * same operand unpacking and int8 matrix instructions as the GEMM.

@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     decl = declared_functions()
-    assert len(decl) == 17, decl
+    assert len(decl) == 21, decl
     assert sorted(_binding.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -246,3 +246,56 @@ def test_qkv_struct_layout_matches_header(tmp_path):
     want = [ctypes.sizeof(_binding.QkvEpilogue)] + [getattr(_binding.QkvEpilogue, f).offset
                                                     for f, _ in _binding.QkvEpilogue._fields_]
     assert got == want
+
+
+def _gqd(lib, M=8, N=256, K=128, r=16, rn=32, ws_bytes=1 << 30, act=1, **kw):
+    a = dict(qa=A, sa=A, qw=A, sw=A, xl1=A, L2=A, bias=A, lam=A, L1n=A, qan=A, san=A, xl1n=A, ws=A)
+    a.update(kw)
+    return lib.svdq_w4a4_lr_gemm_quant_down(
+        P(a["qa"]), P(a["sa"]), P(a["qw"]), P(a["sw"]), P(a["xl1"]), P(a["L2"]), P(a["bias"]), act,
+        M, N, K, r, P(a["lam"]), P(a["L1n"]), rn, P(a["qan"]), P(a["san"]), P(a["xl1n"]),
+        P(a["ws"]), ws_bytes, None)
+
+
+def _mlp(lib, M=8, K=128, Nh=256, ru=16, rd=32, ws_bytes=1 << 30, act=1, **kw):
+    a = dict(X=A, lu=A, L1u=A, qwu=A, swu=A, L2u=A, bu=A, ld=A, L1d=A, qwd=A, swd=A, L2d=A, bd=A,
+             Y=A, ws=A)
+    a.update(kw)
+    return lib.svdq_mlp(P(a["X"]), P(a["lu"]), P(a["L1u"]), P(a["qwu"]), P(a["swu"]), P(a["L2u"]),
+                        P(a["bu"]), P(a["ld"]), P(a["L1d"]), P(a["qwd"]), P(a["swd"]), P(a["L2d"]),
+                        P(a["bd"]), act, M, K, Nh, ru, rd, P(a["Y"]), P(a["ws"]), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=192), SHAPE), (dict(rn=48), SHAPE), (dict(rn=8), SHAPE), (dict(act=7), INVALID),
+    (dict(K=100), SHAPE), (dict(lam=0), INVALID), (dict(san=0), INVALID), (dict(qan=U), MISALIGNED),
+    (dict(L1n=0), INVALID), (dict(rn=0), INVALID), (dict(xl1n=U), MISALIGNED),
+    (dict(ws_bytes=16), WS_SMALL), (dict(ws=0), INVALID), (dict(qa=0), INVALID),
+])
+def test_gemm_quant_down_rejects(lib, kw, code):
+    assert _gqd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Nh=192), SHAPE), (dict(rd=48), SHAPE), (dict(ru=17), SHAPE), (dict(K=100), SHAPE),
+    (dict(K=64 * 3 + 4), SHAPE), (dict(act=3), INVALID), (dict(X=0), INVALID),
+    (dict(ld=0), INVALID), (dict(L1d=0), INVALID), (dict(L2u=0), INVALID), (dict(Y=U), MISALIGNED),
+    (dict(bd=U), MISALIGNED), (dict(ws_bytes=16), WS_SMALL), (dict(ws=0), INVALID),
+])
+def test_mlp_rejects(lib, kw, code):
+    assert _mlp(lib, **kw) == code
+
+
+def test_mlp_empty_and_workspace_sizes(lib):
+    assert _gqd(lib, M=0, qa=0, sa=0, qw=0, sw=0, xl1=0, L2=0, bias=0, lam=0, L1n=0, qan=0, san=0,
+                xl1n=0, ws=0, ws_bytes=0) == OK
+    assert _mlp(lib, M=0, X=0, lu=0, L1u=0, qwu=0, swu=0, L2u=0, bu=0, ld=0, L1d=0, qwd=0, swd=0,
+                L2d=0, bd=0, Y=0, ws=0, ws_bytes=0) == OK
+    # partial down-projections: [N/128][M][r_next] fp32, 256-byte aligned
+    assert lib.svdq_w4a4_lr_gemm_quant_down_workspace_bytes(4608, 12288, 32) == 96 * 4608 * 32 * 4
+    assert lib.svdq_w4a4_lr_gemm_quant_down_workspace_bytes(5, 256, 16) == 768
+    assert lib.svdq_w4a4_lr_gemm_quant_down_workspace_bytes(5, 256, 0) == 0
+    lin = lib.svdq_linear_workspace_bytes(100, 128, 16)
+    mlp = lib.svdq_mlp_workspace_bytes(100, 128, 256, 16, 32)
+    # up-layer workspace + hidden codes, scales, xl1 and partials
+    assert mlp == lin + 12800 + 1792 + 12800 + 25600
