@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="qkv",
                     choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single",
-                             "qkv_fused"])
+                             "qkv_fused", "mlp_chain"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-overhead", action="store_true",
@@ -312,17 +312,153 @@ def bench_qkv_fused(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_mlp_chain(args):
+    """One DiT block's MLP (3072 -> 12288 GELU -> 3072, rank 32, 4608 tokens): one step =
+    one svdq_mlp call (the up GEMM runs the down layer's activation step in its epilogue).
+    Metric 2 M (K Nh + Nh K) / t; the unfused chain (svdq_linear twice, through the bf16
+    intermediate) is timed beside it on the same inputs."""
+    import torch
+
+    import bit_diffusion_transformer_amd as bdt
+    from synth import DIT_CHAIN, make_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    up_s, dn_s = DIT_CHAIN[2], DIT_CHAIN[3]
+    M = up_s.M if args.M is None else args.M
+    up, dn = make_layer(up_s, seed=0, M=M), make_layer(dn_s, seed=0, M=M)
+    K, Nh, ru, rd = up_s.K, up_s.N, up_s.r, dn_s.r
+
+    def d(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def layer(L):
+        qw, sw = bdt.pack_weights(d(L.R))
+        return dict(lam=d(L.lam), L1=d(L.L1), L2=d(L.L2), bias=d(L.bias), qw=qw, sw=sw)
+
+    U0, D0 = layer(up), layer(dn)
+    ws_mlp = bdt.svdq_mlp_workspace_bytes(M, K, Nh, ru, rd)
+    ws_up = bdt.svdq_linear_workspace_bytes(M, K, ru)
+    ws_dn = bdt.svdq_linear_workspace_bytes(M, Nh, rd)
+    wbytes = sum(v.numel() * v.element_size() for L in (U0, D0) for v in L.values()
+                 if v is not None)
+    set_bytes = wbytes + 2 * M * K * 2 + 2 * M * Nh + max(ws_mlp, ws_up + ws_dn)
+    nsets = max(2, int(np.ceil(2 * CACHE_BYTES / set_bytes)))
+    bits = bdt._bits
+    sets = []
+    for _ in range(nsets):
+        st = dict(U={k: (v.clone() if v is not None else None) for k, v in U0.items()},
+                  D={k: (v.clone() if v is not None else None) for k, v in D0.items()},
+                  X=d(up.X).clone(), Y=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                  H=torch.empty((M, Nh), dtype=torch.bfloat16, device=dev),
+                  ws=torch.empty(max(ws_mlp, ws_up, ws_dn), dtype=torch.uint8, device=dev))
+        sets.append(st)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def fused(i):
+        st = sets[i % nsets]
+        U, D = st["U"], st["D"]
+        bdt.svdq_mlp(bits(st["X"]), U["lam"], bits(U["L1"]), U["qw"], U["sw"], bits(U["L2"]),
+                     bits(U["bias"]), D["lam"], bits(D["L1"]), D["qw"], D["sw"], bits(D["L2"]),
+                     bits(D["bias"]), 1, M, K, Nh, ru, rd, bits(st["Y"]), st["ws"], ws_mlp,
+                     stream)
+
+    def unfused(i):
+        st = sets[i % nsets]
+        U, D = st["U"], st["D"]
+        bdt.svdq_linear(bits(st["X"]), U["lam"], bits(U["L1"]), U["qw"], U["sw"], bits(U["L2"]),
+                        bits(U["bias"]), 1, M, Nh, K, ru, bits(st["H"]), st["ws"], ws_up, stream)
+        bdt.svdq_linear(bits(st["H"]), D["lam"], bits(D["L1"]), D["qw"], D["sw"], bits(D["L2"]),
+                        bits(D["bias"]), 0, M, K, Nh, rd, bits(st["Y"]), st["ws"], ws_dn, stream)
+
+    for i in range(args.warmup):
+        fused(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    ops = 2.0 * M * K * Nh * 2
+
+    def time_loop(fn, n):
+        for i in range(20):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    n_k = max(args.steps, 20)
+    # the fused up GEMM alone (its inputs from one K1 per set)
+    carved = [bdt.quantize_act_down(st["X"], st["U"]["lam"], st["U"]["L1"]) for st in sets]
+    outs = [(torch.empty((M, Nh // 2), dtype=torch.uint8, device=dev),
+             torch.empty((M, Nh // 64), dtype=torch.float32, device=dev),
+             torch.empty((M, rd), dtype=torch.float32, device=dev)) for _ in sets]
+    ws_g = bdt.svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, Nh, rd)
+    torch.cuda.synchronize()
+
+    def up_fused(i):
+        st, (qa, sa, xl1), (qn, sn, xn) = sets[i % nsets], carved[i % nsets], outs[i % nsets]
+        U, D = st["U"], st["D"]
+        bdt.svdq_w4a4_lr_gemm_quant_down(qa, sa, U["qw"], U["sw"], xl1, bits(U["L2"]),
+                                         bits(U["bias"]), 1, M, Nh, K, ru, D["lam"],
+                                         bits(D["L1"]), rd, qn, sn, xn, st["ws"], ws_g, stream)
+
+    def up_plain(i):
+        st, (qa, sa, xl1) = sets[i % nsets], carved[i % nsets]
+        U = st["U"]
+        bdt.svdq_w4a4_lr_gemm(qa, sa, U["qw"], U["sw"], xl1, bits(U["L2"]), bits(U["bias"]), 1,
+                              M, Nh, K, ru, bits(st["H"]), stream)
+
+    t_f = time_loop(fused, n_k)
+    t_u = time_loop(unfused, n_k)
+    t_gf = time_loop(up_fused, n_k)
+    t_gp = time_loop(up_plain, n_k)
+    ops_up = 2.0 * M * Nh * K
+    out = {
+        "metric": METRIC, "value": round(ops / t_step / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
+        "config": {"workload": "mlp_chain: M=%d %d -> %d (GELU) -> %d, r=%d/%d group=64"
+                               % (M, K, Nh, K, ru, rd),
+                   "global_batch": M, "input_sets_rotated": nsets},
+        "roofline": {"bound": "mfma", "achieved": round(ops_up / t_gf / 1e12, 2),
+                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(ops_up / t_gf / 1e12 / PEAK_INT8_TOPS, 4), "traffic": None,
+                     "kernel": "w4a4_lr_gemm_mlp_kernel + xl1 reduce (one "
+                               "svdq_w4a4_lr_gemm_quant_down call)",
+                     "avg_launch_us": round(t_gf * 1e6, 2), "algorithmic_ops": ops_up},
+        "fused_vs_unfused": {"mlp_fused_us": round(t_f * 1e6, 2),
+                             "mlp_unfused_us": round(t_u * 1e6, 2),
+                             "speedup": round(t_u / t_f, 4),
+                             "up_gemm_fused_us": round(t_gf * 1e6, 2),
+                             "up_gemm_plain_us": round(t_gp * 1e6, 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.workload.startswith("awq") or args.workload == "qkv_fused":
+    extra = {"qkv_fused": bench_qkv_fused, "mlp_chain": bench_mlp_chain}
+    if args.workload.startswith("awq") or args.workload in extra:
         if args.gpus != 1:
             print("bench.py runs on one GPU only (--gpus %d requested)" % args.gpus,
                   file=sys.stderr)
             sys.exit(2)
-        (bench_awq if args.workload.startswith("awq") else bench_qkv_fused)(args)
+        (bench_awq if args.workload.startswith("awq") else extra[args.workload])(args)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the layer has no multi-GPU path in this build "

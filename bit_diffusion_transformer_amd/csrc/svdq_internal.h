@@ -87,6 +87,8 @@ hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl
 
 // 0 auto, 1 full tiles only, 2 quarter tiles only (process-wide test hook)
 void set_tile_policy(int policy);
+int tile_policy();
+int64_t wg_slots();   // 128 x 128 workgroup slots of the current device
 
 hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw,
                             const float *sw, const float *xl1, const uint16_t *L2,

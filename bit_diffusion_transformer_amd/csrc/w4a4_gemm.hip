@@ -79,10 +79,11 @@ group_sums_kernel(const uint8_t *__restrict__ qa, const uint8_t *__restrict__ qw
 static std::atomic<int> g_tile_policy{0};
 
 void set_tile_policy(int policy) { g_tile_policy.store(policy, std::memory_order_relaxed); }
+int tile_policy() { return g_tile_policy.load(std::memory_order_relaxed); }
 
 // Workgroup slots of the device (two 128 x 128 workgroups per compute
 // unit), cached per device.
-static int64_t wg_slots() {
+int64_t wg_slots() {
     static int64_t slots[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
@@ -105,7 +106,7 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
                             const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
                             int r, uint16_t *Y, hipStream_t stream) {
     const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
-    const int policy = g_tile_policy.load(std::memory_order_relaxed);
+    const int policy = tile_policy();
     int64_t rest = 0;
     if (policy == 2) {
         rest = tiles;

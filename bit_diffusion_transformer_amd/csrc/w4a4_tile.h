@@ -426,6 +426,9 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
         }
         return;
     }
+    if constexpr (WB == 1) {
+        return;   // quarter tiles are only ever V tiles (a head needs the full tile width)
+    } else {
     // sum of squares of each token over this wave's columns (and the partner
     // lane l ^ 32, which holds the other half of every 8-column group)
     float ss[WB];
@@ -499,6 +502,7 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
             }
         }
     }
+    }
 }
 
 // MLP chain epilogue of a 128 x 128 tile (the "Bringing Nunchaku 4-bit
@@ -524,19 +528,25 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
              Smem<WB> &sm, int64_t M, int64_t N, int64_t m0, int64_t n0, int wn, int wm,
              int r32, int ks2, int tid) {
     static_assert(WB == 2, "the MLP epilogue works on 128 x 128 tiles");
+    static_assert(sizeof(Smem<2>) >= 69632 + 512, "room for 1/lambda past the staging");
     constexpr int NB = WB * WB;
     const int64_t nw = n0 + 64 * wn;   // the wave's group of 64 columns
+    // fl32(1 / lambda) of the tile's 128 columns, once each, in LDS beyond
+    // every region the rank-r staging and the steps below use
+    float *linv = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&sm.u) + 69632);
+    if (tid < 128) linv[tid] = 1.0f / ma.lam[n0 + tid];
+    __syncthreads();
     // bias, activation, bf16 rounding, smoothing (x^ kept in acc)
 #pragma unroll
     for (int bi = 0; bi < WB; ++bi) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const f32x4 lam4 = *reinterpret_cast<const f32x4 *>(ma.lam + nw + 32 * bi + 8 * q + 4 * ks2);
+            const f32x4 inv4 = *reinterpret_cast<const f32x4 *>(linv + 64 * wn + 32 * bi + 8 * q + 4 * ks2);
             const u32x2 b2 = bb[bi][q];
             const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float inv = 1.0f / lam4[j];
+                const float inv = inv4[j];
 #pragma unroll
                 for (int bj = 0; bj < WB; ++bj) {
                     float x = acc[bi * WB + bj][4 * q + j] + bv[j];

@@ -152,3 +152,23 @@ def test_qkv_full_size_sampled():
                               to_dev(L.bias), H, D, S, **_dev_epi(epi))
     worst = _check(Q, Kt, V, orc, epi, rows, "qkv full")
     print("  qkv full size worst |err|/bound = %.3f" % worst, flush=True)
+
+
+def test_tile_policies_agree_bit_exact(case):
+    """V tiles as 64 x 64 quarter tiles (the partial-last-round path) give the same bits."""
+    out = {}
+    for pol in (bdt.TILES_FULL, bdt.TILES_QUARTER):
+        bdt.svdq_debug_set_tile_policy(pol)
+        try:
+            out[pol] = [bf16_host(t) for t in _gemm_qkv(case)]
+        finally:
+            bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
+    for a, b in zip(out[bdt.TILES_FULL], out[bdt.TILES_QUARTER]):
+        assert np.array_equal(a, b)
+    M = case["B"] * case["S"]
+    bdt.svdq_debug_set_tile_policy(bdt.TILES_QUARTER)
+    try:
+        Q, Kt, V = _gemm_qkv(case)
+    finally:
+        bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
+    _check(Q, Kt, V, case["orc"], case["epi"], np.arange(M), "gemm_qkv quarter V tiles")
