@@ -24,6 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "svdq_oracle.c")
 _SRC_AWQ = os.path.join(_HERE, "awq_oracle.c")
 _SRC_QKV = os.path.join(_HERE, "qkv_oracle.c")
+_SRC_MX = os.path.join(_HERE, "mxfp4_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -36,7 +37,8 @@ def build(force: bool = True) -> str:
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, _SRC_AWQ, _SRC_QKV, "-o", tmp, "-lm"]
+           "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, _SRC_AWQ, _SRC_QKV, _SRC_MX, "-o", tmp,
+           "-lm"]
     subprocess.check_call(cmd)
     os.replace(tmp, _LIB)
     return _LIB
@@ -66,12 +68,23 @@ def _load():
     lib.oracle_awq_quantize.argtypes = [P, I64, I64, P, P, P]
     lib.oracle_awq_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.oracle_awq_linear_rows.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, P, P]
+    lib.oracle_mx_e2m1_code.argtypes = [ctypes.c_double]
+    lib.oracle_mx_e2m1_code.restype = ctypes.c_int
+    lib.oracle_mx_e2m1_value.argtypes = [ctypes.c_int]
+    lib.oracle_mx_e2m1_value.restype = ctypes.c_double
+    lib.oracle_mx_scale_byte.argtypes = [ctypes.c_double]
+    lib.oracle_mx_scale_byte.restype = ctypes.c_int
+    lib.oracle_mx_quantize.argtypes = [P, I64, I64, P, P]
+    lib.oracle_mx_dequant.argtypes = [P, P, I64, I64, P]
+    lib.oracle_mx_gemm_rows.argtypes = [P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, I64,
+                                        P, P]
     lib.oracle_qkv_epilogue.argtypes = [P, P, I64, I64, I64, I64, P, P, ctypes.c_double, P, P,
                                         P, P, P, P, P, P, P]
     for f in ("oracle_smooth", "oracle_quantize_groups", "oracle_unpack",
               "oracle_down_proj", "oracle_group_sums", "oracle_gemm_rows",
               "oracle_awq_quantize", "oracle_awq_dequant", "oracle_awq_linear_rows",
-              "oracle_qkv_epilogue"):
+              "oracle_qkv_epilogue", "oracle_mx_quantize", "oracle_mx_dequant",
+              "oracle_mx_gemm_rows"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -301,3 +314,87 @@ def qkv_epilogue(acc: np.ndarray, H: int, D: int, S: int, gamma_q: np.ndarray,
                                     _ptr(out["k"]), _ptr(out["qb"]), _ptr(out["kb"]),
                                     _ptr(out["vb"]), _ptr(out["rho_q"]), _ptr(out["rho_k"]))
     return out
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+
+MX_BLOCK = 32
+
+
+def mx_e2m1_code(y: float) -> int:
+    return int(_load().oracle_mx_e2m1_code(float(y)))
+
+
+def mx_e2m1_value(code: int) -> float:
+    return float(_load().oracle_mx_e2m1_value(int(code)))
+
+
+def mx_scale_byte(amax: float) -> int:
+    return int(_load().oracle_mx_scale_byte(float(amax)))
+
+
+def mx_quantize(v: np.ndarray):
+    """fp32 [rows, K] -> (packed codes uint8 [rows, K/2], E8M0 scale bytes uint8 [rows, K/32]).
+    Readings in mxfp4_oracle.c."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, K = v.shape
+    assert K % MX_BLOCK == 0
+    packed = np.empty((rows, K // 2), np.uint8)
+    scales = np.empty((rows, K // MX_BLOCK), np.uint8)
+    if rows:
+        _load().oracle_mx_quantize(_ptr(v), rows, K, _ptr(packed), _ptr(scales))
+    return packed, scales
+
+
+def mx_dequant(packed: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = packed.shape[0]
+    out = np.empty((rows, K), np.float64)
+    if rows:
+        _load().oracle_mx_dequant(_ptr(packed), _ptr(scales), rows, K, _ptr(out))
+    return out
+
+
+def mx_quantize_act(X: np.ndarray, lam: np.ndarray):
+    """Smoothing (as the INT4 path) then MXFP4 -> (qa, sa bytes, xh fp32)."""
+    xh = smooth(X, lam)
+    qa, sa = mx_quantize(xh)
+    return qa, sa, xh
+
+
+def mx_gemm_rows(qa, sa, qw, sw, xl1: Optional[np.ndarray], L2: Optional[np.ndarray],
+                 bias: Optional[np.ndarray], act: int, K: int,
+                 rows: Optional[Sequence[int]] = None):
+    """MXFP4 layer output for the given rows -> (acc f64 [R, N], y bf16 bits [R, N])."""
+    qa = np.ascontiguousarray(qa, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    qw = np.ascontiguousarray(qw, dtype=np.uint8)
+    sw = np.ascontiguousarray(sw, dtype=np.uint8)
+    M, N = qa.shape[0], qw.shape[0]
+    r = 0 if xl1 is None else xl1.shape[1]
+    if r > 0:
+        xl1 = np.ascontiguousarray(xl1, dtype=np.float64)
+        L2 = np.ascontiguousarray(L2, dtype=np.uint16)
+    else:
+        xl1, L2 = None, None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.uint16)
+    rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    nrows = M if rows is None else len(rows_arr)
+    acc = np.empty((nrows, N), np.float64)
+    y = np.empty((nrows, N), np.uint16)
+    if nrows > 0:
+        _load().oracle_mx_gemm_rows(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(xl1), _ptr(L2),
+                                    _ptr(bias), int(act), M, N, K, r, _ptr(rows_arr), nrows,
+                                    _ptr(acc), _ptr(y))
+    return acc, y
+
+
+def mx_linear(X, lam, L1, qw, sw, L2, bias, act: int, rows=None):
+    """The whole MXFP4 layer from its call inputs."""
+    K = X.shape[1]
+    qa, sa, xh = mx_quantize_act(X, lam)
+    r = 0 if L1 is None else L1.shape[1]
+    xl1 = down_proj(xh, L1) if r > 0 else None
+    return mx_gemm_rows(qa, sa, qw, sw, xl1, L2, bias, act, K, rows)
