@@ -36,11 +36,14 @@ constexpr int K1_ROWS = 64;
 // Chunk size for a tile count: the staged L1 chunk is 64 KC x 16 NT bf16.
 template <int NT> struct K1Chunk { static constexpr int KC = NT <= 2 ? 8 : (NT <= 4 ? 4 : 2); };
 
-template <int NT>
+// MX: the 4-bit float (MXFP4) variant -- the same smoothing and
+// down-projection, the MX quantizer per 32-value block, E8M0 scale bytes
+// [M, K/32] in sa.
+template <int NT, bool MX = false>
 __global__ void __launch_bounds__(256)
 quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
                   const uint16_t *__restrict__ L1, int64_t M, int64_t K, int r, int nc,
-                  uint8_t *__restrict__ qa, float *__restrict__ sa, float *__restrict__ out,
+                  uint8_t *__restrict__ qa, void *__restrict__ sa, float *__restrict__ out,
                   int64_t out_chunk_stride) {
     constexpr int KC = K1Chunk<NT>::KC;
     constexpr int S = KC * kGroup + 8;                 // LDS row of the L1 chunk, bf16
@@ -139,10 +142,19 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
             v[12] = bf16_lo(x1.z) * i3.x; v[13] = bf16_hi(x1.z) * i3.y;
             v[14] = bf16_lo(x1.w) * i3.z; v[15] = bf16_hi(x1.w) * i3.w;
             u32x2 packed;
-            const float s = quantize_group16(v, packed);
-            if (row_ok) {
-                *reinterpret_cast<u32x2 *>(qa + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
-                if (ks == 0) sa[row * G + g] = s;
+            if constexpr (MX) {
+                const uint32_t sb = mx_quantize16(v, packed);
+                if (row_ok) {
+                    *reinterpret_cast<u32x2 *>(qa + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
+                    if ((ks & 1) == 0)
+                        static_cast<uint8_t *>(sa)[row * 2 * G + 2 * g + (ks >> 1)] = (uint8_t)sb;
+                }
+            } else {
+                const float s = quantize_group16(v, packed);
+                if (row_ok) {
+                    *reinterpret_cast<u32x2 *>(qa + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
+                    if (ks == 0) static_cast<float *>(sa)[row * G + g] = s;
+                }
             }
             if (NT > 0) {
                 u32x4 h[2], l[2];
@@ -199,9 +211,10 @@ xl1_reduce_kernel(const float *__restrict__ part, int nc, int64_t total, float *
 // ------------------------------------------------------------------ pack
 // Offline quantization of the fp32 residual R [N, K]: one wave per 16 rows,
 // the same lane layout and group quantizer as K1 (no smoothing).
+template <bool MX = false>
 __global__ void __launch_bounds__(256)
 pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
-                    uint8_t *__restrict__ qw, float *__restrict__ sw) {
+                    uint8_t *__restrict__ qw, void *__restrict__ sw) {
     const int lane = threadIdx.x & 63;
     const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int rl = lane & 15;
@@ -220,10 +233,19 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
             v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
         }
         u32x2 packed;
-        const float s = quantize_group16(v, packed);
-        if (row_ok) {
-            *reinterpret_cast<u32x2 *>(qw + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
-            if (ks == 0) sw[row * G + g] = s;
+        if constexpr (MX) {
+            const uint32_t sb = mx_quantize16(v, packed);
+            if (row_ok) {
+                *reinterpret_cast<u32x2 *>(qw + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
+                if ((ks & 1) == 0)
+                    static_cast<uint8_t *>(sw)[row * 2 * G + 2 * g + (ks >> 1)] = (uint8_t)sb;
+            }
+        } else {
+            const float s = quantize_group16(v, packed);
+            if (row_ok) {
+                *reinterpret_cast<u32x2 *>(qw + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
+                if (ks == 0) static_cast<float *>(sw)[row * G + g] = s;
+            }
         }
     }
 }
@@ -232,7 +254,7 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
 
 hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
                              int64_t M, int64_t K, int r, const DownWorkspace &ws, uint8_t *qa,
-                             float *sa, float *xl1, hipStream_t stream) {
+                             void *sa, float *xl1, hipStream_t stream, bool mx) {
     const int nc = k1_chunks(K, r);
     const int64_t rbs = (M + K1_ROWS - 1) / K1_ROWS;
     const unsigned blocks = (unsigned)(rbs * nc);
@@ -240,8 +262,14 @@ hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint1
     float *out = partial ? ws.part : xl1;
     const int64_t stride = partial ? M * (int64_t)r : 0;
 #define SVDQ_K1(NTV)                                                                       \
-    quant_down_kernel<NTV><<<blocks, 256, 0, stream>>>(X, lambda, L1, M, K, r, nc, qa, sa,  \
-                                                      out, stride)
+    do {                                                                                   \
+        if (mx)                                                                            \
+            quant_down_kernel<NTV, true><<<blocks, 256, 0, stream>>>(X, lambda, L1, M, K, r, \
+                                                                    nc, qa, sa, out, stride); \
+        else                                                                               \
+            quant_down_kernel<NTV><<<blocks, 256, 0, stream>>>(X, lambda, L1, M, K, r, nc,  \
+                                                              qa, sa, out, stride);        \
+    } while (0)
     if (r == 0) SVDQ_K1(0);
     else if (r <= 32) SVDQ_K1(2);
     else if (r <= 64) SVDQ_K1(4);
@@ -262,11 +290,12 @@ hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl
     return hipGetLastError();
 }
 
-hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
-                               hipStream_t stream) {
+hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, void *sw,
+                               hipStream_t stream, bool mx) {
     const int64_t waves = (N + 15) / 16;
     const unsigned blocks = (unsigned)((waves + 3) / 4);
-    pack_weights_kernel<<<blocks, 256, 0, stream>>>(R, N, K, qw, sw);
+    if (mx) pack_weights_kernel<true><<<blocks, 256, 0, stream>>>(R, N, K, qw, sw);
+    else pack_weights_kernel<<<blocks, 256, 0, stream>>>(R, N, K, qw, sw);
     return hipGetLastError();
 }
 

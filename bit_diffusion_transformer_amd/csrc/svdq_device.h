@@ -145,4 +145,43 @@ __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &p
     return s;
 }
 
+// ---------------------------------------------------------------- MXFP4 quantizer
+
+// Quantize the lane's 16 values of a 32-value block shared with lane l ^ 16
+// (OCP MX v1.0, MXFP4): the block's scale X = 2^e with
+// e = clamp(floor(log2 max|v|) - 2, -127, 127) (v_frexp_exp gives
+// floor(log2) + 1 for normal and subnormal values), stored as the E8M0 byte
+// e + 127 (0 for an all-zero block); each value becomes the E2M1 number
+// nearest to v / X (v_ldexp: exact), ties to the even code, saturating at 6,
+// a zero magnitude as code 0.  The lane's 16 codes are packed element j in
+// nibble j of packed (element 2j in the low nibble of byte j).
+__device__ __forceinline__ uint32_t mx_quantize16(const float (&v)[16], u32x2 &packed) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    {
+        const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(amax),
+                                                          __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+    }
+    int e = __builtin_amdgcn_frexp_expf(amax) - 3;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    const bool zero = !(amax > 0.0f);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float y = __builtin_amdgcn_ldexpf(v[j], -e);
+        const float m = fabsf(y);
+        uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                     (m >= 3.5f) + (m > 5.0f);
+        if (c != 0 && y < 0.0f) c |= 8u;
+        if (zero) c = 0;
+        if (j < 8) w0 |= c << (4 * j);
+        else w1 |= c << (4 * (j - 8));
+    }
+    packed.x = w0;
+    packed.y = w1;
+    return zero ? 0u : (uint32_t)(e + 127);
+}
+
 }  // namespace svdq

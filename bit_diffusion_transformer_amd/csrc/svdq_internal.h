@@ -39,11 +39,12 @@ inline DownWorkspace carve_down_workspace(void *base, int64_t M, int64_t K, int 
     return w;
 }
 
+// mx: the MXFP4 variant (E8M0 scale bytes [rows, K/32] in sa / sw)
 hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
                              int64_t M, int64_t K, int r, const DownWorkspace &ws, uint8_t *qa,
-                             float *sa, float *xl1, hipStream_t stream);
-hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
-                               hipStream_t stream);
+                             void *sa, float *xl1, hipStream_t stream, bool mx = false);
+hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, void *sw,
+                               hipStream_t stream, bool mx = false);
 // W4A16 records (16 columns x 4 groups each)
 int64_t awq_packed_bytes(int64_t N, int64_t K);
 int awq_rows_per_pass(int64_t K, size_t lds_limit);   // activation rows staged per workgroup
