@@ -27,7 +27,11 @@ from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError, 
                        svdq_w4a4_lr_gemm, svdq_w4a4_lr_gemm_qkv, svdq_linear_qkv,
                        svdq_w4a4_lr_gemm_quant_down,
                        svdq_w4a4_lr_gemm_quant_down_workspace_bytes, svdq_mlp,
-                       svdq_mlp_workspace_bytes)
+                       svdq_mlp_workspace_bytes, svdq_mx_pack_weights,
+                       svdq_mx_quantize_act_down, svdq_mx_lr_gemm,
+                       svdq_mx_linear_workspace_bytes, svdq_mx_linear)
+
+MX_BLOCK = 32   # values per E8M0 scale in the MXFP4 variant
 
 
 def _bits(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
@@ -233,3 +237,57 @@ class SVDQLinear:
             self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
         return linear(X, self.lam, self.L1, self.qw, self.sw, self.L2, self.bias, self.act,
                       workspace=self._ws)
+
+
+# ----------------------------------------------------------- MXFP4 variant
+
+def mx_pack_weights(R: torch.Tensor):
+    """Residual fp32 [N, K] -> (qw uint8 [N, K/2], sw uint8 E8M0 [N, K/32])."""
+    N, K = R.shape
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=R.device)
+    sw = torch.empty((N, K // MX_BLOCK), dtype=torch.uint8, device=R.device)
+    svdq_mx_pack_weights(R, N, K, qw, sw)
+    return qw, sw
+
+
+def mx_quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Tensor]):
+    """X bf16 [M, K] -> (qa uint8 [M, K/2], sa uint8 [M, K/32], xl1 fp32 [M, r] or None)."""
+    M, K = X.shape
+    r = _rank(L1, 1)
+    dev = X.device
+    qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // MX_BLOCK), dtype=torch.uint8, device=dev)
+    xl1 = torch.empty((M, r), dtype=torch.float32, device=dev) if r > 0 else None
+    ws_bytes = svdq_quantize_act_down_workspace_bytes(M, K, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    svdq_mx_quantize_act_down(_bits(X), lam, _bits(L1) if r > 0 else None, M, K, r, qa, sa, xl1,
+                              ws, ws_bytes)
+    return qa, sa, xl1
+
+
+def mx_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act: int = ACT_NONE) -> torch.Tensor:
+    """The MXFP4 GEMM with the low-rank up-projection, bias and act -> Y bf16 [M, N]."""
+    M = qa.shape[0]
+    N = qw.shape[0]
+    K = qa.shape[1] * 2
+    r = _rank(L2, 0)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    svdq_mx_lr_gemm(qa, sa, qw, sw, xl1 if r > 0 else None, _bits(L2) if r > 0 else None,
+                    _bits(bias), act, M, N, K, r, _bits(Y))
+    return Y
+
+
+def mx_linear(X, lam, L1, qw, sw, L2, bias, act: int = ACT_NONE,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole MXFP4 layer (svdq_mx_linear) -> Y bf16 [M, N]."""
+    M, K = X.shape
+    N = qw.shape[0]
+    r = _rank(L1, 1)
+    need = svdq_mx_linear_workspace_bytes(M, K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    svdq_mx_linear(_bits(X), lam, _bits(L1) if r > 0 else None, qw, sw,
+                   _bits(L2) if r > 0 else None, _bits(bias), act, M, N, K, r, _bits(Y),
+                   workspace, need)
+    return Y

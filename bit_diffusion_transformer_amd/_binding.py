@@ -32,7 +32,8 @@ EXPORTS = (
     "svdq_debug_set_tile_policy", "svdq_awq_packed_bytes", "svdq_awq_pack_weights",
     "svdq_awq_repack", "svdq_awq_w4a16_linear", "svdq_w4a4_lr_gemm_qkv", "svdq_linear_qkv",
     "svdq_w4a4_lr_gemm_quant_down_workspace_bytes", "svdq_w4a4_lr_gemm_quant_down",
-    "svdq_mlp_workspace_bytes", "svdq_mlp",
+    "svdq_mlp_workspace_bytes", "svdq_mlp", "svdq_mx_pack_weights", "svdq_mx_quantize_act_down",
+    "svdq_mx_lr_gemm", "svdq_mx_linear_workspace_bytes", "svdq_mx_linear",
 )
 
 
@@ -105,6 +106,11 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_mlp_workspace_bytes": ([I64, I64, I64, I32, I32], SZ),
         "svdq_mlp": ([P, P, P, P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, I32, I32, P, P,
                       SZ, P], I32),
+        "svdq_mx_pack_weights": ([P, I64, I64, P, P, P], I32),
+        "svdq_mx_quantize_act_down": ([P, P, P, I64, I64, I32, P, P, P, P, SZ, P], I32),
+        "svdq_mx_lr_gemm": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P], I32),
+        "svdq_mx_linear_workspace_bytes": ([I64, I64, I32], SZ),
+        "svdq_mx_linear": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -253,3 +259,32 @@ def svdq_mlp(X, lambda_up, L1_up, qw_up, sw_up, L2_up, bias_up, lambda_down, L1_
         _p(lambda_down), _p(L1_down), _p(qw_down), _p(sw_down), _p(L2_down), _p(bias_down),
         act, M, K, N_hidden, r_up, r_down, _p(Y), _p(workspace), ws_bytes, _stream(stream)),
         "svdq_mlp")
+
+
+def svdq_mx_pack_weights(R, N, K, qw, sw, stream=None):
+    _check(load_library().svdq_mx_pack_weights(_p(R), N, K, _p(qw), _p(sw), _stream(stream)),
+           "svdq_mx_pack_weights")
+
+
+def svdq_mx_quantize_act_down(X, lam, L1, M, K, r, qa, sa, xl1, workspace, ws_bytes,
+                              stream=None):
+    _check(load_library().svdq_mx_quantize_act_down(
+        _p(X), _p(lam), _p(L1), M, K, r, _p(qa), _p(sa), _p(xl1), _p(workspace), ws_bytes,
+        _stream(stream)), "svdq_mx_quantize_act_down")
+
+
+def svdq_mx_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, stream=None):
+    _check(load_library().svdq_mx_lr_gemm(
+        _p(qa), _p(sa), _p(qw), _p(sw), _p(xl1), _p(L2), _p(bias), act, M, N, K, r, _p(Y),
+        _stream(stream)), "svdq_mx_lr_gemm")
+
+
+def svdq_mx_linear_workspace_bytes(M, K, r) -> int:
+    return int(load_library().svdq_mx_linear_workspace_bytes(M, K, r))
+
+
+def svdq_mx_linear(X, lam, L1, qw, sw, L2, bias, act, M, N, K, r, Y, workspace, ws_bytes,
+                   stream=None):
+    _check(load_library().svdq_mx_linear(
+        _p(X), _p(lam), _p(L1), _p(qw), _p(sw), _p(L2), _p(bias), act, M, N, K, r, _p(Y),
+        _p(workspace), ws_bytes, _stream(stream)), "svdq_mx_linear")

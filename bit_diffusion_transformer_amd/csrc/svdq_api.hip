@@ -71,6 +71,14 @@ int32_t check_k(int64_t K) {
     return SVDQ_OK;
 }
 
+// The MXFP4 variant: whole stages of two groups (128 values) along K.
+int32_t check_k_mx(int64_t K) {
+    if (K < 128 || K % 128 != 0)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
+                    "K must be a positive multiple of 128 for MXFP4 (got %lld)", (long long)K);
+    return SVDQ_OK;
+}
+
 int32_t check_r(int32_t r) {
     if (r < 0 || r > SVDQ_MAX_RANK || r % 16 != 0)
         return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
@@ -108,7 +116,7 @@ int32_t lr_ptrs(const void *a, const char *an, const void *b, const char *bn, in
 }
 
 int32_t validate_down(const uint16_t *X, const float *lambda, const uint16_t *L1, int64_t M,
-                      int64_t K, int32_t r, const uint8_t *qa, const float *sa,
+                      int64_t K, int32_t r, const uint8_t *qa, const void *sa,
                       const float *xl1, const void *ws, size_t ws_bytes) {
     if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
     SVDQ_TRY(check_k(K));
@@ -126,7 +134,7 @@ int32_t validate_down(const uint16_t *X, const float *lambda, const uint16_t *L1
     return need == 0 ? SVDQ_OK : need_ptr(ws, "workspace");
 }
 
-int32_t validate_gemm(const uint8_t *qa, const float *sa, const uint8_t *qw, const float *sw,
+int32_t validate_gemm(const uint8_t *qa, const void *sa, const uint8_t *qw, const void *sw,
                       const float *xl1, const uint16_t *L2, const uint16_t *bias, int32_t act,
                       int64_t M, int64_t N, int64_t K, int32_t r, const uint16_t *Y) {
     if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
@@ -194,7 +202,8 @@ struct LinearWorkspace {
     size_t bytes;
 };
 
-LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r) {
+// mx: the scales are E8M0 bytes [M, K/32] instead of fp32 [M, K/64].
+LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r, bool mx = false) {
     using svdq::align256;
     LinearWorkspace w{};
     char *p = static_cast<char *>(base);
@@ -202,7 +211,7 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r) {
     w.qa = reinterpret_cast<uint8_t *>(p + off);
     off += align256((size_t)M * (size_t)(K / 2));
     w.sa = reinterpret_cast<float *>(p + off);
-    off += align256((size_t)M * (size_t)(K / SVDQ_GROUP) * 4);
+    off += align256(mx ? (size_t)M * (size_t)(K / 32) : (size_t)M * (size_t)(K / SVDQ_GROUP) * 4);
     w.xl1 = r > 0 ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256((size_t)M * (size_t)r * 4);
     w.down = p + off;
@@ -550,6 +559,92 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
                                              bias_down, SVDQ_ACT_NONE, M, K, N_hidden, r_down, Y,
                                              s),
                       "w4a4_lr_gemm launch");
+}
+
+// ------------------------------------------------------------------ MXFP4
+
+int32_t svdq_mx_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, uint8_t *sw,
+                             void *stream) {
+    g_last_error[0] = 0;
+    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+    SVDQ_TRY(check_k_mx(K));
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(R, "R"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_pack_weights(R, N, K, qw, sw, (hipStream_t)stream, true),
+                      "mx_pack_weights launch");
+}
+
+int32_t svdq_mx_quantize_act_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                                  int64_t M, int64_t K, int32_t r, uint8_t *qa, uint8_t *sa,
+                                  float *xl1, void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    SVDQ_TRY(check_k_mx(K));
+    SVDQ_TRY(validate_down(X, lambda, L1, M, K, r, qa, sa, xl1, workspace, ws_bytes));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(workspace, M, K, r);
+    return hip_status(svdq::launch_quant_down(X, lambda, L1, M, K, r, dw, qa, sa, xl1, s, true),
+                      "mx_quantize_act_down launch");
+}
+
+int32_t svdq_mx_lr_gemm(const uint8_t *qa, const uint8_t *sa, const uint8_t *qw,
+                        const uint8_t *sw, const float *xl1, const uint16_t *L2,
+                        const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                        int32_t r, uint16_t *Y, void *stream) {
+    g_last_error[0] = 0;
+    SVDQ_TRY(check_k_mx(K));
+    SVDQ_TRY(validate_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_w4a4_mx_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r,
+                                                Y, (hipStream_t)stream),
+                      "mx_lr_gemm launch");
+}
+
+size_t svdq_mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t r) {
+    if (M < 0 || K < 0 || r < 0) return 0;
+    return carve_linear(nullptr, M, K, r, true).bytes;
+}
+
+int32_t svdq_mx_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                       const uint8_t *qw, const uint8_t *sw, const uint16_t *L2,
+                       const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                       int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
+        return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
+    SVDQ_TRY(check_n(N));
+    SVDQ_TRY(check_k_mx(K));
+    SVDQ_TRY(check_r(r));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(X, "X"));
+    SVDQ_TRY(need_ptr(lambda, "lambda"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
+    SVDQ_TRY(need_ptr(Y, "Y"));
+    SVDQ_TRY(lr_ptrs(L1, "L1", L2, "L2", r));
+    if (bias && !aligned16(bias)) return fail(SVDQ_ERR_MISALIGNED, "bias is not 16-byte aligned");
+    const size_t need = carve_linear(nullptr, M, K, r, true).bytes;
+    if (ws_bytes < need)
+        return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < %zu needed", ws_bytes,
+                    need);
+    SVDQ_TRY(need_ptr(workspace, "workspace"));
+    SVDQ_TRY(check_device());
+    hipStream_t s = (hipStream_t)stream;
+    const LinearWorkspace w = carve_linear(workspace, M, K, r, true);
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.down, M, K, r);
+    uint8_t *sa = reinterpret_cast<uint8_t *>(w.sa);
+    SVDQ_TRY(hip_status(svdq::launch_quant_down(X, lambda, L1, M, K, r, dw, w.qa, sa, w.xl1, s,
+                                                true),
+                        "mx_quantize_act_down launch"));
+    return hip_status(svdq::launch_w4a4_mx_gemm(w.qa, sa, qw, sw, w.xl1, L2, bias, act, M, N, K,
+                                                r, Y, s),
+                      "mx_lr_gemm launch");
 }
 
 int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,

@@ -79,6 +79,21 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(u32x4 a, u32x4 b, f32x16 c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32 output tile, K = 64 E2M1 (4-bit float) per call, each k block of 32
+// scaled by its E8M0 byte (the matrix-core form of the OCP MX dot product).
+// Lane l supplies, for row/column l % 32, the 32 codes of k block l / 32
+// (16 bytes, element 2j in the low nibble of byte j) and that block's scale
+// byte in bits 0-7 of sa / sb; fp32 accumulate; same output layout as the
+// int8 instruction.
+__device__ __forceinline__ f32x16 mfma_mxfp4_32x32x64(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb,
+                                                      f32x16 c) {
+    const i32x8 A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8 B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 // ---------------------------------------------------------------- 4-bit operands
 
 // Widen 16 packed two's-complement nibbles (two dwords, element 2j in the

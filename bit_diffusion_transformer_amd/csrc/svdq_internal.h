@@ -95,6 +95,11 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
                             const float *sw, const float *xl1, const uint16_t *L2,
                             const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
                             int r, uint16_t *Y, hipStream_t stream);
+// MXFP4 variant: E8M0 scale bytes sa [M, K/32], sw [N, K/32]; K % 128 == 0.
+hipError_t launch_w4a4_mx_gemm(const uint8_t *qa, const uint8_t *sa, const uint8_t *qw,
+                               const uint8_t *sw, const float *xl1, const uint16_t *L2,
+                               const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
+                               int r, uint16_t *Y, hipStream_t stream);
 hipError_t launch_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
                              int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
                              int32_t *S, hipStream_t stream);

@@ -355,6 +355,137 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
     }
 }
 
+// ---------------------------------------------------------------- MXFP4 K loop
+// The 4-bit float variant: E2M1 codes in the same packed layout and the same
+// LDS ring, swizzle and code copies; E8M0 scale bytes [rows, K / 32] instead
+// of fp32 group scales.  The matrix unit applies the block scales itself
+// (one v_mfma_scale_f32_32x32x64_f8f6f4 per group of 64 and 32 x 32 block),
+// so the VALU does no per-group work at all.  K % 128 == 0: every stage holds
+// two full groups, i.e. four scale bytes (one dword) per row.
+//
+// Scale copies: one 256-byte transfer per wave and stage, lane l carrying
+// the dword of one row.  WB = 2: wave w copies operand w / 2 (weights,
+// tokens), rows 64 (w % 2) + l.  WB = 1: wave w copies operand w % 2, rows
+// l; waves 2, 3 repeat waves 0, 1 (identical bytes to identical addresses),
+// so that every wave issues the same number of copies per stage, which the
+// counted waits rely on.  In LDS the dwords sit at [row] after each
+// operand's codes (SA_OFF, SB_OFF of the stage).
+template <int WB>
+struct MxLoads { static constexpr int L = 2 * WB + 1; };
+
+template <int WB>
+__device__ __forceinline__ void issue_stage_mx(uint8_t *st, const CopyPlan<WB> &cp,
+                                               const Operands &op, int c) {
+    using C = Cfg<WB>;
+    const uint8_t *qws = op.qw0 + c * ROWP;
+    const uint8_t *qas = op.qa0 + c * ROWP;
+    const int wave = cp.wave;
+#pragma unroll
+    for (int i = 0; i < WB; ++i) {
+        const int row = 16 * WB * wave + 16 * i;
+        __builtin_amdgcn_global_load_lds(qws + cp.a_off[i], (lds_void *)(st + C::A_OFF + row * ROWP), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qas + cp.b_off[i], (lds_void *)(st + C::B_OFF + row * ROWP), 16, 0, 0);
+    }
+    const bool tok = WB == 2 ? (wave >> 1) != 0 : (wave & 1) != 0;
+    const int r0 = WB == 2 ? 64 * (wave & 1) : 0;
+    const uint8_t *src = (tok ? op.sa0 : op.sw0) + 4 * c;
+    __builtin_amdgcn_global_load_lds(src + cp.s_off[0],
+                                     (lds_void *)(st + (tok ? C::SB_OFF : C::SA_OFF) + 4 * r0), 4, 0, 0);
+}
+
+// One group's codes of the lane's blocks (16 bytes each).
+template <int WB>
+struct MxCodes { u32x4 a[WB], b[WB]; };
+
+template <int WB>
+__device__ __forceinline__ void read_codes_mx(MxCodes<WB> &f, const uint8_t *st,
+                                              const ReadPlan &rp, int gi) {
+#pragma unroll
+    for (int blk = 0; blk < WB; ++blk) {
+        f.a[blk] = *reinterpret_cast<const u32x4 *>(st + rp.a_code[gi] + blk * 32 * ROWP);
+        f.b[blk] = *reinterpret_cast<const u32x4 *>(st + rp.b_code[gi] + blk * 32 * ROWP);
+    }
+}
+
+// One stage's scale dwords of the lane's rows (byte q: k block q of the stage).
+template <int WB>
+struct MxScales { uint32_t a[WB], b[WB]; };
+
+template <int WB>
+__device__ __forceinline__ void read_scales_mx(MxScales<WB> &s, const uint8_t *st,
+                                               const ReadPlan &rp) {
+#pragma unroll
+    for (int blk = 0; blk < WB; ++blk) {
+        s.a[blk] = *reinterpret_cast<const uint32_t *>(st + rp.a_scale + blk * 32 * 4);
+        s.b[blk] = *reinterpret_cast<const uint32_t *>(st + rp.b_scale + blk * 32 * 4);
+    }
+}
+
+// Group gi of the stage on every block of the wave: the lane's k block is
+// 2 gi + ks2, so its scale byte sits at bit 8 (2 gi + ks2) of the dword.
+template <int WB>
+__device__ __forceinline__ void group_mx(f32x16 (&acc)[WB * WB], const MxCodes<WB> &f,
+                                         const MxScales<WB> &s, int sh) {
+    uint32_t ea[WB], eb[WB];
+#pragma unroll
+    for (int blk = 0; blk < WB; ++blk) {
+        ea[blk] = (s.a[blk] >> sh) & 0xFFu;
+        eb[blk] = (s.b[blk] >> sh) & 0xFFu;
+    }
+#pragma unroll
+    for (int t = 0; t < WB * WB; ++t) {
+        const int bi = t / WB, bj = t % WB;
+        acc[t] = mfma_mxfp4_32x32x64(f.a[bi], ea[bi], f.b[bj], eb[bj], acc[t]);
+    }
+}
+
+// Stage s: group 1 of the stage is read while group 0 computes; after the
+// barrier the buffer is refilled with stage s + 4 and the next stage's first
+// group and scales are read while group 1 computes.
+template <int WB>
+__device__ __forceinline__ void k_loop_mx(uint8_t *__restrict__ b0, uint8_t *__restrict__ b1,
+                                          uint8_t *__restrict__ b2, uint8_t *__restrict__ b3,
+                                          const CopyPlan<WB> &cp, const ReadPlan &rp,
+                                          const Operands &op, int ns, int ks2,
+                                          f32x16 (&acc)[WB * WB]) {
+    constexpr int L = MxLoads<WB>::L;
+    issue_stage_mx<WB>(b0, cp, op, 0);
+    if (ns > 1) issue_stage_mx<WB>(b1, cp, op, 1);
+    if (ns > 2) issue_stage_mx<WB>(b2, cp, op, 2);
+    if (ns > 3) issue_stage_mx<WB>(b3, cp, op, 3);
+    wait_stages<L>(ns < 4 ? ns - 1 : 3);
+    barrier();
+    const int sh0 = 8 * ks2, sh1 = 8 * (2 + ks2);
+    MxCodes<WB> f0, f1;
+    MxScales<WB> sc, sn;
+    read_codes_mx<WB>(f0, b0, rp, 0);
+    read_scales_mx<WB>(sc, b0, rp);
+
+    auto step = [&](int s, uint8_t *cur, uint8_t *nxt) {
+        read_codes_mx<WB>(f1, cur, rp, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        group_mx<WB>(acc, f0, sc, sh0);
+        wait_stages<L>(s + 1 < ns ? (ns - 2 - s < 2 ? ns - 2 - s : 2) : 0);
+        barrier();
+        if (s + 4 < ns) issue_stage_mx<WB>(cur, cp, op, s + 4);
+        // (after the last stage these read a stale, unused buffer)
+        read_codes_mx<WB>(f0, nxt, rp, 0);
+        read_scales_mx<WB>(sn, nxt, rp);
+        __builtin_amdgcn_sched_barrier(0);
+        group_mx<WB>(acc, f1, sc, sh1);
+        sc = sn;
+    };
+    for (int s = 0; s < ns; s += 4) {
+        step(s, b0, b1);
+        if (s + 1 >= ns) break;
+        step(s + 1, b1, b2);
+        if (s + 2 >= ns) break;
+        step(s + 2, b2, b3);
+        if (s + 3 >= ns) break;
+        step(s + 3, b3, b0);
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -671,11 +802,13 @@ enum { EPI_STORE = 0, EPI_QKV = 1, EPI_MLP = 2 };
 // One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0).
 // EPI_STORE: bias, activation, the [M, N] bf16 store; EPI_QKV: the fused QKV
 // epilogue (epi -> QkvArgs); EPI_MLP: the next layer's activation step
-// (epi -> MlpArgs).  The last two need WB = 2.
-template <int WB, int EPI = EPI_STORE>
+// (epi -> MlpArgs).  The last two need WB = 2.  MXF: the operands are MXFP4
+// (sa, sw point to E8M0 bytes [rows, K / 32]; K % 128 == 0); otherwise INT4
+// with fp32 group scales [rows, K / 64].
+template <int WB, int EPI = EPI_STORE, bool MXF = false>
 __device__ __forceinline__ void
-tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
-          const uint8_t *__restrict__ qw, const float *__restrict__ sw,
+tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
+          const uint8_t *__restrict__ qw, const void *__restrict__ sw,
           const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
           const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N, int64_t K, int r,
           uint16_t *__restrict__ Y, Smem<WB> &sm, int64_t m0, int64_t n0,
@@ -697,8 +830,13 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
     Operands op;
     op.qw0 = qw + n0 * (int64_t)kb;
     op.qa0 = qa + m0 * (int64_t)kb;
-    op.sw0 = reinterpret_cast<const uint8_t *>(sw + n0 * (int64_t)G);
-    op.sa0 = reinterpret_cast<const uint8_t *>(sa + m0 * (int64_t)G);
+    if constexpr (MXF) {                       // a byte per block of 32: 2 G per row
+        op.sw0 = static_cast<const uint8_t *>(sw) + n0 * (int64_t)(2 * G);
+        op.sa0 = static_cast<const uint8_t *>(sa) + m0 * (int64_t)(2 * G);
+    } else {                                   // an fp32 per group: 4 G bytes per row
+        op.sw0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sw) + n0 * (int64_t)G);
+        op.sa0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sa) + m0 * (int64_t)G);
+    }
 
     CopyPlan<WB> cp;
     cp.wave = __builtin_amdgcn_readfirstlane(wave);
@@ -712,7 +850,11 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
         cp.a_tail[i] = (uint32_t)(ra * kb + 16 * (seg & 1));
         cp.b_tail[i] = (uint32_t)(rb * kb + 16 * (seg & 1));
     }
-    {
+    if constexpr (MXF) {
+        const bool tok = WB == 2 ? (wave >> 1) != 0 : (wave & 1) != 0;
+        const int row = (WB == 2 ? 64 * (wave & 1) : 0) + lane;
+        cp.s_off[0] = (uint32_t)(min(row, tok ? mlast : nlast) * 2 * G);
+    } else {
         const int blk = WB == 2 ? wave : (wave & 1);
         const int row = 32 * blk + (lane >> 1);
         const int g = lane & 1;
@@ -732,8 +874,9 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
             rp.a_code[gi] = C::A_OFF + (wn * 32 * WB + r32) * ROWP + 16 * slot;
             rp.b_code[gi] = C::B_OFF + (wm * 32 * WB + r32) * ROWP + 16 * slot;
         }
-        rp.a_scale = C::SA_OFF + (wn * 32 * WB + r32) * GC * 4;
-        rp.b_scale = C::SB_OFF + (wm * 32 * WB + r32) * GC * 4;
+        constexpr int SROW = MXF ? 4 : GC * 4;    // scale bytes of a row per stage
+        rp.a_scale = C::SA_OFF + (wn * 32 * WB + r32) * SROW;
+        rp.b_scale = C::SB_OFF + (wm * 32 * WB + r32) * SROW;
         rp.keep_b = ks2 == 0;
     }
 
@@ -741,7 +884,12 @@ tile_body(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
 #pragma unroll
     for (int t = 0; t < NB; ++t) acc[t] = f32x16{};
 
-    k_loop<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, odd, acc);
+    if constexpr (MXF)
+        k_loop_mx<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, ks2,
+                      acc);
+    else
+        k_loop<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, odd,
+                   acc);
     __syncthreads();
 
     // ---- epilogue: rank-r up-projection on the same tile (bf16 MFMA, the

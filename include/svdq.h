@@ -270,6 +270,58 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
                  int32_t r_up, int32_t r_down, uint16_t *Y, void *workspace, size_t ws_bytes,
                  void *stream);
 
+/* ------------------------------------------------------------------
+ * The 4-bit float variant (MXFP4).  The blog "Bringing Nunchaku 4-bit
+ * inference to Diffusers" (section "Introducing Nunchaku Lite" and the
+ * quantization_config listing) gives svdq_w4a4 a 4-bit float variant beside
+ * INT4, for GPUs with native 4-bit float arithmetic, and leaves its scale
+ * format open.  The 4-bit float form with matrix-core support on gfx950 is
+ * MXFP4 of the OCP Microscaling Formats (MX) specification v1.0, which these
+ * entry points use:
+ *   - blocks of 32 consecutive values along K share one scale 2^e, stored
+ *     as the E8M0 byte e + 127, e = floor(log2 max|v|) - 2 clamped to
+ *     [-127, 127]; an all-zero block gets the byte 0 and zero codes;
+ *   - each value becomes the E2M1 number (magnitudes 0, 0.5, 1, 1.5, 2, 3,
+ *     4, 6; sign in bit 3) nearest to v / 2^e, ties to the even code,
+ *     magnitudes above 6 to 6; zero is stored as +0;
+ *   - codes packed as in the INT4 layout (two per byte, element 2j in the
+ *     low nibble, [rows, K/2]); scales u8 [rows, K/32].
+ * Y = act(sum_blocks 2^(ea + ew) sum_k a_k w_k + xl1 L2 + bias), with the
+ * smoothing, rank-r branch, bias and activation of the INT4 path; the block
+ * sums are formed by the matrix unit in fp32.  K % 128 == 0 throughout.
+ * Errors as the INT4 entry points, plus SVDQ_ERR_UNSUPPORTED_SHAPE for K.
+ * ------------------------------------------------------------------ */
+
+/* Offline MXFP4 quantization of the residual R (device fp32 [N, K]): codes
+ * qw [N, K/2], scale bytes sw [N, K/32] (device, out).  N >= 0 (0: no-op). */
+int32_t svdq_mx_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, uint8_t *sw,
+                             void *stream);
+
+/* svdq_quantize_act_down with the MXFP4 quantizer: qa [M, K/2], sa u8
+ * [M, K/32] (device, out; bit-exact with the definition above), xl1 as
+ * there.  Workspace: svdq_quantize_act_down_workspace_bytes(M, K, r). */
+int32_t svdq_mx_quantize_act_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                                  int64_t M, int64_t K, int32_t r, uint8_t *qa, uint8_t *sa,
+                                  float *xl1, void *workspace, size_t ws_bytes, void *stream);
+
+/* svdq_w4a4_lr_gemm on MXFP4 operands (sa u8 [M, K/32], sw u8 [N, K/32]);
+ * other arguments and shape rules as there.  Y is accumulated in fp32 and
+ * rounded once to bf16. */
+int32_t svdq_mx_lr_gemm(const uint8_t *qa, const uint8_t *sa, const uint8_t *qw,
+                        const uint8_t *sw, const float *xl1, const uint16_t *L2,
+                        const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                        int32_t r, uint16_t *Y, void *stream);
+
+/* Workspace bytes of svdq_mx_linear (qa, sa, xl1, down-projection scratch). */
+size_t svdq_mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t r);
+
+/* The whole MXFP4 layer: svdq_mx_quantize_act_down, then svdq_mx_lr_gemm on
+ * the same stream, intermediates carved out of `workspace`. */
+int32_t svdq_mx_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                       const uint8_t *qw, const uint8_t *sw, const uint16_t *L2,
+                       const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                       int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream);
+
 /*
  * Test hook: the exact per-group integer sums of a block, computed with the
  * same operand unpacking and int8 matrix instructions as the GEMM.

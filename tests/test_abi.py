@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     decl = declared_functions()
-    assert len(decl) == 21, decl
+    assert len(decl) == 26, decl
     assert sorted(_binding.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -299,3 +299,56 @@ def test_mlp_empty_and_workspace_sizes(lib):
     mlp = lib.svdq_mlp_workspace_bytes(100, 128, 256, 16, 32)
     # up-layer workspace + hidden codes, scales, xl1 and partials
     assert mlp == lin + 12800 + 1792 + 12800 + 25600
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+
+def _mxd(lib, X=A, lam=A, L1=A, M=16, K=1024, r=16, qa=A, sa=A, xl1=A, ws=A, ws_bytes=1 << 20):
+    return lib.svdq_mx_quantize_act_down(P(X), P(lam), P(L1), M, K, r, P(qa), P(sa), P(xl1),
+                                         P(ws), ws_bytes, None)
+
+
+def _mxg(lib, qa=A, sa=A, qw=A, sw=A, xl1=A, L2=A, bias=A, act=0, M=16, N=64, K=128, r=16, Y=A):
+    return lib.svdq_mx_lr_gemm(P(qa), P(sa), P(qw), P(sw), P(xl1), P(L2), P(bias), act,
+                               M, N, K, r, P(Y), None)
+
+
+def _mxl(lib, X=A, lam=A, L1=A, qw=A, sw=A, L2=A, bias=A, act=0, M=16, N=64, K=128, r=16, Y=A,
+         ws=A, ws_bytes=1 << 30):
+    return lib.svdq_mx_linear(P(X), P(lam), P(L1), P(qw), P(sw), P(L2), P(bias), act, M, N, K,
+                              r, P(Y), P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("call,kw,code", [
+    # K must be a positive multiple of 128 (whole stages of two 64-value groups)
+    (_mxd, dict(K=64), SHAPE), (_mxd, dict(K=192), SHAPE), (_mxd, dict(K=0), SHAPE),
+    (_mxg, dict(K=64), SHAPE), (_mxg, dict(K=320), SHAPE), (_mxl, dict(K=64), SHAPE),
+    (_mxd, dict(M=-1), INVALID), (_mxd, dict(r=8), SHAPE), (_mxd, dict(sa=0), INVALID),
+    (_mxd, dict(sa=U), MISALIGNED), (_mxd, dict(ws_bytes=16), WS_SMALL),
+    (_mxd, dict(r=0), INVALID),
+    (_mxg, dict(act=2), INVALID), (_mxg, dict(N=60), SHAPE), (_mxg, dict(sw=0), INVALID),
+    (_mxg, dict(sa=U), MISALIGNED), (_mxg, dict(L2=0), INVALID), (_mxg, dict(r=0), INVALID),
+    (_mxl, dict(M=-1), INVALID), (_mxl, dict(N=12), SHAPE), (_mxl, dict(r=17), SHAPE),
+    (_mxl, dict(sw=0), INVALID), (_mxl, dict(ws_bytes=1000), WS_SMALL),
+    (_mxl, dict(lam=U), MISALIGNED),
+])
+def test_mx_rejects(lib, call, kw, code):
+    assert call(lib, **kw) == code
+    assert lib.svdq_last_error()
+
+
+def test_mx_pack_rejects_empty_and_sizes(lib):
+    mp = lib.svdq_mx_pack_weights
+    assert mp(P(A), -1, 128, P(A), P(A), None) == INVALID
+    assert mp(P(A), 8, 64, P(A), P(A), None) == SHAPE
+    assert mp(P(0), 8, 128, P(A), P(A), None) == INVALID
+    assert mp(P(A), 8, 128, P(A), P(U), None) == MISALIGNED
+    assert mp(P(0), 0, 128, P(0), P(0), None) == OK
+    assert _mxd(lib, X=0, lam=0, L1=0, qa=0, sa=0, xl1=0, ws=0, M=0) == OK
+    assert _mxg(lib, qa=0, sa=0, qw=0, sw=0, xl1=0, L2=0, bias=0, Y=0, M=0) == OK
+    assert _mxl(lib, X=0, lam=0, L1=0, qw=0, sw=0, L2=0, bias=0, Y=0, ws=0, M=0) == OK
+    # codes, E8M0 bytes [M, K/32], xl1, down-projection partials (each 256-aligned)
+    M, K, r = 4608, 3072, 32
+    down = lib.svdq_quantize_act_down_workspace_bytes(M, K, r)
+    assert lib.svdq_mx_linear_workspace_bytes(M, K, r) == M * K // 2 + M * K // 32 + M * r * 4 + down
+    assert lib.svdq_mx_linear_workspace_bytes(-1, K, r) == 0
