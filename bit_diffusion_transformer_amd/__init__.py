@@ -34,6 +34,11 @@ from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError, 
 MX_BLOCK = 32   # values per E8M0 scale in the MXFP4 variant
 
 
+def mx_scale_rows(rows: int) -> int:
+    """Padded row count P of the block-major MXFP4 scale bytes [K/32, P]."""
+    return (int(rows) + 15) // 16 * 16
+
+
 def _bits(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     """bf16 tensor -> the same storage viewed as int16 (no copy)."""
     if t is None:
@@ -242,21 +247,22 @@ class SVDQLinear:
 # ----------------------------------------------------------- MXFP4 variant
 
 def mx_pack_weights(R: torch.Tensor):
-    """Residual fp32 [N, K] -> (qw uint8 [N, K/2], sw uint8 E8M0 [N, K/32])."""
+    """Residual fp32 [N, K] -> (qw uint8 [N, K/2], sw uint8 E8M0 [K/32, mx_scale_rows(N)])."""
     N, K = R.shape
     qw = torch.empty((N, K // 2), dtype=torch.uint8, device=R.device)
-    sw = torch.empty((N, K // MX_BLOCK), dtype=torch.uint8, device=R.device)
+    sw = torch.empty((K // MX_BLOCK, mx_scale_rows(N)), dtype=torch.uint8, device=R.device)
     svdq_mx_pack_weights(R, N, K, qw, sw)
     return qw, sw
 
 
 def mx_quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Tensor]):
-    """X bf16 [M, K] -> (qa uint8 [M, K/2], sa uint8 [M, K/32], xl1 fp32 [M, r] or None)."""
+    """X bf16 [M, K] -> (qa uint8 [M, K/2], sa uint8 [K/32, mx_scale_rows(M)],
+    xl1 fp32 [M, r] or None)."""
     M, K = X.shape
     r = _rank(L1, 1)
     dev = X.device
     qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-    sa = torch.empty((M, K // MX_BLOCK), dtype=torch.uint8, device=dev)
+    sa = torch.empty((K // MX_BLOCK, mx_scale_rows(M)), dtype=torch.uint8, device=dev)
     xl1 = torch.empty((M, r), dtype=torch.float32, device=dev) if r > 0 else None
     ws_bytes = svdq_quantize_act_down_workspace_bytes(M, K, r)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)

@@ -38,7 +38,7 @@ template <int NT> struct K1Chunk { static constexpr int KC = NT <= 2 ? 8 : (NT <
 
 // MX: the 4-bit float (MXFP4) variant -- the same smoothing and
 // down-projection, the MX quantizer per 32-value block, E8M0 scale bytes
-// [M, K/32] in sa.
+// block-major in sa ([K/32][mx_scale_rows(M)]).
 template <int NT, bool MX = false>
 __global__ void __launch_bounds__(256)
 quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
@@ -147,7 +147,8 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
                 if (row_ok) {
                     *reinterpret_cast<u32x2 *>(qa + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
                     if ((ks & 1) == 0)
-                        static_cast<uint8_t *>(sa)[row * 2 * G + 2 * g + (ks >> 1)] = (uint8_t)sb;
+                        static_cast<uint8_t *>(sa)[(2 * g + (ks >> 1)) * mx_scale_rows(M) + row] =
+                            (uint8_t)sb;
                 }
             } else {
                 const float s = quantize_group16(v, packed);
@@ -238,7 +239,8 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
             if (row_ok) {
                 *reinterpret_cast<u32x2 *>(qw + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
                 if ((ks & 1) == 0)
-                    static_cast<uint8_t *>(sw)[row * 2 * G + 2 * g + (ks >> 1)] = (uint8_t)sb;
+                    static_cast<uint8_t *>(sw)[(2 * g + (ks >> 1)) * mx_scale_rows(N) + row] =
+                        (uint8_t)sb;
             }
         } else {
             const float s = quantize_group16(v, packed);

@@ -202,7 +202,8 @@ struct LinearWorkspace {
     size_t bytes;
 };
 
-// mx: the scales are E8M0 bytes [M, K/32] instead of fp32 [M, K/64].
+// mx: the scales are block-major E8M0 bytes [K/32][mx_scale_rows(M)] instead of fp32
+// [M, K/64].
 LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r, bool mx = false) {
     using svdq::align256;
     LinearWorkspace w{};
@@ -211,7 +212,8 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r, bool m
     w.qa = reinterpret_cast<uint8_t *>(p + off);
     off += align256((size_t)M * (size_t)(K / 2));
     w.sa = reinterpret_cast<float *>(p + off);
-    off += align256(mx ? (size_t)M * (size_t)(K / 32) : (size_t)M * (size_t)(K / SVDQ_GROUP) * 4);
+    off += align256(mx ? (size_t)svdq::mx_scale_rows(M) * (size_t)(K / 32)
+                       : (size_t)M * (size_t)(K / SVDQ_GROUP) * 4);
     w.xl1 = r > 0 ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256((size_t)M * (size_t)r * 4);
     w.down = p + off;

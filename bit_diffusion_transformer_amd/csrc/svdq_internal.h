@@ -10,6 +10,10 @@ namespace svdq {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// MXFP4 scale bytes are block-major, [K/32][P]: P = rows rounded up to a
+// multiple of 16 (the bytes past `rows` are padding, never read into a result).
+__host__ __device__ inline int64_t mx_scale_rows(int64_t rows) { return (rows + 15) & ~(int64_t)15; }
+
 // svdq_quantize_act_down splits K into chunks of kc groups (one workgroup per
 // 64 rows and chunk); with more than one chunk and r > 0 the chunks' partial
 // x^ L1 sums go to the workspace and a second kernel adds them up.  kc keeps
@@ -39,7 +43,8 @@ inline DownWorkspace carve_down_workspace(void *base, int64_t M, int64_t K, int 
     return w;
 }
 
-// mx: the MXFP4 variant (E8M0 scale bytes [rows, K/32] in sa / sw)
+// mx: the MXFP4 variant (block-major E8M0 scale bytes [K/32][mx_scale_rows(rows)] in
+// sa / sw)
 hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
                              int64_t M, int64_t K, int r, const DownWorkspace &ws, uint8_t *qa,
                              void *sa, float *xl1, hipStream_t stream, bool mx = false);
@@ -95,7 +100,8 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
                             const float *sw, const float *xl1, const uint16_t *L2,
                             const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
                             int r, uint16_t *Y, hipStream_t stream);
-// MXFP4 variant: E8M0 scale bytes sa [M, K/32], sw [N, K/32]; K % 128 == 0.
+// MXFP4 variant: block-major E8M0 scale bytes sa [K/32][mx_scale_rows(M)], sw
+// [K/32][mx_scale_rows(N)]; K % 128 == 0.
 hipError_t launch_w4a4_mx_gemm(const uint8_t *qa, const uint8_t *sa, const uint8_t *qw,
                                const uint8_t *sw, const float *xl1, const uint16_t *L2,
                                const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,

@@ -357,25 +357,38 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
 
 // ---------------------------------------------------------------- MXFP4 K loop
 // The 4-bit float variant: E2M1 codes in the same packed layout and the same
-// LDS ring, swizzle and code copies; E8M0 scale bytes [rows, K / 32] instead
-// of fp32 group scales.  The matrix unit applies the block scales itself
-// (one v_mfma_scale_f32_32x32x64_f8f6f4 per group of 64 and 32 x 32 block),
-// so the VALU does no per-group work at all.  K % 128 == 0: every stage holds
-// two full groups, i.e. four scale bytes (one dword) per row.
+// LDS ring, swizzle and code copies; E8M0 scale bytes instead of fp32 group
+// scales.  The matrix unit applies the block scales itself (one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per group of 64 and 32 x 32 block), so the
+// VALU does no per-group work.  K % 128 == 0: every stage holds two full
+// groups, i.e. four k blocks of 32.
 //
-// Scale copies: one 256-byte transfer per wave and stage, lane l carrying
-// the dword of one row.  WB = 2: wave w copies operand w / 2 (weights,
-// tokens), rows 64 (w % 2) + l.  WB = 1: wave w copies operand w % 2, rows
-// l; waves 2, 3 repeat waves 0, 1 (identical bytes to identical addresses),
-// so that every wave issues the same number of copies per stage, which the
-// counted waits rely on.  In LDS the dwords sit at [row] after each
-// operand's codes (SA_OFF, SB_OFF of the stage).
+// The scale bytes are block-major, [K/32][P] with the row count rounded up
+// to P (a multiple of 16): a stage's bytes of a tile are four runs of BT
+// consecutive bytes, fetched in a few whole cache lines (row-major bytes
+// would cost one memory request per row and stage, as many as the codes).
+// Scale copies: one 256-byte transfer per wave and stage, lane l carrying 4
+// consecutive rows of one k block.  WB = 2: wave w copies operand w / 2
+// (weights, tokens), k blocks 2 (w % 2) + l / 32, rows 4 (l % 32) ..;
+// WB = 1: wave w copies operand w % 2, k block l / 16, rows 4 (l % 16) ..;
+// waves 2, 3 repeat waves 0, 1 (identical bytes to identical addresses), so
+// that every wave issues the same number of copies per stage, which the
+// counted waits rely on.  In LDS a stage holds [k block][BT rows] bytes per
+// operand at SA_OFF / SB_OFF.  Row groups past the padded rows re-read the
+// last one (never stored).
 template <int WB>
 struct MxLoads { static constexpr int L = 2 * WB + 1; };
 
+struct MxScaleSrc {
+    const uint8_t *base;   // the wave's operand, k block 0, first row of the tile
+    uint32_t stage;        // bytes per stage: 4 P
+    uint32_t off;          // the lane's offset: k block * P + row
+    int dst;               // LDS offset of the wave's transfer within a stage
+};
+
 template <int WB>
 __device__ __forceinline__ void issue_stage_mx(uint8_t *st, const CopyPlan<WB> &cp,
-                                               const Operands &op, int c) {
+                                               const Operands &op, const MxScaleSrc &ss, int c) {
     using C = Cfg<WB>;
     const uint8_t *qws = op.qw0 + c * ROWP;
     const uint8_t *qas = op.qa0 + c * ROWP;
@@ -386,94 +399,73 @@ __device__ __forceinline__ void issue_stage_mx(uint8_t *st, const CopyPlan<WB> &
         __builtin_amdgcn_global_load_lds(qws + cp.a_off[i], (lds_void *)(st + C::A_OFF + row * ROWP), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(qas + cp.b_off[i], (lds_void *)(st + C::B_OFF + row * ROWP), 16, 0, 0);
     }
-    const bool tok = WB == 2 ? (wave >> 1) != 0 : (wave & 1) != 0;
-    const int r0 = WB == 2 ? 64 * (wave & 1) : 0;
-    const uint8_t *src = (tok ? op.sa0 : op.sw0) + 4 * c;
-    __builtin_amdgcn_global_load_lds(src + cp.s_off[0],
-                                     (lds_void *)(st + (tok ? C::SB_OFF : C::SA_OFF) + 4 * r0), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(ss.base + c * ss.stage + ss.off, (lds_void *)(st + ss.dst), 4,
+                                     0, 0);
 }
 
-// One group's codes of the lane's blocks (16 bytes each).
+// One group's operands of the lane's blocks: 16 code bytes and the k block's
+// scale byte each.
 template <int WB>
-struct MxCodes { u32x4 a[WB], b[WB]; };
+struct MxFrag {
+    u32x4 a[WB], b[WB];
+    uint32_t ea[WB], eb[WB];
+};
 
+// rp.a_scale / b_scale: LDS offset of the lane's k block 0 (of the group)
+// byte of its block-0 row; k block q adds q BT, block j adds 32 j.
 template <int WB>
-__device__ __forceinline__ void read_codes_mx(MxCodes<WB> &f, const uint8_t *st,
-                                              const ReadPlan &rp, int gi) {
+__device__ __forceinline__ void read_mx(MxFrag<WB> &f, const uint8_t *st, const ReadPlan &rp,
+                                        int gi) {
+    constexpr int BT = Cfg<WB>::BT;
 #pragma unroll
     for (int blk = 0; blk < WB; ++blk) {
         f.a[blk] = *reinterpret_cast<const u32x4 *>(st + rp.a_code[gi] + blk * 32 * ROWP);
         f.b[blk] = *reinterpret_cast<const u32x4 *>(st + rp.b_code[gi] + blk * 32 * ROWP);
+        f.ea[blk] = st[rp.a_scale + 2 * gi * BT + 32 * blk];
+        f.eb[blk] = st[rp.b_scale + 2 * gi * BT + 32 * blk];
     }
 }
 
-// One stage's scale dwords of the lane's rows (byte q: k block q of the stage).
+// One group on every block of the wave.
 template <int WB>
-struct MxScales { uint32_t a[WB], b[WB]; };
-
-template <int WB>
-__device__ __forceinline__ void read_scales_mx(MxScales<WB> &s, const uint8_t *st,
-                                               const ReadPlan &rp) {
-#pragma unroll
-    for (int blk = 0; blk < WB; ++blk) {
-        s.a[blk] = *reinterpret_cast<const uint32_t *>(st + rp.a_scale + blk * 32 * 4);
-        s.b[blk] = *reinterpret_cast<const uint32_t *>(st + rp.b_scale + blk * 32 * 4);
-    }
-}
-
-// Group gi of the stage on every block of the wave: the lane's k block is
-// 2 gi + ks2, so its scale byte sits at bit 8 (2 gi + ks2) of the dword.
-template <int WB>
-__device__ __forceinline__ void group_mx(f32x16 (&acc)[WB * WB], const MxCodes<WB> &f,
-                                         const MxScales<WB> &s, int sh) {
-    uint32_t ea[WB], eb[WB];
-#pragma unroll
-    for (int blk = 0; blk < WB; ++blk) {
-        ea[blk] = (s.a[blk] >> sh) & 0xFFu;
-        eb[blk] = (s.b[blk] >> sh) & 0xFFu;
-    }
+__device__ __forceinline__ void group_mx(f32x16 (&acc)[WB * WB], const MxFrag<WB> &f) {
 #pragma unroll
     for (int t = 0; t < WB * WB; ++t) {
         const int bi = t / WB, bj = t % WB;
-        acc[t] = mfma_mxfp4_32x32x64(f.a[bi], ea[bi], f.b[bj], eb[bj], acc[t]);
+        acc[t] = mfma_mxfp4_32x32x64(f.a[bi], f.ea[bi], f.b[bj], f.eb[bj], acc[t]);
     }
 }
 
 // Stage s: group 1 of the stage is read while group 0 computes; after the
 // barrier the buffer is refilled with stage s + 4 and the next stage's first
-// group and scales are read while group 1 computes.
+// group is read while group 1 computes.
 template <int WB>
 __device__ __forceinline__ void k_loop_mx(uint8_t *__restrict__ b0, uint8_t *__restrict__ b1,
                                           uint8_t *__restrict__ b2, uint8_t *__restrict__ b3,
                                           const CopyPlan<WB> &cp, const ReadPlan &rp,
-                                          const Operands &op, int ns, int ks2,
+                                          const Operands &op, const MxScaleSrc &ss, int ns,
                                           f32x16 (&acc)[WB * WB]) {
     constexpr int L = MxLoads<WB>::L;
-    issue_stage_mx<WB>(b0, cp, op, 0);
-    if (ns > 1) issue_stage_mx<WB>(b1, cp, op, 1);
-    if (ns > 2) issue_stage_mx<WB>(b2, cp, op, 2);
-    if (ns > 3) issue_stage_mx<WB>(b3, cp, op, 3);
+    issue_stage_mx<WB>(b0, cp, op, ss, 0);
+    if (ns > 1) issue_stage_mx<WB>(b1, cp, op, ss, 1);
+    if (ns > 2) issue_stage_mx<WB>(b2, cp, op, ss, 2);
+    if (ns > 3) issue_stage_mx<WB>(b3, cp, op, ss, 3);
     wait_stages<L>(ns < 4 ? ns - 1 : 3);
     barrier();
-    const int sh0 = 8 * ks2, sh1 = 8 * (2 + ks2);
-    MxCodes<WB> f0, f1;
-    MxScales<WB> sc, sn;
-    read_codes_mx<WB>(f0, b0, rp, 0);
-    read_scales_mx<WB>(sc, b0, rp);
+    MxFrag<WB> f0, f1;
+    read_mx<WB>(f0, b0, rp, 0);
 
     auto step = [&](int s, uint8_t *cur, uint8_t *nxt) {
-        read_codes_mx<WB>(f1, cur, rp, 1);
+        read_mx<WB>(f1, cur, rp, 1);
         __builtin_amdgcn_sched_barrier(0);
-        group_mx<WB>(acc, f0, sc, sh0);
+        group_mx<WB>(acc, f0);
         wait_stages<L>(s + 1 < ns ? (ns - 2 - s < 2 ? ns - 2 - s : 2) : 0);
         barrier();
-        if (s + 4 < ns) issue_stage_mx<WB>(cur, cp, op, s + 4);
-        // (after the last stage these read a stale, unused buffer)
-        read_codes_mx<WB>(f0, nxt, rp, 0);
-        read_scales_mx<WB>(sn, nxt, rp);
+        if (s + 4 < ns) issue_stage_mx<WB>(cur, cp, op, ss, s + 4);
+        // (after the last stage this reads a stale, unused buffer)
+        read_mx<WB>(f0, nxt, rp, 0);
         __builtin_amdgcn_sched_barrier(0);
-        group_mx<WB>(acc, f1, sc, sh1);
-        sc = sn;
+        group_mx<WB>(acc, f1);
     };
     for (int s = 0; s < ns; s += 4) {
         step(s, b0, b1);
@@ -830,9 +822,9 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
     Operands op;
     op.qw0 = qw + n0 * (int64_t)kb;
     op.qa0 = qa + m0 * (int64_t)kb;
-    if constexpr (MXF) {                       // a byte per block of 32: 2 G per row
-        op.sw0 = static_cast<const uint8_t *>(sw) + n0 * (int64_t)(2 * G);
-        op.sa0 = static_cast<const uint8_t *>(sa) + m0 * (int64_t)(2 * G);
+    if constexpr (MXF) {                       // block-major bytes [K/32][P]: column offset
+        op.sw0 = static_cast<const uint8_t *>(sw) + n0;
+        op.sa0 = static_cast<const uint8_t *>(sa) + m0;
     } else {                                   // an fp32 per group: 4 G bytes per row
         op.sw0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sw) + n0 * (int64_t)G);
         op.sa0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sa) + m0 * (int64_t)G);
@@ -850,10 +842,21 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
         cp.a_tail[i] = (uint32_t)(ra * kb + 16 * (seg & 1));
         cp.b_tail[i] = (uint32_t)(rb * kb + 16 * (seg & 1));
     }
+    MxScaleSrc ss{};
     if constexpr (MXF) {
         const bool tok = WB == 2 ? (wave >> 1) != 0 : (wave & 1) != 0;
-        const int row = (WB == 2 ? 64 * (wave & 1) : 0) + lane;
-        cp.s_off[0] = (uint32_t)(min(row, tok ? mlast : nlast) * 2 * G);
+        const int64_t P = tok ? mx_scale_rows(M) : mx_scale_rows(N);
+        const int64_t r0 = tok ? m0 : n0;
+        // k block and first of the lane's 4 rows; clamped so that the dword
+        // stays inside the padded rows
+        const int blk = WB == 2 ? 2 * (wave & 1) + (lane >> 5) : (lane >> 4);
+        const int row4 = WB == 2 ? 4 * (lane & 31) : 4 * (lane & 15);
+        const int64_t rmax = P - 4 - r0;
+        const int rowc = (int)(row4 < rmax ? row4 : rmax);
+        ss.base = tok ? op.sa0 : op.sw0;
+        ss.stage = (uint32_t)(4 * P);
+        ss.off = (uint32_t)(blk * P + rowc);
+        ss.dst = (tok ? C::SB_OFF : C::SA_OFF) + (WB == 2 ? 256 * (wave & 1) : 0);
     } else {
         const int blk = WB == 2 ? wave : (wave & 1);
         const int row = 32 * blk + (lane >> 1);
@@ -874,9 +877,13 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
             rp.a_code[gi] = C::A_OFF + (wn * 32 * WB + r32) * ROWP + 16 * slot;
             rp.b_code[gi] = C::B_OFF + (wm * 32 * WB + r32) * ROWP + 16 * slot;
         }
-        constexpr int SROW = MXF ? 4 : GC * 4;    // scale bytes of a row per stage
-        rp.a_scale = C::SA_OFF + (wn * 32 * WB + r32) * SROW;
-        rp.b_scale = C::SB_OFF + (wm * 32 * WB + r32) * SROW;
+        if constexpr (MXF) {                      // [k block][row] bytes, k block ks2 of group 0
+            rp.a_scale = C::SA_OFF + ks2 * BT + wn * 32 * WB + r32;
+            rp.b_scale = C::SB_OFF + ks2 * BT + wm * 32 * WB + r32;
+        } else {
+            rp.a_scale = C::SA_OFF + (wn * 32 * WB + r32) * GC * 4;
+            rp.b_scale = C::SB_OFF + (wm * 32 * WB + r32) * GC * 4;
+        }
         rp.keep_b = ks2 == 0;
     }
 
@@ -885,7 +892,7 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
     for (int t = 0; t < NB; ++t) acc[t] = f32x16{};
 
     if constexpr (MXF)
-        k_loop_mx<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, ks2,
+        k_loop_mx<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ss, ns,
                       acc);
     else
         k_loop<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, odd,

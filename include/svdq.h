@@ -285,7 +285,11 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
  *     4, 6; sign in bit 3) nearest to v / 2^e, ties to the even code,
  *     magnitudes above 6 to 6; zero is stored as +0;
  *   - codes packed as in the INT4 layout (two per byte, element 2j in the
- *     low nibble, [rows, K/2]); scales u8 [rows, K/32].
+ *     low nibble, [rows, K/2]); scales u8 block-major, [K/32, P] with
+ *     P = rows rounded up to a multiple of 16: byte [b][i] scales k block b
+ *     of row i; bytes [b][rows .. P) are padding, left unwritten and never
+ *     read into a result.  (Row-major bytes would cost the GEMM one memory
+ *     request per row and k step, as many as the codes.)
  * Y = act(sum_blocks 2^(ea + ew) sum_k a_k w_k + xl1 L2 + bias), with the
  * smoothing, rank-r branch, bias and activation of the INT4 path; the block
  * sums are formed by the matrix unit in fp32.  K % 128 == 0 throughout.
@@ -293,18 +297,20 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
  * ------------------------------------------------------------------ */
 
 /* Offline MXFP4 quantization of the residual R (device fp32 [N, K]): codes
- * qw [N, K/2], scale bytes sw [N, K/32] (device, out).  N >= 0 (0: no-op). */
+ * qw [N, K/2], scale bytes sw [K/32, roundup(N, 16)] (device, out).  N >= 0
+ * (0: no-op). */
 int32_t svdq_mx_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, uint8_t *sw,
                              void *stream);
 
 /* svdq_quantize_act_down with the MXFP4 quantizer: qa [M, K/2], sa u8
- * [M, K/32] (device, out; bit-exact with the definition above), xl1 as
+ * [K/32, roundup(M, 16)] (device, out; bit-exact with the definition above), xl1 as
  * there.  Workspace: svdq_quantize_act_down_workspace_bytes(M, K, r). */
 int32_t svdq_mx_quantize_act_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
                                   int64_t M, int64_t K, int32_t r, uint8_t *qa, uint8_t *sa,
                                   float *xl1, void *workspace, size_t ws_bytes, void *stream);
 
-/* svdq_w4a4_lr_gemm on MXFP4 operands (sa u8 [M, K/32], sw u8 [N, K/32]);
+/* svdq_w4a4_lr_gemm on MXFP4 operands (sa u8 [K/32, roundup(M, 16)], sw u8
+ * [K/32, roundup(N, 16)]);
  * other arguments and shape rules as there.  Y is accumulated in fp32 and
  * rounded once to bf16. */
 int32_t svdq_mx_lr_gemm(const uint8_t *qa, const uint8_t *sa, const uint8_t *qw,

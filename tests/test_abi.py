@@ -352,3 +352,5 @@ def test_mx_pack_rejects_empty_and_sizes(lib):
     down = lib.svdq_quantize_act_down_workspace_bytes(M, K, r)
     assert lib.svdq_mx_linear_workspace_bytes(M, K, r) == M * K // 2 + M * K // 32 + M * r * 4 + down
     assert lib.svdq_mx_linear_workspace_bytes(-1, K, r) == 0
+    # block-major scale bytes [K/32][M rounded up to 16]: 4 x 112 -> 512 after alignment
+    assert lib.svdq_mx_linear_workspace_bytes(100, 128, 16) == 6400 + 512 + 6400

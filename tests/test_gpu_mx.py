@@ -17,6 +17,21 @@ from tests.helpers import assert_y_close, bf16_host, to_dev, xl1_bound
 
 pytestmark = pytest.mark.gpu
 
+
+def to_block_major(s: np.ndarray) -> np.ndarray:
+    """Oracle scale bytes [rows, K/32] -> the device layout [K/32, P] (padding zero)."""
+    rows = s.shape[0]
+    out = np.zeros((s.shape[1], bdt.mx_scale_rows(rows)), np.uint8)
+    out[:, :rows] = s.T
+    return out
+
+
+def from_block_major(d, rows: int) -> np.ndarray:
+    """Device scale bytes [K/32, P] -> [rows, K/32] (the padding dropped)."""
+    d = d.cpu().numpy() if hasattr(d, "cpu") else d
+    assert d.shape[1] == bdt.mx_scale_rows(rows)
+    return np.ascontiguousarray(d[:, :rows].T)
+
 # (M, K, N, r, act, bias): K % 128 == 0; one to nine stages of 128 along K
 # (fewer stages than the ring holds, and wrap-around), ragged M and N tails.
 SHAPES = [
@@ -49,7 +64,7 @@ def case(request):
 def test_mx_pack_weights_bit_exact(case):
     qw, sw = bdt.mx_pack_weights(to_dev(case["L"].R))
     assert np.array_equal(qw.cpu().numpy(), case["qw"])
-    assert np.array_equal(sw.cpu().numpy(), case["sw"])
+    assert np.array_equal(from_block_major(sw, case["N"]), case["sw"])
 
 
 def test_mx_quantize_act_down(case):
@@ -57,7 +72,7 @@ def test_mx_quantize_act_down(case):
     qa, sa, xl1 = bdt.mx_quantize_act_down(to_dev(L.X), to_dev(L.lam),
                                            to_dev(L.L1) if r else None)
     assert np.array_equal(qa.cpu().numpy(), case["qa"])
-    assert np.array_equal(sa.cpu().numpy(), case["sa"])
+    assert np.array_equal(from_block_major(sa, case["M"]), case["sa"])
     if r:
         got = xl1.cpu().numpy().astype(np.float64)
         assert np.all(np.abs(got - case["xl1"]) <= xl1_bound(case["xh"], L.L1))
@@ -76,8 +91,9 @@ def test_mx_gemm_stagewise(case, tiles):
     # Same inputs on both sides: the oracle's codes, scale bytes and xl1 (fp32).
     L, r, K = case["L"], case["r"], case["K"]
     xl1_32 = case["xl1"].astype(np.float32) if r else None
-    Y = bdt.mx_lr_gemm(to_dev(case["qa"]), to_dev(case["sa"]), to_dev(case["qw"]),
-                       to_dev(case["sw"]), to_dev(xl1_32), to_dev(L.L2) if r else None,
+    Y = bdt.mx_lr_gemm(to_dev(case["qa"]), to_dev(to_block_major(case["sa"])),
+                       to_dev(case["qw"]), to_dev(to_block_major(case["sw"])), to_dev(xl1_32),
+                       to_dev(L.L2) if r else None,
                        to_dev(L.bias), case["act"])
     _, y_or = oracle.mx_gemm_rows(case["qa"], case["sa"], case["qw"], case["sw"],
                                   None if xl1_32 is None else xl1_32.astype(np.float64),
@@ -88,7 +104,8 @@ def test_mx_gemm_stagewise(case, tiles):
 def test_mx_linear_end_to_end(case, tiles):
     L, r = case["L"], case["r"]
     Y = bdt.mx_linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None,
-                      to_dev(case["qw"]), to_dev(case["sw"]), to_dev(L.L2) if r else None,
+                      to_dev(case["qw"]), to_dev(to_block_major(case["sw"])),
+                      to_dev(L.L2) if r else None,
                       to_dev(L.bias), case["act"])
     _, y_or = oracle.mx_linear(L.X, L.lam, L.L1 if r else None, case["qw"], case["sw"],
                                L.L2 if r else None, L.bias, case["act"])
@@ -99,7 +116,8 @@ def test_mx_deterministic_and_tile_shapes_agree(case):
     # Both tile shapes run the same per-output instruction sequence.
     L, r = case["L"], case["r"]
     args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
-            to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
+            to_dev(to_block_major(case["sw"])), to_dev(L.L2) if r else None, to_dev(L.bias),
+            case["act"])
     out = []
     try:
         for pol in (bdt.TILES_FULL, bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_AUTO):
@@ -141,12 +159,12 @@ def test_mx_quantizer_special_blocks():
     qa_o, sa_o, _ = oracle.mx_quantize_act(Xb, lam)
     qa, sa, _ = bdt.mx_quantize_act_down(to_dev(Xb), to_dev(lam), None)
     assert np.array_equal(qa.cpu().numpy(), qa_o)
-    assert np.array_equal(sa.cpu().numpy(), sa_o)
+    assert np.array_equal(from_block_major(sa, 3), sa_o)
     assert sa_o[0, 0] == 0 and sa_o[0, 1] == 0        # zero blocks
     qw, sw = bdt.mx_pack_weights(to_dev(X.astype(np.float32)))
     qw_o, sw_o = oracle.mx_quantize(X.astype(np.float32))
     assert np.array_equal(qw.cpu().numpy(), qw_o)
-    assert np.array_equal(sw.cpu().numpy(), sw_o)
+    assert np.array_equal(from_block_major(sw, 3), sw_o)
 
 
 FULL = [("qkv", CONFIGS["qkv"]), ("mlp_up", CONFIGS["mlp_up"]), ("mlp_down", CONFIGS["mlp_down"])]
@@ -162,12 +180,12 @@ def test_mx_full_size(name, spec):
     qw_o, sw_o = oracle.mx_quantize(L.R)
     qw, sw = bdt.mx_pack_weights(to_dev(L.R))
     assert np.array_equal(qw.cpu().numpy(), qw_o)
-    assert np.array_equal(sw.cpu().numpy(), sw_o)
+    assert np.array_equal(from_block_major(sw, N), sw_o)
     X, lam, L1, L2, bias = to_dev(L.X), to_dev(L.lam), to_dev(L.L1), to_dev(L.L2), to_dev(L.bias)
     qa_o, sa_o, xh = oracle.mx_quantize_act(L.X, L.lam)
     qa, sa, xl1 = bdt.mx_quantize_act_down(X, lam, L1)
     assert np.array_equal(qa.cpu().numpy(), qa_o)
-    assert np.array_equal(sa.cpu().numpy(), sa_o)
+    assert np.array_equal(from_block_major(sa, M), sa_o)
     xl1_o = oracle.down_proj(xh, L.L1)
     assert np.all(np.abs(xl1.cpu().numpy().astype(np.float64) - xl1_o) <= xl1_bound(xh, L.L1))
     Y = bdt.mx_linear(X, lam, L1, qw, sw, L2, bias, act)
