@@ -1011,17 +1011,24 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
                          wm, r32, ks2, tid);
         return;
     }
+    // The tile goes out through LDS: staged in [m][n] order, then written as
+    // 16-byte row segments, eight lanes per 128-byte line (a direct store
+    // from the transposed tile would write 8 bytes into each of 32 rows per
+    // instruction).  The staging area lies past the L2^T rows that other
+    // waves may still be reading for the rank-r step.
     // Block (bi, bj); element i of the lane is n = base + 8 (i / 4) +
     // 4 (lane / 32) + i % 4, m = base + lane % 32.
+    constexpr int OP = 2 * BT + 16;                          // staged row pitch, bytes
+    constexpr int OUT_OFF = BT * (SVDQ_MAX_RANK_DEV + 8) * 2;
+    static_assert(OUT_OFF + BT * OP <= (int)sizeof(Smem<WB>), "output staging fits in LDS");
+    uint8_t *ost = reinterpret_cast<uint8_t *>(&sm) + OUT_OFF;
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
         const int bi = t / WB, bj = t % WB;
-        const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
-        if (m >= M) continue;
+        const int ml = wm * 32 * WB + 32 * bj + r32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
-            if (n >= N) continue;
+            const int nl = wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
             const u32x2 b2 = bb[bi][q];
             const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
             float o[4];
@@ -1034,8 +1041,18 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
             u32x2 out;
             out.x = pack_bf16x2(o[0], o[1]);
             out.y = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<u32x2 *>(Y + m * N + n) = out;
+            *reinterpret_cast<u32x2 *>(ost + ml * OP + 2 * nl) = out;
         }
+    }
+    __syncthreads();
+    constexpr int CH = BT / 8;                               // 16-byte segments of a row
+#pragma unroll
+    for (int idx = tid; idx < BT * CH; idx += NTHR) {
+        const int row = idx / CH, ch = idx % CH;
+        const int64_t m = m0 + row, n = n0 + 8 * ch;
+        if (m < M && n < N)
+            *reinterpret_cast<u32x4 *>(Y + m * N + n) =
+                *reinterpret_cast<const u32x4 *>(ost + row * OP + 16 * ch);
     }
 }
 
