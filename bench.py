@@ -26,6 +26,9 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP4 (and FP6) MFMA, 10.1 PFLOP/s
+# VALU lane-operations per second without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 CACHE_BYTES = 256 << 20      # Infinity Cache; rotating input sets exceed 2x this
 METRIC = "effective TOPS (2MNK/t) of W4A4+rank-32 linear; % of INT8 MFMA / HBM peak"
 
@@ -37,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="qkv",
                     choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single",
-                             "qkv_fused", "mlp_chain"])
+                             "qkv_fused", "mlp_chain", "mx_qkv", "mx_mlp_up", "mx_mlp_down"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-overhead", action="store_true",
@@ -70,6 +73,8 @@ TRAFFIC = {
     "qkv": (None, None),
     "awq_mod": (os.path.join(ROOT, "profiles", "awq_w4a16_linear_mod_traffic.txt"),
                 (os.path.join(_CSRC, "awq_w4a16.hip"),)),
+    "mx_qkv": (os.path.join(ROOT, "profiles", "w4a4_mx_lr_gemm_qkv_traffic.txt"),
+               (os.path.join(_CSRC, "w4a4_tile.h"), os.path.join(_CSRC, "w4a4_mx_gemm.hip"))),
 }
 
 
@@ -312,6 +317,159 @@ def bench_qkv_fused(args):
     print(json.dumps(out), flush=True)
 
 
+def mx_gemm_bytes(M, N, K, r):
+    """Algorithmic bytes of one MXFP4 GEMM call: codes and E8M0 bytes of both
+    operands, xl1, L2, bias once, Y once."""
+    return (M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 4 * M * r + 2 * r * N + 2 * N
+            + 2 * M * N)
+
+
+def bench_mx(args):
+    """The MXFP4 (4-bit float) variant of the layer: one step = one svdq_mx_linear call on
+    the named workload's shapes.  Metric 2MNK/t as the default line; the INT4 svdq_linear
+    on the same inputs is timed beside it."""
+    import torch
+
+    import bit_diffusion_transformer_amd as bdt
+    from synth import CONFIGS, make_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    spec = CONFIGS[args.workload[3:]]
+    L = make_layer(spec, seed=0, M=args.M)
+    M, K, N, r, act = L.spec.M, L.spec.K, L.spec.N, L.spec.r, L.spec.act
+
+    def d(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    R = d(L.R)
+    qw, sw = bdt.mx_pack_weights(R)
+    qw4, sw4 = bdt.pack_weights(R)
+    del R
+    base = dict(X=d(L.X), lam=d(L.lam), L1=d(L.L1), L2=d(L.L2), bias=d(L.bias), qw=qw, sw=sw,
+                qw4=qw4, sw4=sw4)
+    ws_bytes = max(bdt.svdq_mx_linear_workspace_bytes(M, K, r),
+                   bdt.svdq_linear_workspace_bytes(M, K, r))
+    set_bytes = (2 * M * K + qw.numel() + sw.numel() + 2 * M * N + ws_bytes
+                 + 4 * K + 2 * K * r + 2 * r * N + 2 * N)
+    nsets = max(2, int(np.ceil(2 * CACHE_BYTES / set_bytes)))
+    bits = bdt._bits
+    sets = []
+    for _ in range(nsets):
+        st = {k: (v.clone() if v is not None else None) for k, v in base.items()}
+        st["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        st["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        sets.append(st)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        st = sets[i % nsets]
+        bdt.svdq_mx_linear(bits(st["X"]), st["lam"], bits(st["L1"]), st["qw"], st["sw"],
+                           bits(st["L2"]), bits(st["bias"]), act, M, N, K, r, bits(st["Y"]),
+                           st["ws"], ws_bytes, stream)
+
+    def int4(i):
+        st = sets[i % nsets]
+        bdt.svdq_linear(bits(st["X"]), st["lam"], bits(st["L1"]), st["qw4"], st["sw4"],
+                        bits(st["L2"]), bits(st["bias"]), act, M, N, K, r, bits(st["Y"]),
+                        st["ws"], ws_bytes, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    ops = 2.0 * M * N * K
+
+    carved = [bdt.mx_quantize_act_down(st["X"], st["lam"], st["L1"]) for st in sets]
+    down_ws = bdt.svdq_quantize_act_down_workspace_bytes(M, K, r)
+    for st in sets:
+        st["ws_down"] = torch.empty(max(down_ws, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def gemm(i):
+        st, (qa, sa, xl1) = sets[i % nsets], carved[i % nsets]
+        bdt.svdq_mx_lr_gemm(qa, sa, st["qw"], st["sw"], xl1, bits(st["L2"]), bits(st["bias"]),
+                            act, M, N, K, r, bits(st["Y"]), stream)
+
+    def quant(i):
+        st, (qa, sa, xl1) = sets[i % nsets], carved[i % nsets]
+        bdt.svdq_mx_quantize_act_down(bits(st["X"]), st["lam"], bits(st["L1"]), M, K, r, qa, sa,
+                                      xl1, st["ws_down"], down_ws, stream)
+
+    def time_loop(fn, n):
+        for i in range(20):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    n_k = max(args.steps, 20)
+    t_gemm = time_loop(gemm, n_k)
+    t_quant = time_loop(quant, n_k)
+    t_lin = time_loop(step, n_k)
+    t_int4 = time_loop(int4, n_k)
+    gemm_tflops = ops / t_gemm / 1e12
+    out = {
+        "metric": METRIC, "value": round(ops / t_step / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4",
+        "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
+        "config": {"workload": "%s: MXFP4 (E2M1, E8M0 per 32) M=%d K=%d N=%d r=%d act=%s "
+                               "bias=%s" % (args.workload, M, K, N, r, "gelu" if act else "none",
+                                            L.bias is not None),
+                   "global_batch": M, "input_sets_rotated": nsets},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload) if args.M is None else None,
+                     "kernel": "w4a4_mx_lr_gemm_kernel (one launch per svdq_mx_lr_gemm call)",
+                     "avg_launch_us": round(t_gemm * 1e6, 2), "algorithmic_ops": ops,
+                     "algorithmic_bytes": mx_gemm_bytes(M, N, K, r)},
+        "quantize_act_down": {"us": round(t_quant * 1e6, 2)},
+        "vs_int4": {"mx_linear_us": round(t_lin * 1e6, 2), "int4_linear_us": round(t_int4 * 1e6, 2),
+                    "speedup": round(t_int4 / t_lin, 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_mx(L, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_mx(L, target_s):
+    """The CPU oracle of the MXFP4 layer on a bounded sample (rows of X)."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    M, K, N, act = L.spec.M, L.spec.K, L.spec.N, L.spec.act
+    qw, sw = oracle.mx_quantize(L.R)              # offline, not timed
+
+    def run(rows):
+        X = np.ascontiguousarray(L.X[:rows])
+        t0 = time.perf_counter()
+        oracle.mx_linear(X, L.lam, L.L1, qw, sw, L.L2, L.bias, act)
+        return time.perf_counter() - t0
+
+    rows = min(M, 16)
+    t = run(rows)
+    if t < target_s / 4 and rows < M:
+        rows = int(min(M, max(rows + 1, rows * target_s / max(t, 1e-3))))
+        t = run(rows)
+    return {"value": round(2.0 * rows * N * K / t / 1e12, 5), "unit": "TOPS", "cores": cores,
+            "kind": "oracle",
+            "sample": "first %d of %d token rows of the same MXFP4 layer, %.1f s" % (rows, M, t)}
+
+
 def bench_mlp_chain(args):
     """One DiT block's MLP (3072 -> 12288 GELU -> 3072, rank 32, 4608 tokens): one step =
     one svdq_mlp call (the up GEMM runs the down layer's activation step in its epilogue).
@@ -452,7 +610,8 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    extra = {"qkv_fused": bench_qkv_fused, "mlp_chain": bench_mlp_chain}
+    extra = {"qkv_fused": bench_qkv_fused, "mlp_chain": bench_mlp_chain, "mx_qkv": bench_mx,
+             "mx_mlp_up": bench_mx, "mx_mlp_down": bench_mx}
     if args.workload.startswith("awq") or args.workload in extra:
         if args.gpus != 1:
             print("bench.py runs on one GPU only (--gpus %d requested)" % args.gpus,
@@ -576,6 +735,12 @@ def main():
                 "unit": "GB/s", "frac": round(gemm_gbs / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(args.workload) if args.M is None else None
     roof["kernel"] = "w4a4_lr_gemm_kernel (one launch per svdq_w4a4_lr_gemm call)"
+    # the co-bound: the per-group rescale, one int->float convert and one fma per output
+    # and group of 64 on the VALU
+    valu_ops = 2.0 * M * N * (K // 64)
+    roof["valu_rescale"] = {"lane_ops": valu_ops, "achieved": round(valu_ops / t_gemm / 1e12, 2),
+                            "peak": round(PEAK_VALU_TOPS, 2), "unit": "Tops",
+                            "frac": round(valu_ops / t_gemm / 1e12 / PEAK_VALU_TOPS, 4)}
     roof["avg_launch_us"] = round(t_gemm * 1e6, 2)
     roof["algorithmic_ops"] = ops
     roof["algorithmic_bytes"] = k2_bytes(M, N, K, r)
