@@ -55,18 +55,11 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-typedef int   i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// 32x32 output tile, K = 32 int8 per call.  Lane l supplies, for row/column
-// l % 32, 16 int8 of k-slot l / 32; output element i of lane l is row
-// 8*(i/4) + 4*(l/32) + i%4, column l % 32.
-__device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b, i32x16 c) {
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-
 // 32x32 output tile, K = 8 bf16 per call (4 per lane, k-slot l / 32), fp32
-// accumulate; same output layout as the int8 instruction.
+// accumulate; output element i of lane l is row 8 (i / 4) + 4 (l / 32) + i % 4,
+// column l % 32 (the layout of every 32x32 instruction used here).
 __device__ __forceinline__ f32x16 mfma_bf16_32x32x8(u32x2 a, u32x2 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a),
                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
@@ -85,8 +78,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // scaled by its E8M0 byte (the matrix-core form of the OCP MX dot product).
 // Lane l supplies, for row/column l % 32, the 32 codes of k block l / 32
 // (16 bytes, element 2j in the low nibble of byte j) and that block's scale
-// byte in bits 0-7 of sa / sb; fp32 accumulate; same output layout as the
-// int8 instruction.
+// byte in bits 0-7 of sa / sb; fp32 accumulate; the 32x32 output layout.
 __device__ __forceinline__ f32x16 mfma_mxfp4_32x32x64(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb,
                                                       f32x16 c) {
     const i32x8 A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
@@ -95,19 +87,52 @@ __device__ __forceinline__ f32x16 mfma_mxfp4_32x32x64(u32x4 a, uint32_t sa, u32x
 }
 
 // ---------------------------------------------------------------- 4-bit operands
+// Stored layout of the INT4 codes (qa, qw): two per byte, code e of each block
+// of 16 consecutive codes in nibble e of the block's 8 bytes (element 2j in
+// the low nibble of byte j); a nibble holds |c_e| in its low three bits and
+// the sign of c_((e - 1) mod 16) in its top bit.  One AND then gives the FP8
+// (E4M3) bytes of the even codes and a funnel shift plus an AND those of the
+// odd codes: the byte s000 0mmm is the E4M3 subnormal (-1)^s m 2^-9, so the
+// codes enter the FP8 matrix instruction as exact multiples of 2^-9, and the
+// instruction's block scale 2^9 on each operand makes its sums exact
+// integers (|sum| <= 64 * 49).
 
-// Widen 16 packed two's-complement nibbles (two dwords, element 2j in the
-// low nibble of byte j) into 16 int8 holding 16 * code: the even elements
-// land in dwords 0 and 2, the odd ones in dwords 1 and 3.  Both GEMM
-// operands are widened the same way, so the k pairing is preserved and the
-// int32 dot product is exactly 256 * (the dot product of the codes).
-__device__ __forceinline__ i32x4 widen_nibbles(u32x2 p) {
-    i32x4 r;
-    r.x = (int)((p.x << 4) & 0xF0F0F0F0u);
-    r.y = (int)(p.x & 0xF0F0F0F0u);
-    r.z = (int)((p.y << 4) & 0xF0F0F0F0u);
-    r.w = (int)(p.y & 0xF0F0F0F0u);
-    return r;
+// Two words of 8 two's-complement nibbles (codes 0-7 and 8-15 of a block,
+// code e in nibble e mod 8, every code in [-7, 7]) -> the stored words.
+__device__ __forceinline__ u32x2 store_code_words(uint32_t w0, uint32_t w1) {
+    // nibble-wise two's complement -> sign | magnitude: a negative nibble t
+    // (bit 3 set) becomes 8 | (16 - t), i.e. its bits flipped, plus one
+    auto sign_mag = [](uint32_t w) {
+        const uint32_t sg = w & 0x88888888u;
+        const uint32_t one = sg >> 3;
+        const uint32_t flip = (sg << 1) - one;       // 0xF in each negative nibble
+        return (((w ^ flip) + one) & 0x77777777u) | sg;
+    };
+    const uint32_t s0 = sign_mag(w0), s1 = sign_mag(w1);
+    // each nibble takes the sign bit of the nibble below it (cyclically over
+    // the block's 16 nibbles)
+    const uint32_t r0 = __builtin_amdgcn_alignbit(s0, s1, 28);
+    const uint32_t r1 = __builtin_amdgcn_alignbit(s1, s0, 28);
+    return u32x2{(r0 & 0x88888888u) | (s0 & 0x77777777u), (r1 & 0x88888888u) | (s1 & 0x77777777u)};
+}
+
+// The FP8 operand of 32 stored codes (two blocks, one 16-byte read).  The
+// slot order (codes 0, 2, 4, 6 | 1, 3, 5, 7 | 8, 10, .. of each block) is the
+// same for both GEMM operands, so the k pairing is preserved.
+__device__ __forceinline__ i32x8 codes_to_fp8(u32x4 x) {
+    constexpr uint32_t M = 0x87878787u;
+    return i32x8{(int)(x.x & M), (int)(__builtin_amdgcn_alignbit(x.y, x.x, 4) & M),
+                 (int)(x.y & M), (int)(__builtin_amdgcn_alignbit(x.x, x.y, 4) & M),
+                 (int)(x.z & M), (int)(__builtin_amdgcn_alignbit(x.w, x.z, 4) & M),
+                 (int)(x.w & M), (int)(__builtin_amdgcn_alignbit(x.z, x.w, 4) & M)};
+}
+
+// 32x32 output tile of exact per-group code sums S = sum_k qa qw over one
+// group of 64: lane l supplies row l % 32 and 32 of the group's codes
+// (k half l / 32) as FP8; the 32x32 output layout.  Scale bytes 127 + 9
+// multiply each operand by 2^9.
+__device__ __forceinline__ f32x16 mfma_codes_32x32x64(i32x8 a, i32x8 b) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, f32x16{}, 0, 0, 0, 136, 0, 136);
 }
 
 // ---------------------------------------------------------------- quantizer
@@ -115,8 +140,8 @@ __device__ __forceinline__ i32x4 widen_nibbles(u32x2 p) {
 // Quantize one group of 64 values spread over the four lanes
 // l, l^16, l^32, l^48 (16 consecutive values per lane).  Returns the group
 // scale s = max|v| / 7 (every lane of the group gets it) and writes the
-// lane's 16 codes, packed two per byte (element 2j in the low nibble), into
-// `packed`.  The code is rint(fl32(v * fl32(1/s))) clamped to [-7, 7]; a
+// lane's 16 codes (one block of the stored layout above) into `packed`.
+// The code is rint(fl32(v * fl32(1/s))) clamped to [-7, 7]; a
 // zero scale or a non-finite 1/s gives zero codes.  Division is IEEE
 // correctly rounded (hipcc's default); no contraction is allowed here.
 __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &packed) {
@@ -143,7 +168,7 @@ __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &p
     // rint via the 1.5*2^23 bias: after the clamp |y| <= 7, so y + 12582912
     // rounds (nearest even) to an integer whose low 4 bits are the code's
     // two's-complement nibble.  Funnel-shifting the nibbles in from the top
-    // leaves element j in nibble j.
+    // leaves element j in nibble j; store_code_words makes the stored form.
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -155,8 +180,7 @@ __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &p
         const float y = __builtin_amdgcn_fmed3f(v[j] * inv, -7.0f, 7.0f);
         w1 = __builtin_amdgcn_alignbit(__float_as_uint(y + 12582912.0f), w1, 4);
     }
-    packed.x = w0;
-    packed.y = w1;
+    packed = store_code_words(w0, w1);
     return s;
 }
 

@@ -47,9 +47,9 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
     }
 }
 
-// Test hook: per-group integer sums with the GEMM's k split, operand
-// widening and int8 matrix instruction; one wave per 32 x 32 block of
-// (n, m), operands read from memory.
+// Test hook: per-group integer sums with the GEMM's k split, FP8 operand
+// form and matrix instruction; one wave per 32 x 32 block of (n, m),
+// operands read from memory.  The sums are exact integers in fp32.
 __global__ void __launch_bounds__(64)
 group_sums_kernel(const uint8_t *__restrict__ qa, const uint8_t *__restrict__ qw, int64_t M,
                   int64_t N, int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
@@ -64,14 +64,12 @@ group_sums_kernel(const uint8_t *__restrict__ qa, const uint8_t *__restrict__ qw
     for (int64_t g = 0; g < G; ++g) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(qw + n * (K / 2) + g * 32 + 16 * ks2);
         const u32x4 b = *reinterpret_cast<const u32x4 *>(qa + m * (K / 2) + g * 32 + 16 * ks2);
-        i32x16 D = mfma_i8_32x32x32(widen_nibbles(u32x2{a.x, a.y}), widen_nibbles(u32x2{b.x, b.y}),
-                                    i32x16{});
-        D = mfma_i8_32x32x32(widen_nibbles(u32x2{a.z, a.w}), widen_nibbles(u32x2{b.z, b.w}), D);
+        const f32x16 D = mfma_codes_32x32x64(codes_to_fp8(a), codes_to_fp8(b));
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int64_t nl = nb * 32 + 8 * (i / 4) + 4 * ks2 + (i % 4);
             const int64_t ml = mb * 32 + r32;
-            if (nl < tn && ml < tm) S[(ml * tn + nl) * G + g] = D[i] >> 8;
+            if (nl < tn && ml < tm) S[(ml * tn + nl) * G + g] = (int32_t)D[i];
         }
     }
 }

@@ -17,23 +17,24 @@
 // one 8-byte write.
 //
 // Per group of 64 along K and per 32 x 32 output block the wave issues
-//   - two v_mfma_i32_32x32x32_i8 on the widened codes (the two k halves of
-//     the group, accumulated in the matrix unit): S, exact int32;
+//   - one v_mfma_scale_f32_32x32x64_f8f6f4 on the codes as FP8 (the stored
+//     code layout turns them into E4M3 subnormals with three VALU ops per
+//     8 codes, svdq_device.h): S, the group's exact integer sums, in fp32;
 //   - one v_mfma_f32_32x32x8_bf16 that forms the scale products
 //     P[n][m] = sw[n] sa[m] as an outer product of bf16 hi/lo pairs
 //     ((sw_hi + sw_lo)(sa_hi + sa_lo), exact bf16 products, fp32 sums,
 //     ~2^-16 relative to the fp32 product) in the same output layout;
-// and the VALU does only acc = fma(float(S), P, acc).  Formed on the VALU,
-// the scale product would be a third VALU op per output and group; the
-// rescale is what bounds this kernel on this chip (one group of 64 MACs per
-// output costs 1/16 of a 32x32x32 MFMA but 2 wave-wide VALU ops), so it is
-// kept to the minimum.
+// and the VALU does only acc = fma(S, P, acc).  The rescale is what bounds
+// this kernel on this chip (one group of 64 MACs per output costs 1/64 of a
+// 32x32x64 MFMA but a wave-wide VALU op), so it is kept to the minimum: with
+// the int8 instruction S came out as an integer and needed a convert per
+// output and group as well.
 //
 // Data movement: packed 4-bit codes and raw fp32 scales go from global
 // memory straight into a four-stage LDS ring with global_load_lds (no
 // registers, no LDS write instructions), up to three stages ahead of the one
 // being read; each wave reads its fragments with 16-byte LDS reads
-// (XOR-swizzled rows, no bank conflicts) and widens the codes to int8 in
+// (XOR-swizzled rows, no bank conflicts) and turns the codes into FP8 in
 // registers.
 #include "svdq_device.h"
 #include "svdq_internal.h"
@@ -195,7 +196,7 @@ struct Raw {
 };
 template <int WB>
 struct Frags {
-    i32x4 A[WB][2], B[WB][2];      // [block][k half]
+    i32x8 A[WB], B[WB];            // FP8 codes of the group, per block
     u32x2 AS[WB], BS[WB];
 };
 
@@ -211,22 +212,18 @@ __device__ __forceinline__ void read_raw(Raw<WB> &rw, const uint8_t *st, const R
     }
 }
 
-// Widen the codes and build the scale operands.  A lane holds 32 codes of
-// its row: k half h of the group takes codes [16 h, 16 h + 16) of them in
-// both operands, so the pairing of k is the same on both sides.  Weight scale
-// operand: bf16 (hi, hi, lo, lo) of sw * 2^-8 (the 2^-8 undoes the x16 of
-// both widened operands; exact).  Token operand: (hi, lo, hi, lo) of sa on
-// k-slot 0 lanes and zero elsewhere; `keep` false also zeroes a group past K,
-// which then adds exactly nothing.
+// FP8 codes and the scale operands.  A lane holds 32 codes of its row (the
+// group's k half ks2), the same 32 k in both operands.  Weight scale
+// operand: bf16 (hi, hi, lo, lo) of sw.  Token operand: (hi, lo, hi, lo) of sa
+// on k-slot 0 lanes and zero elsewhere; `keep` false also zeroes a group past
+// K, which then adds exactly nothing.
 template <int WB>
 __device__ __forceinline__ void make_frags(Frags<WB> &f, const Raw<WB> &rw, bool keep) {
 #pragma unroll
     for (int blk = 0; blk < WB; ++blk) {
-        f.A[blk][0] = widen_nibbles(u32x2{rw.a[blk].x, rw.a[blk].y});
-        f.A[blk][1] = widen_nibbles(u32x2{rw.a[blk].z, rw.a[blk].w});
-        f.B[blk][0] = widen_nibbles(u32x2{rw.b[blk].x, rw.b[blk].y});
-        f.B[blk][1] = widen_nibbles(u32x2{rw.b[blk].z, rw.b[blk].w});
-        const float va = rw.sa[blk] * 0.00390625f;
+        f.A[blk] = codes_to_fp8(rw.a[blk]);
+        f.B[blk] = codes_to_fp8(rw.b[blk]);
+        const float va = rw.sa[blk];
         const uint32_t ha = pack_bf16x2(va, va);
         const float la = va - bf16_lo(ha);
         f.AS[blk] = u32x2{ha, pack_bf16x2(la, la)};
@@ -239,44 +236,40 @@ __device__ __forceinline__ void make_frags(Frags<WB> &f, const Raw<WB> &rw, bool
 
 // The MFMA -> VALU pipeline of a wave.  The blocks of the two groups of a
 // stage form one stream j = 0 .. 2 NB - 1 (block j % NB, result slot j & 1):
-// the three MFMAs of block j go out while the VALU converts and accumulates
-// block j - 1, so the matrix unit and the VALU work side by side, also
-// across the group boundary.
+// the two MFMAs of block j go out while the VALU accumulates block j - 1, so
+// the matrix unit and the VALU work side by side, also across the group
+// boundary.
 struct Pipe {
-    i32x16 S[2];
+    f32x16 S[2];
     f32x16 P[2];
 };
 
 template <int WB>
 __device__ __forceinline__ void issue_block(Pipe &p, const Frags<WB> &f, int t, int k) {
     const int bi = t / WB, bj = t % WB;
-    p.S[k] = mfma_i8_32x32x32(f.A[bi][0], f.B[bj][0], i32x16{});
-    p.S[k] = mfma_i8_32x32x32(f.A[bi][1], f.B[bj][1], p.S[k]);
+    p.S[k] = mfma_codes_32x32x64(f.A[bi], f.B[bj]);
     p.P[k] = mfma_bf16_32x32x8(f.AS[bi], f.BS[bj], f32x16{});
 }
 
 template <int NB>
 __device__ __forceinline__ void valu_block(f32x16 (&acc)[NB], const Pipe &p, int t, int k) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        acc[t][i] = __builtin_fmaf((float)p.S[k][i], p.P[k][i], acc[t][i]);
+    for (int i = 0; i < 16; ++i) acc[t][i] = __builtin_fmaf(p.S[k][i], p.P[k][i], acc[t][i]);
 }
 
 // Issue stream element j while the VALU finishes element j - 1: one MFMA,
-// then about a third of the VALU work, three times.  The empty asm pins the
-// updated accumulator so later passes cannot sink the VALU work below the
-// following MFMAs.
+// then half of the VALU work, twice.  The empty asm pins the updated
+// accumulator so later passes cannot sink the VALU work below the following
+// MFMAs.
 template <int WB>
 __device__ __forceinline__ void pair(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f, int j) {
     constexpr int NB = WB * WB;
     issue_block<WB>(p, f, j % NB, j & 1);
     valu_block<NB>(acc, p, (j - 1) % NB, (j - 1) & 1);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 11, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     asm volatile("" : "+v"(acc[(j - 1) % NB]));
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -699,19 +692,41 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
             const float t = 1.0f / s;
             inv = __builtin_isfinite(t) ? t : 0.0f;
         }
+        // The lane's codes come in groups of four (nibbles e0 .. e0 + 3 of a
+        // stored block, e0 = 8 (q % 2) + 4 ks2); the stored nibble e carries
+        // the sign of code e - 1, so nibble e0 takes the sign of the last code
+        // of a group held by lane l ^ 32 (same token): q ^ 1 for ks2 = 0, q
+        // for ks2 = 1.
+        uint32_t wsm[WB][4];                 // sign | magnitude nibbles
+        uint32_t last = 0;                   // their last codes' signs, bit 4 bi + q
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float y = __builtin_amdgcn_fmed3f(acc[bi * WB + bj][4 * q + j] * inv, -7.0f, 7.0f);
+                    w |= (__float_as_uint(y + 12582912.0f) & 15u) << (4 * j);
+                }
+                const uint32_t sg = w & 0x8888u, one = sg >> 3;
+                w = (((w ^ ((sg << 1) - one)) + one) & 0x7777u) | sg;
+                wsm[bi][q] = w;
+                last |= (w >> 15) << (4 * bi + q);
+            }
+        }
+        const auto pl = __builtin_amdgcn_permlane32_swap(last, last, false, false);
+        const uint32_t other = pl[0] ^ pl[1] ^ last;   // the value of lane l ^ 32
         if (m < M) {
 #pragma unroll
             for (int bi = 0; bi < WB; ++bi) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    uint32_t w = 0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float y = __builtin_amdgcn_fmed3f(acc[bi * WB + bj][4 * q + j] * inv, -7.0f, 7.0f);
-                        w |= (__float_as_uint(y + 12582912.0f) & 15u) << (4 * j);
-                    }
+                    const uint32_t w = wsm[bi][q];
+                    const uint32_t first = (other >> (4 * bi + (ks2 ? q : (q ^ 1)))) & 1u;
+                    const uint32_t st = (w & 0x7777u) | ((w << 4) & 0x8880u) | (first << 3);
                     *reinterpret_cast<uint16_t *>(ma.qa + m * kb + (nw + 32 * bi + 8 * q + 4 * ks2) / 2) =
-                        (uint16_t)w;
+                        (uint16_t)st;
                 }
             }
             if (ks2 == 0) ma.sa[m * G + nw / kGroup] = s;

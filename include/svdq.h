@@ -32,8 +32,13 @@
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are
  *     row-major and contiguous.  Pointers marked "device" must point to
  *     memory of the current HIP device and be 16-byte aligned.
- *   - Packed codes: two per byte, element 2j in the low nibble, two's
- *     complement (nibble 0x9 = -7, 0xF = -1).  Scales: fp32 [rows, K/64].
+ *   - Packed INT4 codes (qa, qw): [rows, K/2] bytes, two per byte; in each
+ *     block of 16 consecutive codes of a row (8 bytes), code e sits in
+ *     nibble e (element 2j in the low nibble of byte j) and that nibble
+ *     holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 16) in bit 3
+ *     (zero is stored without sign).  With this layout the GEMM turns the
+ *     codes into FP8 (E4M3) operands of the matrix unit with three bit
+ *     operations per 8 codes.  Scales: fp32 [rows, K/64].
  *   - The caller owns and allocates every buffer.  The library allocates
  *     nothing and keeps no state except a per-device architecture check.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
@@ -284,8 +289,9 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
  *   - each value becomes the E2M1 number (magnitudes 0, 0.5, 1, 1.5, 2, 3,
  *     4, 6; sign in bit 3) nearest to v / 2^e, ties to the even code,
  *     magnitudes above 6 to 6; zero is stored as +0;
- *   - codes packed as in the INT4 layout (two per byte, element 2j in the
- *     low nibble, [rows, K/2]); scales u8 block-major, [K/32, P] with
+ *   - E2M1 codes packed two per byte, element 2j in the low nibble of byte
+ *     j, [rows, K/2] (the plain order: the scaled matrix instruction takes
+ *     them as they are); scales u8 block-major, [K/32, P] with
  *     P = rows rounded up to a multiple of 16: byte [b][i] scales k block b
  *     of row i; bytes [b][rows .. P) are padding, left unwritten and never
  *     read into a result.  (Row-major bytes would cost the GEMM one memory
