@@ -23,8 +23,13 @@
  *   - the code is rint(fl32(v * fl32(1 / scale))), ties to even; a zero
  *     scale, or a scale whose reciprocal overflows, gives all-zero codes;
  *   - smoothing is one fp32 multiply by fl32(1 / lambda);
- *   - codes are packed two per byte, element 2j in the low nibble, two's
- *     complement, row-major [rows, K/2]; scales row-major [rows, K/64];
+ *   - codes are packed two per byte, code k in the low nibble of byte k/2
+ *     when k is even and in the high nibble when odd, row-major [rows, K/2];
+ *     within each block of 16 consecutive codes of a row the nibble of code
+ *     e holds |c_e| in bits 0-2 and the sign of code (e - 1) mod 16 of the
+ *     same block in bit 3 (a zero code has no sign) -- the layout lets a GPU
+ *     hand the codes to an FP8 matrix instruction as exact subnormals;
+ *     scales row-major [rows, K/64];
  *   - the rescale, the low-rank products, bias and the erf-form GELU are
  *     taken in fp64, and the output is ONE correct rounding of that fp64
  *     value to bf16 (nearest, ties to even).
@@ -47,11 +52,11 @@ static float bf16_to_float(uint16_t h)
     return f;
 }
 
-/* Two's complement 4-bit code stored in a nibble -> integer in [-8, 7]. */
-static int nibble_to_int(unsigned nib)
+/* Nibble of code e of a block of 16 codes: |c_e|, and the sign of the code
+ * before it (cyclically) in bit 3. */
+static unsigned code_nibble(const int *blk, int e)
 {
-    int c = (int)(nib & 0xFu);
-    return c >= 8 ? c - 16 : c;
+    return (unsigned)abs(blk[e]) | (blk[(e + 15) % 16] < 0 ? 8u : 0u);
 }
 
 /*
@@ -151,21 +156,30 @@ void oracle_quantize_groups(const float *v, int64_t rows, int64_t K,
                 q[j] = (int)c;
             }
             uint8_t *dst = packed + row * (K / 2) + g * (GROUP / 2);
-            for (int b = 0; b < GROUP / 2; ++b)
-                dst[b] = (uint8_t)(((unsigned)q[2 * b] & 0xFu) |
-                                   (((unsigned)q[2 * b + 1] & 0xFu) << 4));
+            for (int b = 0; b < GROUP / 2; ++b) {
+                const int *blk = q + 16 * ((2 * b) / 16);
+                const int e = (2 * b) % 16;
+                dst[b] = (uint8_t)(code_nibble(blk, e) | (code_nibble(blk, e + 1) << 4));
+            }
         }
     }
 }
 
-/* Decode packed codes [rows, K/2] into one int8 per element [rows, K]. */
+/* Decode packed codes [rows, K/2] into one int8 per element [rows, K]: the
+ * magnitude of code e from its own nibble, its sign from bit 3 of the nibble
+ * of code (e + 1) mod 16 of the block. */
 void oracle_unpack(const uint8_t *packed, int64_t rows, int64_t K, int8_t *codes)
 {
     for (int64_t row = 0; row < rows; ++row)
-        for (int64_t k = 0; k < K; k += 2) {
-            uint8_t byte = packed[row * (K / 2) + k / 2];
-            codes[row * K + k] = (int8_t)nibble_to_int(byte);
-            codes[row * K + k + 1] = (int8_t)nibble_to_int(byte >> 4);
+        for (int64_t t = 0; t < K / 16; ++t) {
+            const uint8_t *src = packed + row * (K / 2) + 8 * t;
+            unsigned nib[16];
+            for (int e = 0; e < 16; ++e)
+                nib[e] = (e % 2 == 0) ? (src[e / 2] & 0xFu) : (src[e / 2] >> 4);
+            for (int e = 0; e < 16; ++e) {
+                const int mag = (int)(nib[e] & 7u);
+                codes[row * K + 16 * t + e] = (int8_t)((nib[(e + 1) % 16] & 8u) ? -mag : mag);
+            }
         }
 }
 

@@ -61,40 +61,6 @@ def xl1_bound(xh: np.ndarray, L1_bits: np.ndarray) -> np.ndarray:
     return (2.0 ** -15 + K * 2.0 ** -24) * mag + 1e-30
 
 
-def _nibbles(packed: np.ndarray) -> np.ndarray:
-    """[..., B] bytes -> [..., 2B] nibbles, element 2j = low nibble of byte j."""
-    p = np.asarray(packed, np.uint8)
-    return np.stack([p & 15, p >> 4], axis=-1).reshape(p.shape[:-1] + (2 * p.shape[-1],))
-
-
-def _pack_nibbles(n: np.ndarray) -> np.ndarray:
-    n = n.astype(np.uint8)
-    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
-
-
-def dev_codes(packed: np.ndarray) -> np.ndarray:
-    """The oracle's packed codes (two's complement nibbles, element 2j in the low nibble
-    of byte j) -> the library's stored layout of qa / qw (include/svdq.h, written from
-    that description alone): in each block of 16 consecutive codes of a row, nibble e
-    holds |c_e| in bits 0-2 and the sign of c_((e - 1) mod 16) in bit 3."""
-    n = _nibbles(packed).astype(np.int16)
-    c = np.where(n >= 8, n - 16, n).reshape(n.shape[:-1] + (-1, 16))
-    sign = (c < 0).astype(np.uint8)
-    prev = np.roll(sign, 1, axis=-1)              # prev[e] = sign[(e - 1) mod 16]
-    out = np.abs(c).astype(np.uint8) | (prev << 3)
-    return _pack_nibbles(out.reshape(n.shape))
-
-
-def plain_codes(stored: np.ndarray) -> np.ndarray:
-    """Inverse of dev_codes."""
-    n = _nibbles(stored)
-    blk = n.reshape(n.shape[:-1] + (-1, 16))
-    mag = (blk & 7).astype(np.int16)
-    sign = np.roll(blk >> 3, -1, axis=-1)         # sign[e] = bit 3 of nibble (e + 1) mod 16
-    c = np.where(sign == 1, -mag, mag)
-    return _pack_nibbles((c & 15).reshape(n.shape))
-
-
 def awq_records(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, N: int, K: int) -> np.ndarray:
     """The W4A16 records (the byte layout documented with svdq_awq_packed_bytes in svdq.h),
     built on the host from row-major codes [N, K/2] (element 2j in the low nibble of byte j),

@@ -10,7 +10,7 @@ import bit_diffusion_transformer_amd as bdt
 import oracle
 from bit_diffusion_transformer_amd import _binding
 from synth import LayerSpec, f32_to_bf16_bits, make_layer
-from tests.helpers import assert_y_close, bf16_host, dev_codes, to_dev
+from tests.helpers import assert_y_close, bf16_host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def test_zero_and_subnormal_groups_bit_exact():
     lam[200:260] = np.float32(3e38)              # pushes those x / lam into subnormals
     qa_o, sa_o, _ = oracle.quantize_act(X, lam)
     qa, sa, _ = bdt.quantize_act_down(to_dev(X), to_dev(lam), None)
-    assert np.array_equal(qa.cpu().numpy(), dev_codes(qa_o))
+    assert np.array_equal(qa.cpu().numpy(), qa_o)
     assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
     assert (sa_o == 0).any() and ((sa_o > 0) & (sa_o < 2.0 ** -126)).any()
     R = (rng.standard_normal((64, K)) * 0.05).astype(np.float32)
@@ -50,7 +50,7 @@ def test_zero_and_subnormal_groups_bit_exact():
     R[4, :64] = np.float32(1e-40)
     qw_o, sw_o = oracle.pack_weights(R)
     qw, sw = bdt.pack_weights(to_dev(R))
-    assert np.array_equal(qw.cpu().numpy(), dev_codes(qw_o))
+    assert np.array_equal(qw.cpu().numpy(), qw_o)
     assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_o.view(np.uint32))
 
 
@@ -62,10 +62,9 @@ def test_all_extreme_codes():
     R = np.where(np.arange(K) % 2 == 0, -0.5, 0.5)[None, :].repeat(N, 0).astype(np.float32)
     qa_o, sa_o, _ = oracle.quantize_act(X, lam)
     qw_o, sw_o = oracle.pack_weights(R)
-    qa_d, qw_d = to_dev(dev_codes(qa_o)), to_dev(dev_codes(qw_o))
-    S = bdt.group_sums(qa_d, qw_d, 0, 0, M, N).cpu().numpy()
+    S = bdt.group_sums(to_dev(qa_o), to_dev(qw_o), 0, 0, M, N).cpu().numpy()
     assert np.all(S == -3136)
-    Y = bdt.w4a4_lr_gemm(qa_d, to_dev(sa_o), qw_d, to_dev(sw_o), None, None, None)
+    Y = bdt.w4a4_lr_gemm(to_dev(qa_o), to_dev(sa_o), to_dev(qw_o), to_dev(sw_o), None, None, None)
     _, y_or = oracle.gemm_rows(qa_o, sa_o, qw_o, sw_o, None, None, None, 0, K)
     assert_y_close(bf16_host(Y), y_or)
 
@@ -96,7 +95,7 @@ def test_canaries_untouched():
         h = b.cpu()
         assert torch.all(h[:64] == fill) and torch.all(h[-64:] == fill)
     qa_o, sa_o, _ = oracle.quantize_act(L.X, L.lam)
-    assert np.array_equal(qa.cpu().numpy().reshape(M, K // 2), dev_codes(qa_o))
+    assert np.array_equal(qa.cpu().numpy().reshape(M, K // 2), qa_o)
 
 
 def test_side_stream_matches_default_stream():

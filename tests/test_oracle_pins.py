@@ -254,18 +254,21 @@ def test_zero_and_tiny_groups():
 # ---------------------------------------------------------------- group sums
 
 def _decode(packed, K):
-    lo = (packed & 0xF).astype(np.int64)
-    hi = (packed >> 4).astype(np.int64)
-    out = np.empty((packed.shape[0], K), np.int64)
-    out[:, 0::2] = lo
-    out[:, 1::2] = hi
-    return np.where(out >= 8, out - 16, out)
+    """Codes from the packed layout, written from its definition: code k in nibble k of
+    its row (low nibble of byte k/2 for even k); in each block of 16 codes, nibble e
+    holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 16) in bit 3."""
+    nib = np.empty((packed.shape[0], K), np.int64)
+    nib[:, 0::2] = packed & 0xF
+    nib[:, 1::2] = packed >> 4
+    blk = nib.reshape(packed.shape[0], K // 16, 16)
+    neg = np.roll(blk >> 3, -1, axis=-1)          # the sign of c_e sits in nibble e + 1
+    return np.where(neg == 1, -(blk & 7), blk & 7).reshape(packed.shape[0], K)
 
 
 def test_group_sums_closed_form_extreme():
     K = 128
     qa = np.full((2, K // 2), 0x77, np.uint8)          # every code 7
-    qw = np.full((3, K // 2), 0x99, np.uint8)          # every code -7
+    qw = np.full((3, K // 2), 0xFF, np.uint8)          # every code -7 (each nibble 7 | sign of the last)
     S = oracle.group_sums(qa, qw, K, 0, 0, 2, 3)
     assert S.shape == (2, 3, 2) and np.all(S == -3136)
 
