@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_INT8_TOPS = 5000.0      # MI355X dense 8-bit MFMA: INT8 5.0 POP/s, FP8 5.0 PFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP4 (and FP6) MFMA, 10.1 PFLOP/s
 # VALU lane-operations per second without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
@@ -299,7 +299,7 @@ def bench_qkv_fused(args):
     out = {
         "metric": METRIC, "value": round(ops / t_step / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
         "config": {"workload": "qkv_fused: M=%d K=%d N=%d r=%d group=64 heads=%d head_dim=%d "
                                "seq=%d, Q/K RMS norm + rotary, [B,H,S,D] bf16 out"
@@ -585,7 +585,7 @@ def bench_mlp_chain(args):
     out = {
         "metric": METRIC, "value": round(ops / t_step / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
         "config": {"workload": "mlp_chain: M=%d %d -> %d (GELU) -> %d, r=%d/%d group=64"
                                % (M, K, Nh, K, ru, rd),
@@ -756,7 +756,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "fp8",
         "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
         "config": {"workload": "%s: M=%d K=%d N=%d r=%d group=64 act=%s bias=%s"
                                % (spec.name, M, K, N, r, "gelu" if act else "none",
