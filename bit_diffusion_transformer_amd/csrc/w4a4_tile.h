@@ -485,7 +485,8 @@ namespace {
 // the wave's own 64 columns), v = x gamma / rho, then each adjacent pair
 // (2p, 2p + 1) -- two consecutive values of the same lane -- turns by the
 // caller's (cos, sin) of position s = m mod S.  V is only re-laid out.  The
-// stores go to [B, H, S, D] as 8-byte writes of four consecutive d.
+// results go to [B, H, S, D] through an LDS staging of the tile, as 16-byte
+// writes of eight consecutive d.
 template <int WB>
 __device__ __forceinline__ void
 qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk,
@@ -509,42 +510,44 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
             acc[t][4 * q + 3] += bf16_hi(b2.y);
         }
     }
-    // token of the lane in each column block bj: row offset in [B, H, S, D]
-    int64_t tok[WB];
+    // sequence position of the lane's token in each column block bj (rows
+    // past M take the last token's; they are never stored)
     int64_t spos[WB];
-    bool live[WB];
 #pragma unroll
     for (int bj = 0; bj < WB; ++bj) {
         const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
-        live[bj] = m < M;
         const int64_t mc = m < M ? m : M - 1;
-        const int64_t b = mc / S;
-        spos[bj] = mc - b * S;
-        tok[bj] = (b * qk.H * S + spos[bj]) * D;
+        spos[bj] = mc - (mc / S) * S;
     }
+    // The tile goes out through LDS (as the plain store): staged in [m][n]
+    // order past the L2^T rows, then written as 16-byte segments of 8
+    // consecutive d of one token and head, eight lanes per 128-byte line.
+    constexpr int BT = 64 * WB;
+    constexpr int OP = 2 * BT + 16;                          // staged row pitch, bytes
+    uint8_t *ost = reinterpret_cast<uint8_t *>(&sm) + BT * (SVDQ_MAX_RANK_DEV + 8) * 2;
+    static_assert(BT * (SVDQ_MAX_RANK_DEV + 8) * 2 + BT * OP <= (int)sizeof(Smem<WB>),
+                  "QKV output staging fits in LDS");
+    auto stage = [&](int bi, int bj, int q, u32x2 out) {
+        const int ml = wm * 32 * WB + 32 * bj + r32;
+        const int nl = wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
+        *reinterpret_cast<u32x2 *>(ost + ml * OP + 2 * nl) = out;
+    };
     if (sec == 2) {
 #pragma unroll
         for (int bi = 0; bi < WB; ++bi) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t nl = nsec + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
-                const int64_t h = nl / D, d = nl - h * D;
 #pragma unroll
                 for (int bj = 0; bj < WB; ++bj) {
-                    if (!live[bj]) continue;
                     const int t = bi * WB + bj;
                     u32x2 out;
                     out.x = pack_bf16x2(acc[t][4 * q], acc[t][4 * q + 1]);
                     out.y = pack_bf16x2(acc[t][4 * q + 2], acc[t][4 * q + 3]);
-                    *reinterpret_cast<u32x2 *>(qk.V + tok[bj] + h * S * D + d) = out;
+                    stage(bi, bj, q, out);
                 }
             }
         }
-        return;
-    }
-    if constexpr (WB == 1) {
-        return;   // quarter tiles are only ever V tiles (a head needs the full tile width)
-    } else {
+    } else if constexpr (WB == 2) {   // quarter tiles are only ever V tiles (a head needs the full tile width)
     // sum of squares of each token over this wave's columns (and the partner
     // lane l ^ 32, which holds the other half of every 8-column group)
     float ss[WB];
@@ -575,19 +578,16 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
 #pragma unroll
     for (int bj = 0; bj < WB; ++bj) inv[bj] = 1.0f / sqrtf(ss[bj] / (float)D + qk.eps);
     const uint16_t *gam = sec == 0 ? qk.gq : qk.gk;
-    uint16_t *dst = sec == 0 ? qk.Q : qk.K;
     const int half = D / 2;
 #pragma unroll
     for (int bi = 0; bi < WB; ++bi) {
         u32x2 g4[4];
         f32x2 cs[4][WB], sn[4][WB];
-        int64_t hoff[4], dd[4];
+        int64_t dd[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t nl = nsec + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
-            const int64_t h = nl / D;
-            dd[q] = nl - h * D;
-            hoff[q] = h * S * D;
+            dd[q] = nl - (nl / D) * D;
             g4[q] = *reinterpret_cast<const u32x2 *>(gam + dd[q]);
 #pragma unroll
             for (int bj = 0; bj < WB; ++bj) {
@@ -602,7 +602,6 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
                                  bf16_hi(g4[q].y)};
 #pragma unroll
             for (int bj = 0; bj < WB; ++bj) {
-                if (!live[bj]) continue;
                 const int t = bi * WB + bj;
                 float v[4];
 #pragma unroll
@@ -614,10 +613,25 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
                 u32x2 out;
                 out.x = pack_bf16x2(o0, o1);
                 out.y = pack_bf16x2(o2, o3);
-                *reinterpret_cast<u32x2 *>(dst + tok[bj] + hoff[q] + dd[q]) = out;
+                stage(bi, bj, q, out);
             }
         }
     }
+    }
+    __syncthreads();
+    uint16_t *dst = sec == 0 ? qk.Q : (sec == 1 ? qk.K : qk.V);
+    constexpr int CH = BT / 8;                               // 16-byte segments of a row
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int idx = tid; idx < BT * CH; idx += NTHR) {
+        const int row = idx / CH, ch = idx % CH;
+        const int64_t m = m0 + row;
+        if (m >= M) continue;
+        const int64_t nl = nsec + 8 * ch;
+        const int64_t h = nl / D, d = nl - h * D;
+        const int64_t b = m / S, sp = m - b * S;
+        *reinterpret_cast<u32x4 *>(dst + ((b * qk.H + h) * S + sp) * D + d) =
+            *reinterpret_cast<const u32x4 *>(ost + row * OP + 16 * ch);
     }
 }
 
