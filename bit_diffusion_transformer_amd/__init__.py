@@ -247,21 +247,22 @@ class SVDQLinear:
 # ----------------------------------------------------------- MXFP4 variant
 
 def mx_pack_weights(R: torch.Tensor):
-    """Residual fp32 [N, K] -> (qw uint8 [N, K/2], sw uint8 E8M0 [K/32, mx_scale_rows(N)])."""
+    """Residual fp32 [N, K] -> (qw uint8 [ceil(N/2), K] in row pairs,
+    sw uint8 E8M0 [K/32, mx_scale_rows(N)])."""
     N, K = R.shape
-    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=R.device)
+    qw = torch.empty(((N + 1) // 2, K), dtype=torch.uint8, device=R.device)
     sw = torch.empty((K // MX_BLOCK, mx_scale_rows(N)), dtype=torch.uint8, device=R.device)
     svdq_mx_pack_weights(R, N, K, qw, sw)
     return qw, sw
 
 
 def mx_quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Tensor]):
-    """X bf16 [M, K] -> (qa uint8 [M, K/2], sa uint8 [K/32, mx_scale_rows(M)],
-    xl1 fp32 [M, r] or None)."""
+    """X bf16 [M, K] -> (qa uint8 [ceil(M/2), K] in row pairs, sa uint8
+    [K/32, mx_scale_rows(M)], xl1 fp32 [M, r] or None)."""
     M, K = X.shape
     r = _rank(L1, 1)
     dev = X.device
-    qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    qa = torch.empty(((M + 1) // 2, K), dtype=torch.uint8, device=dev)
     sa = torch.empty((K // MX_BLOCK, mx_scale_rows(M)), dtype=torch.uint8, device=dev)
     xl1 = torch.empty((M, r), dtype=torch.float32, device=dev) if r > 0 else None
     ws_bytes = svdq_quantize_act_down_workspace_bytes(M, K, r)
@@ -271,11 +272,14 @@ def mx_quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.
     return qa, sa, xl1
 
 
-def mx_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act: int = ACT_NONE) -> torch.Tensor:
-    """The MXFP4 GEMM with the low-rank up-projection, bias and act -> Y bf16 [M, N]."""
-    M = qa.shape[0]
-    N = qw.shape[0]
-    K = qa.shape[1] * 2
+def mx_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act: int = ACT_NONE, M: Optional[int] = None,
+               N: Optional[int] = None) -> torch.Tensor:
+    """The MXFP4 GEMM with the low-rank up-projection, bias and act -> Y bf16 [M, N].
+    qa / qw hold row pairs ([ceil(rows/2), K]); M and N default to twice the pair
+    counts and must be given when odd."""
+    K = qa.shape[1]
+    M = 2 * qa.shape[0] if M is None else M
+    N = 2 * qw.shape[0] if N is None else N
     r = _rank(L2, 0)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
     svdq_mx_lr_gemm(qa, sa, qw, sw, xl1 if r > 0 else None, _bits(L2) if r > 0 else None,
@@ -284,10 +288,11 @@ def mx_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act: int = ACT_NONE) -> torch.Tens
 
 
 def mx_linear(X, lam, L1, qw, sw, L2, bias, act: int = ACT_NONE,
-              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The whole MXFP4 layer (svdq_mx_linear) -> Y bf16 [M, N]."""
+              workspace: Optional[torch.Tensor] = None, N: Optional[int] = None) -> torch.Tensor:
+    """The whole MXFP4 layer (svdq_mx_linear) -> Y bf16 [M, N]; N defaults to twice
+    qw's pair count and must be given when odd."""
     M, K = X.shape
-    N = qw.shape[0]
+    N = 2 * qw.shape[0] if N is None else N
     r = _rank(L1, 1)
     need = svdq_mx_linear_workspace_bytes(M, K, r)
     if workspace is None or workspace.numel() < need:

@@ -349,9 +349,9 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
 }
 
 // ---------------------------------------------------------------- MXFP4 K loop
-// The 4-bit float variant: E2M1 codes in the same packed layout and the same
-// LDS ring, swizzle and code copies; E8M0 scale bytes instead of fp32 group
-// scales.  The matrix unit applies the block scales itself (one
+// The 4-bit float variant: E2M1 codes (stored in row pairs, so that a code
+// copy reads whole 128-byte lines: a stage of two rows) in the same LDS ring,
+// swizzle and copy pattern; E8M0 scale bytes instead of fp32 group scales.  The matrix unit applies the block scales itself (one
 // v_mfma_scale_f32_32x32x64_f8f6f4 per group of 64 and 32 x 32 block), so the
 // VALU does no per-group work.  K % 128 == 0: every stage holds two full
 // groups, i.e. four k blocks of 32.
@@ -383,8 +383,8 @@ template <int WB>
 __device__ __forceinline__ void issue_stage_mx(uint8_t *st, const CopyPlan<WB> &cp,
                                                const Operands &op, const MxScaleSrc &ss, int c) {
     using C = Cfg<WB>;
-    const uint8_t *qws = op.qw0 + c * ROWP;
-    const uint8_t *qas = op.qa0 + c * ROWP;
+    const uint8_t *qws = op.qw0 + c * 128;   // row pairs: a stage is 128 bytes per pair
+    const uint8_t *qas = op.qa0 + c * 128;   // row pairs: a stage is 128 bytes per pair
     const int wave = cp.wave;
 #pragma unroll
     for (int i = 0; i < WB; ++i) {
@@ -866,8 +866,13 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
         const int row = 16 * WB * wave + 16 * i + (lane >> 2);
         const int seg = (lane & 3) ^ swz(row);     // global segment landing in this lane's slot
         const int ra = min(row, nlast), rb = min(row, mlast);
-        cp.a_off[i] = (uint32_t)(ra * kb + 16 * seg);
-        cp.b_off[i] = (uint32_t)(rb * kb + 16 * seg);
+        if constexpr (MXF) {   // row pairs (mx_code_offset): chunk of rows 2p, 2p + 1 in one line
+            cp.a_off[i] = (uint32_t)((ra >> 1) * 2 * kb + 64 * (ra & 1) + 16 * seg);
+            cp.b_off[i] = (uint32_t)((rb >> 1) * 2 * kb + 64 * (rb & 1) + 16 * seg);
+        } else {
+            cp.a_off[i] = (uint32_t)(ra * kb + 16 * seg);
+            cp.b_off[i] = (uint32_t)(rb * kb + 16 * seg);
+        }
         cp.a_tail[i] = (uint32_t)(ra * kb + 16 * (seg & 1));
         cp.b_tail[i] = (uint32_t)(rb * kb + 16 * (seg & 1));
     }

@@ -289,9 +289,13 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
  *   - each value becomes the E2M1 number (magnitudes 0, 0.5, 1, 1.5, 2, 3,
  *     4, 6; sign in bit 3) nearest to v / 2^e, ties to the even code,
  *     magnitudes above 6 to 6; zero is stored as +0;
- *   - E2M1 codes packed two per byte, element 2j in the low nibble of byte
- *     j, [rows, K/2] (the plain order: the scaled matrix instruction takes
- *     them as they are); scales u8 block-major, [K/32, P] with
+ *   - E2M1 codes two per byte, element 2j in the low nibble of byte j of
+ *     its row (the scaled matrix instruction takes them as they are); rows
+ *     stored in pairs, [ceil(rows/2), K] bytes: byte b of row i sits at
+ *     (i / 2) K + (b / 64) 128 + (i % 2) 64 + b % 64, so that each 64-byte
+ *     chunk of a row (128 codes) is followed by the same chunk of its pair
+ *     partner (one 128-byte line; a stage of the GEMM), and an odd row
+ *     count's last pair has an unwritten half; scales u8 block-major, [K/32, P] with
  *     P = rows rounded up to a multiple of 16: byte [b][i] scales k block b
  *     of row i; bytes [b][rows .. P) are padding, left unwritten and never
  *     read into a result.  (Row-major bytes would cost the GEMM one memory
@@ -303,13 +307,14 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
  * ------------------------------------------------------------------ */
 
 /* Offline MXFP4 quantization of the residual R (device fp32 [N, K]): codes
- * qw [N, K/2], scale bytes sw [K/32, roundup(N, 16)] (device, out).  N >= 0
- * (0: no-op). */
+ * qw [ceil(N/2), K] (row pairs), scale bytes sw [K/32, roundup(N, 16)]
+ * (device, out).  N >= 0 (0: no-op). */
 int32_t svdq_mx_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, uint8_t *sw,
                              void *stream);
 
-/* svdq_quantize_act_down with the MXFP4 quantizer: qa [M, K/2], sa u8
- * [K/32, roundup(M, 16)] (device, out; bit-exact with the definition above), xl1 as
+/* svdq_quantize_act_down with the MXFP4 quantizer: qa [ceil(M/2), K] (row
+ * pairs), sa u8 [K/32, roundup(M, 16)] (device, out; bit-exact with the
+ * definition above), xl1 as
  * there.  Workspace: svdq_quantize_act_down_workspace_bytes(M, K, r). */
 int32_t svdq_mx_quantize_act_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
                                   int64_t M, int64_t K, int32_t r, uint8_t *qa, uint8_t *sa,

@@ -26,6 +26,26 @@ def to_block_major(s: np.ndarray) -> np.ndarray:
     return out
 
 
+def to_pairs(p: np.ndarray) -> np.ndarray:
+    """Oracle codes [rows, K/2] -> the device's row-pair layout [ceil(rows/2), K]: each
+    64-byte chunk of a row followed by the same chunk of its pair partner."""
+    rows, kb = p.shape
+    q = np.zeros(((rows + 1) // 2 * 2, kb), np.uint8)
+    q[:rows] = p
+    return np.ascontiguousarray(
+        q.reshape(-1, 2, kb // 64, 64).transpose(0, 2, 1, 3).reshape(-1, 2 * kb))
+
+
+def from_pairs(d, rows: int) -> np.ndarray:
+    """Inverse of to_pairs (the unwritten half of an odd count's last pair dropped)."""
+    d = d.cpu().numpy() if hasattr(d, "cpu") else d
+    pairs, K = d.shape
+    assert pairs == (rows + 1) // 2
+    kb = K // 2
+    return np.ascontiguousarray(
+        d.reshape(pairs, kb // 64, 2, 64).transpose(0, 2, 1, 3).reshape(2 * pairs, kb)[:rows])
+
+
 def from_block_major(d, rows: int) -> np.ndarray:
     """Device scale bytes [K/32, P] -> [rows, K/32] (the padding dropped)."""
     d = d.cpu().numpy() if hasattr(d, "cpu") else d
@@ -63,7 +83,7 @@ def case(request):
 
 def test_mx_pack_weights_bit_exact(case):
     qw, sw = bdt.mx_pack_weights(to_dev(case["L"].R))
-    assert np.array_equal(qw.cpu().numpy(), case["qw"])
+    assert np.array_equal(from_pairs(qw, case["N"]), case["qw"])
     assert np.array_equal(from_block_major(sw, case["N"]), case["sw"])
 
 
@@ -71,7 +91,7 @@ def test_mx_quantize_act_down(case):
     L, r = case["L"], case["r"]
     qa, sa, xl1 = bdt.mx_quantize_act_down(to_dev(L.X), to_dev(L.lam),
                                            to_dev(L.L1) if r else None)
-    assert np.array_equal(qa.cpu().numpy(), case["qa"])
+    assert np.array_equal(from_pairs(qa, case["M"]), case["qa"])
     assert np.array_equal(from_block_major(sa, case["M"]), case["sa"])
     if r:
         got = xl1.cpu().numpy().astype(np.float64)
@@ -91,10 +111,10 @@ def test_mx_gemm_stagewise(case, tiles):
     # Same inputs on both sides: the oracle's codes, scale bytes and xl1 (fp32).
     L, r, K = case["L"], case["r"], case["K"]
     xl1_32 = case["xl1"].astype(np.float32) if r else None
-    Y = bdt.mx_lr_gemm(to_dev(case["qa"]), to_dev(to_block_major(case["sa"])),
-                       to_dev(case["qw"]), to_dev(to_block_major(case["sw"])), to_dev(xl1_32),
-                       to_dev(L.L2) if r else None,
-                       to_dev(L.bias), case["act"])
+    Y = bdt.mx_lr_gemm(to_dev(to_pairs(case["qa"])), to_dev(to_block_major(case["sa"])),
+                       to_dev(to_pairs(case["qw"])), to_dev(to_block_major(case["sw"])),
+                       to_dev(xl1_32), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"],
+                       M=case["M"], N=case["N"])
     _, y_or = oracle.mx_gemm_rows(case["qa"], case["sa"], case["qw"], case["sw"],
                                   None if xl1_32 is None else xl1_32.astype(np.float64),
                                   L.L2, L.bias, case["act"], K)
@@ -104,9 +124,8 @@ def test_mx_gemm_stagewise(case, tiles):
 def test_mx_linear_end_to_end(case, tiles):
     L, r = case["L"], case["r"]
     Y = bdt.mx_linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None,
-                      to_dev(case["qw"]), to_dev(to_block_major(case["sw"])),
-                      to_dev(L.L2) if r else None,
-                      to_dev(L.bias), case["act"])
+                      to_dev(to_pairs(case["qw"])), to_dev(to_block_major(case["sw"])),
+                      to_dev(L.L2) if r else None, to_dev(L.bias), case["act"], N=case["N"])
     _, y_or = oracle.mx_linear(L.X, L.lam, L.L1 if r else None, case["qw"], case["sw"],
                                L.L2 if r else None, L.bias, case["act"])
     assert_y_close(bf16_host(Y), y_or, "mx linear")
@@ -115,9 +134,9 @@ def test_mx_linear_end_to_end(case, tiles):
 def test_mx_deterministic_and_tile_shapes_agree(case):
     # Both tile shapes run the same per-output instruction sequence.
     L, r = case["L"], case["r"]
-    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
-            to_dev(to_block_major(case["sw"])), to_dev(L.L2) if r else None, to_dev(L.bias),
-            case["act"])
+    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None,
+            to_dev(to_pairs(case["qw"])), to_dev(to_block_major(case["sw"])),
+            to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
     out = []
     try:
         for pol in (bdt.TILES_FULL, bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_AUTO):
@@ -158,12 +177,12 @@ def test_mx_quantizer_special_blocks():
     lam = np.ones(K, np.float32)
     qa_o, sa_o, _ = oracle.mx_quantize_act(Xb, lam)
     qa, sa, _ = bdt.mx_quantize_act_down(to_dev(Xb), to_dev(lam), None)
-    assert np.array_equal(qa.cpu().numpy(), qa_o)
+    assert np.array_equal(from_pairs(qa, 3), qa_o)
     assert np.array_equal(from_block_major(sa, 3), sa_o)
     assert sa_o[0, 0] == 0 and sa_o[0, 1] == 0        # zero blocks
     qw, sw = bdt.mx_pack_weights(to_dev(X.astype(np.float32)))
     qw_o, sw_o = oracle.mx_quantize(X.astype(np.float32))
-    assert np.array_equal(qw.cpu().numpy(), qw_o)
+    assert np.array_equal(from_pairs(qw, 3), qw_o)
     assert np.array_equal(from_block_major(sw, 3), sw_o)
 
 
@@ -179,12 +198,12 @@ def test_mx_full_size(name, spec):
     print("mx config %s M=%d K=%d N=%d r=%d act=%d" % (name, M, K, N, r, act), flush=True)
     qw_o, sw_o = oracle.mx_quantize(L.R)
     qw, sw = bdt.mx_pack_weights(to_dev(L.R))
-    assert np.array_equal(qw.cpu().numpy(), qw_o)
+    assert np.array_equal(from_pairs(qw, N), qw_o)
     assert np.array_equal(from_block_major(sw, N), sw_o)
     X, lam, L1, L2, bias = to_dev(L.X), to_dev(L.lam), to_dev(L.L1), to_dev(L.L2), to_dev(L.bias)
     qa_o, sa_o, xh = oracle.mx_quantize_act(L.X, L.lam)
     qa, sa, xl1 = bdt.mx_quantize_act_down(X, lam, L1)
-    assert np.array_equal(qa.cpu().numpy(), qa_o)
+    assert np.array_equal(from_pairs(qa, M), qa_o)
     assert np.array_equal(from_block_major(sa, M), sa_o)
     xl1_o = oracle.down_proj(xh, L.L1)
     assert np.all(np.abs(xl1.cpu().numpy().astype(np.float64) - xl1_o) <= xl1_bound(xh, L.L1))
