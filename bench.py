@@ -558,7 +558,7 @@ def bench_mlp_chain(args):
     n_k = max(args.steps, 20)
     # the fused up GEMM alone (its inputs from one K1 per set)
     carved = [bdt.quantize_act_down(st["X"], st["U"]["lam"], st["U"]["L1"]) for st in sets]
-    outs = [(torch.empty((M, Nh // 2), dtype=torch.uint8, device=dev),
+    outs = [(torch.empty((bdt.pair_rows(M), Nh), dtype=torch.uint8, device=dev),
              torch.empty((M, Nh // 64), dtype=torch.float32, device=dev),
              torch.empty((M, rd), dtype=torch.float32, device=dev)) for _ in sets]
     ws_g = bdt.svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, Nh, rd)

@@ -54,10 +54,21 @@ def _rank(L: Optional[torch.Tensor], dim: int) -> int:
     return 0 if L is None or L.numel() == 0 else int(L.shape[dim])
 
 
+def pair_rows(rows: int) -> int:
+    """Leading dimension of packed 4-bit codes stored in row pairs: ceil(rows / 2)."""
+    return (rows + 1) // 2
+
+
+def _codes_of(q: torch.Tensor, rows: int, K: int, what: str) -> None:
+    if tuple(q.shape) != (pair_rows(rows), K) or q.dtype != torch.uint8:
+        raise ValueError("%s: expected uint8 row-pair codes of shape %s, got %s %s"
+                         % (what, (pair_rows(rows), K), q.dtype, tuple(q.shape)))
+
+
 def pack_weights(R: torch.Tensor):
-    """Residual fp32 [N, K] -> (qw uint8 [N, K/2], sw fp32 [N, K/64])."""
+    """Residual fp32 [N, K] -> (qw uint8 [ceil(N/2), K] row pairs, sw fp32 [N, K/64])."""
     N, K = R.shape
-    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=R.device)
+    qw = torch.empty((pair_rows(N), K), dtype=torch.uint8, device=R.device)
     sw = torch.empty((N, K // GROUP), dtype=torch.float32, device=R.device)
     svdq_pack_weights(R, N, K, qw, sw)
     return qw, sw
@@ -88,11 +99,12 @@ def awq_linear(X: torch.Tensor, packed: torch.Tensor, N: int, bias=None) -> torc
 
 
 def quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Tensor]):
-    """X bf16 [M, K] -> (qa uint8 [M, K/2], sa fp32 [M, K/64], xl1 fp32 [M, r] or None)."""
+    """X bf16 [M, K] -> (qa uint8 [ceil(M/2), K] row pairs, sa fp32 [M, K/64], xl1 fp32 [M, r]
+    or None)."""
     M, K = X.shape
     r = _rank(L1, 1)
     dev = X.device
-    qa = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    qa = torch.empty((pair_rows(M), K), dtype=torch.uint8, device=dev)
     sa = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
     xl1 = torch.empty((M, r), dtype=torch.float32, device=dev) if r > 0 else None
     ws_bytes = svdq_quantize_act_down_workspace_bytes(M, K, r)
@@ -104,9 +116,9 @@ def quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Ten
 
 def w4a4_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act: int = ACT_NONE) -> torch.Tensor:
     """The W4A4 GEMM with the low-rank up-projection, bias and act -> Y bf16 [M, N]."""
-    M = qa.shape[0]
-    N = qw.shape[0]
-    K = qa.shape[1] * 2
+    M, N, K = sa.shape[0], sw.shape[0], qa.shape[1]
+    _codes_of(qa, M, K, "qa")
+    _codes_of(qw, N, K, "qw")
     r = _rank(L2, 0)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
     svdq_w4a4_lr_gemm(qa, sa, qw, sw, xl1 if r > 0 else None, _bits(L2) if r > 0 else None,
@@ -118,7 +130,8 @@ def linear(X, lam, L1, qw, sw, L2, bias, act: int = ACT_NONE,
            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer (svdq_linear) -> Y bf16 [M, N]."""
     M, K = X.shape
-    N = qw.shape[0]
+    N = sw.shape[0]
+    _codes_of(qw, N, K, "qw")
     r = _rank(L1, 1)
     need = svdq_linear_workspace_bytes(M, K, r)
     if workspace is None or workspace.numel() < need:
@@ -138,7 +151,9 @@ def _qkv_out(M, heads, head_dim, seq, device):
 def w4a4_lr_gemm_qkv(qa, sa, qw, sw, xl1, L2, bias, heads: int, head_dim: int, seq: int,
                      gamma_q, gamma_k, eps: float, cos_t, sin_t):
     """The GEMM with the fused QKV epilogue -> (Q, K, V) bf16 [M/seq, heads, seq, head_dim]."""
-    M, K = qa.shape[0], qa.shape[1] * 2
+    M, K = sa.shape[0], qa.shape[1]
+    _codes_of(qa, M, K, "qa")
+    _codes_of(qw, sw.shape[0], K, "qw")
     r = _rank(L2, 0)
     Q, Kt, V = _qkv_out(M, heads, head_dim, seq, qa.device)
     epi = qkv_epilogue(heads, head_dim, seq, _bits(gamma_q), _bits(gamma_k), eps, cos_t, sin_t,
@@ -152,6 +167,7 @@ def linear_qkv(X, lam, L1, qw, sw, L2, bias, heads: int, head_dim: int, seq: int
                gamma_k, eps: float, cos_t, sin_t, workspace: Optional[torch.Tensor] = None):
     """The whole fused QKV layer (svdq_linear_qkv) -> (Q, K, V) bf16 [M/seq, heads, seq, D]."""
     M, K = X.shape
+    _codes_of(qw, sw.shape[0], K, "qw")
     r = _rank(L1, 1)
     need = svdq_linear_workspace_bytes(M, K, r)
     if workspace is None or workspace.numel() < need:
@@ -166,12 +182,13 @@ def linear_qkv(X, lam, L1, qw, sw, L2, bias, heads: int, head_dim: int, seq: int
 
 def w4a4_lr_gemm_quant_down(qa, sa, qw, sw, xl1, L2, bias, act, lambda_next, L1_next):
     """The GEMM whose output feeds the next layer -> that layer's (qa, sa, xl1)."""
-    M, K = qa.shape[0], qa.shape[1] * 2
-    N = qw.shape[0]
+    M, N, K = sa.shape[0], sw.shape[0], qa.shape[1]
+    _codes_of(qa, M, K, "qa")
+    _codes_of(qw, N, K, "qw")
     r = _rank(L2, 0)
     rn = _rank(L1_next, 1)
     dev = qa.device
-    qa_n = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    qa_n = torch.empty((pair_rows(M), N), dtype=torch.uint8, device=dev)
     sa_n = torch.empty((M, N // GROUP), dtype=torch.float32, device=dev)
     xl1_n = torch.empty((M, rn), dtype=torch.float32, device=dev) if rn > 0 else None
     need = svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, rn)
@@ -187,7 +204,9 @@ def mlp(X, up: dict, down: dict, act: int = ACT_GELU,
         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = down(act(up(X))) through svdq_mlp; up / down: dicts with lam, L1, qw, sw, L2, bias."""
     M, K = X.shape
-    Nh = up["qw"].shape[0]
+    Nh = up["sw"].shape[0]
+    _codes_of(up["qw"], Nh, K, "up qw")
+    _codes_of(down["qw"], K, Nh, "down qw")
     ru, rd = _rank(up["L1"], 1), _rank(down["L1"], 1)
     need = svdq_mlp_workspace_bytes(M, K, Nh, ru, rd)
     if workspace is None or workspace.numel() < need:
@@ -201,9 +220,12 @@ def mlp(X, up: dict, down: dict, act: int = ACT_GELU,
     return Y
 
 
-def group_sums(qa, qw, m0: int, n0: int, tm: int, tn: int) -> torch.Tensor:
-    """Exact per-group int32 sums of a block (test hook) -> int32 [tm, tn, K/64]."""
-    M, N, K = qa.shape[0], qw.shape[0], qa.shape[1] * 2
+def group_sums(qa, qw, M: int, N: int, m0: int, n0: int, tm: int, tn: int) -> torch.Tensor:
+    """Exact per-group int32 sums of a block (test hook) -> int32 [tm, tn, K/64]; qa, qw
+    row-pair codes of M and N rows."""
+    K = qa.shape[1]
+    _codes_of(qa, M, K, "qa")
+    _codes_of(qw, N, K, "qw")
     S = torch.empty((tm, tn, K // GROUP), dtype=torch.int32, device=qa.device)
     svdq_debug_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S)
     return S
@@ -229,11 +251,11 @@ class SVDQLinear:
 
     @property
     def in_features(self) -> int:
-        return self.qw.shape[1] * 2
+        return self.qw.shape[1]
 
     @property
     def out_features(self) -> int:
-        return self.qw.shape[0]
+        return self.sw.shape[0]
 
     def __call__(self, X: torch.Tensor) -> torch.Tensor:
         M, K = X.shape

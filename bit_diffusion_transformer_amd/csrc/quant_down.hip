@@ -37,8 +37,7 @@ constexpr int K1_ROWS = 64;
 template <int NT> struct K1Chunk { static constexpr int KC = NT <= 2 ? 8 : (NT <= 4 ? 4 : 2); };
 
 // MX: the 4-bit float (MXFP4) variant -- the same smoothing and
-// down-projection, the MX quantizer per 32-value block, codes in row pairs
-// (mx_code_offset), E8M0 scale bytes block-major in sa
+// down-projection, the MX quantizer per 32-value block, E8M0 scale bytes block-major in sa
 // ([K/32][mx_scale_rows(M)]).
 template <int NT, bool MX = false>
 __global__ void __launch_bounds__(256)
@@ -146,7 +145,7 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
             if constexpr (MX) {
                 const uint32_t sb = mx_quantize16(v, packed);
                 if (row_ok) {
-                    *reinterpret_cast<u32x2 *>(qa + mx_code_offset(row, K, g * (kGroup / 2) + 8 * ks)) =
+                    *reinterpret_cast<u32x2 *>(qa + code_offset(row, K / 2, g * (kGroup / 2) + 8 * ks)) =
                         packed;
                     if ((ks & 1) == 0)
                         static_cast<uint8_t *>(sa)[(2 * g + (ks >> 1)) * mx_scale_rows(M) + row] =
@@ -155,7 +154,7 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
             } else {
                 const float s = quantize_group16(v, packed);
                 if (row_ok) {
-                    *reinterpret_cast<u32x2 *>(qa + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
+                    *reinterpret_cast<u32x2 *>(qa + code_offset(row, K / 2, g * (kGroup / 2) + 8 * ks)) = packed;
                     if (ks == 0) static_cast<float *>(sa)[row * G + g] = s;
                 }
             }
@@ -239,7 +238,7 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
         if constexpr (MX) {
             const uint32_t sb = mx_quantize16(v, packed);
             if (row_ok) {
-                *reinterpret_cast<u32x2 *>(qw + mx_code_offset(row, K, g * (kGroup / 2) + 8 * ks)) = packed;
+                *reinterpret_cast<u32x2 *>(qw + code_offset(row, K / 2, g * (kGroup / 2) + 8 * ks)) = packed;
                 if ((ks & 1) == 0)
                     static_cast<uint8_t *>(sw)[(2 * g + (ks >> 1)) * mx_scale_rows(N) + row] =
                         (uint8_t)sb;
@@ -247,7 +246,7 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
         } else {
             const float s = quantize_group16(v, packed);
             if (row_ok) {
-                *reinterpret_cast<u32x2 *>(qw + row * (K / 2) + g * (kGroup / 2) + 8 * ks) = packed;
+                *reinterpret_cast<u32x2 *>(qw + code_offset(row, K / 2, g * (kGroup / 2) + 8 * ks)) = packed;
                 if (ks == 0) static_cast<float *>(sw)[row * G + g] = s;
             }
         }

@@ -210,7 +210,7 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r, bool m
     char *p = static_cast<char *>(base);
     size_t off = 0;
     w.qa = reinterpret_cast<uint8_t *>(p + off);
-    off += align256(mx ? (size_t)((M + 1) / 2) * (size_t)K : (size_t)M * (size_t)(K / 2));
+    off += align256((size_t)((M + 1) / 2) * (size_t)K);   // row-pair codes
     w.sa = reinterpret_cast<float *>(p + off);
     off += align256(mx ? (size_t)svdq::mx_scale_rows(M) * (size_t)(K / 32)
                        : (size_t)M * (size_t)(K / SVDQ_GROUP) * 4);
@@ -288,7 +288,7 @@ MlpWorkspace carve_mlp(void *base, int64_t M, int64_t K, int64_t Nh, int32_t r_u
     char *p = static_cast<char *>(base);
     size_t off = w.up.bytes;
     w.qa_h = reinterpret_cast<uint8_t *>(p + off);
-    off += align256((size_t)M * (size_t)(Nh / 2));
+    off += align256((size_t)((M + 1) / 2) * (size_t)Nh);   // row-pair codes
     w.sa_h = reinterpret_cast<float *>(p + off);
     off += align256((size_t)M * (size_t)(Nh / SVDQ_GROUP) * 4);
     w.xl1_h = r_down > 0 ? reinterpret_cast<float *>(p + off) : nullptr;

@@ -14,13 +14,17 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // multiple of 16 (the bytes past `rows` are padding, never read into a result).
 __host__ __device__ inline int64_t mx_scale_rows(int64_t rows) { return (rows + 15) & ~(int64_t)15; }
 
-// MXFP4 codes are stored in row pairs: for rows 2p and 2p + 1, each 64-byte
-// chunk of a row's K/2 bytes (128 codes, one GEMM stage) is followed by the
-// same chunk of the other row, so one 128-byte line holds a stage of both
-// rows ([ceil(rows/2)][K] bytes; an odd count's last pair has an unwritten
-// half).  Byte b of row `row`:
-__host__ __device__ inline int64_t mx_code_offset(int64_t row, int64_t K, int64_t b) {
-    return (row >> 1) * K + (b >> 6) * 128 + (row & 1) * 64 + (b & 63);
+// Packed 4-bit codes (INT4 and MXFP4 alike) are stored in row pairs: for
+// rows 2p and 2p + 1, each 64-byte chunk of a row's kb = K/2 bytes (128
+// codes, one GEMM stage) is followed by the same chunk of the other row, so
+// one 128-byte line holds a stage of both rows.  When kb is not a multiple
+// of 64 (INT4 with an odd group count) the last chunk is 32 bytes wide and
+// the pair interleaves in 32-byte halves there.  [ceil(rows/2)][2 kb] bytes;
+// an odd count's last pair has an unwritten half.  Byte b of row `row`:
+__host__ __device__ inline int64_t code_offset(int64_t row, int64_t kb, int64_t b) {
+    const int64_t c = b >> 6;
+    const int64_t w = kb - (c << 6) < 64 ? kb - (c << 6) : 64;
+    return (row >> 1) * 2 * kb + (c << 7) + (row & 1) * w + (b & 63);
 }
 
 // svdq_quantize_act_down splits K into chunks of kc groups (one workgroup per

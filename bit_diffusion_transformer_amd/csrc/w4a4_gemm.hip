@@ -62,8 +62,8 @@ group_sums_kernel(const uint8_t *__restrict__ qa, const uint8_t *__restrict__ qw
     if (n >= N) n = N - 1;
     if (m >= M) m = M - 1;
     for (int64_t g = 0; g < G; ++g) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(qw + n * (K / 2) + g * 32 + 16 * ks2);
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(qa + m * (K / 2) + g * 32 + 16 * ks2);
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(qw + code_offset(n, K / 2, g * 32 + 16 * ks2));
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(qa + code_offset(m, K / 2, g * 32 + 16 * ks2));
         const f32x16 D = mfma_codes_32x32x64(codes_to_fp8(a), codes_to_fp8(b));
 #pragma unroll
         for (int i = 0; i < 16; ++i) {

@@ -51,6 +51,7 @@ namespace {
 // round, so that they spread over four times as many workgroups.
 constexpr int GC = 2;              // K groups per stage
 constexpr int ROWP = GC * 32;      // packed bytes of one row per stage (4 x 16)
+constexpr int PAIRP = 2 * ROWP;    // global bytes of one row pair per stage (row-pair codes)
 constexpr int NBUF = 4;            // stages in the LDS ring
 constexpr int NTHR = 256;          // 4 waves
 constexpr int TILE = 128;          // the tile grid (a quarter tile is a quadrant of one)
@@ -108,9 +109,10 @@ __device__ __forceinline__ void raster(int64_t id, int64_t nbm, int64_t nbn, int
 // row 32 j + l / 2, group l % 2 (WB = 2: block j = w of both operands;
 // WB = 1: waves 0, 1 the weight rows, waves 2, 3 the token rows).  Rows past
 // the matrix re-read its last row (never stored); a stage that holds only
-// one group (odd group count) re-reads that group for the second.  Offsets
-// are unsigned bytes from the tile's first row, so each copy is a uniform
-// (scalar) base plus a per-lane 32-bit offset.
+// one group (odd group count) re-reads that group for the second.  Codes are
+// in row pairs (code_offset); offsets are unsigned bytes from the tile's
+// first pair, so each copy is a uniform (scalar) base plus a per-lane 32-bit
+// offset.
 template <int WB>
 struct CopyPlan {
     uint32_t a_off[WB], b_off[WB];   // code transfers
@@ -129,8 +131,8 @@ __device__ __forceinline__ void issue_copies(uint8_t *st, const Operands &op, in
                                              const uint32_t (&ao)[WB], const uint32_t (&bo)[WB],
                                              const uint32_t (&so)[2]) {
     using C = Cfg<WB>;
-    const uint8_t *qws = op.qw0 + c * ROWP;
-    const uint8_t *qas = op.qa0 + c * ROWP;
+    const uint8_t *qws = op.qw0 + c * PAIRP;
+    const uint8_t *qas = op.qa0 + c * PAIRP;
 #pragma unroll
     for (int i = 0; i < WB; ++i) {
         const int row = 16 * WB * wave + 16 * i;
@@ -383,8 +385,8 @@ template <int WB>
 __device__ __forceinline__ void issue_stage_mx(uint8_t *st, const CopyPlan<WB> &cp,
                                                const Operands &op, const MxScaleSrc &ss, int c) {
     using C = Cfg<WB>;
-    const uint8_t *qws = op.qw0 + c * 128;   // row pairs: a stage is 128 bytes per pair
-    const uint8_t *qas = op.qa0 + c * 128;   // row pairs: a stage is 128 bytes per pair
+    const uint8_t *qws = op.qw0 + c * PAIRP;
+    const uint8_t *qas = op.qa0 + c * PAIRP;
     const int wave = cp.wave;
 #pragma unroll
     for (int i = 0; i < WB; ++i) {
@@ -739,8 +741,8 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
                     const uint32_t w = wsm[bi][q];
                     const uint32_t first = (other >> (4 * bi + (ks2 ? q : (q ^ 1)))) & 1u;
                     const uint32_t st = (w & 0x7777u) | ((w << 4) & 0x8880u) | (first << 3);
-                    *reinterpret_cast<uint16_t *>(ma.qa + m * kb + (nw + 32 * bi + 8 * q + 4 * ks2) / 2) =
-                        (uint16_t)st;
+                    *reinterpret_cast<uint16_t *>(
+                        ma.qa + code_offset(m, kb, (nw + 32 * bi + 8 * q + 4 * ks2) / 2)) = (uint16_t)st;
                 }
             }
             if (ks2 == 0) ma.sa[m * G + nw / kGroup] = s;
@@ -866,15 +868,12 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
         const int row = 16 * WB * wave + 16 * i + (lane >> 2);
         const int seg = (lane & 3) ^ swz(row);     // global segment landing in this lane's slot
         const int ra = min(row, nlast), rb = min(row, mlast);
-        if constexpr (MXF) {   // row pairs (mx_code_offset): chunk of rows 2p, 2p + 1 in one line
-            cp.a_off[i] = (uint32_t)((ra >> 1) * 2 * kb + 64 * (ra & 1) + 16 * seg);
-            cp.b_off[i] = (uint32_t)((rb >> 1) * 2 * kb + 64 * (rb & 1) + 16 * seg);
-        } else {
-            cp.a_off[i] = (uint32_t)(ra * kb + 16 * seg);
-            cp.b_off[i] = (uint32_t)(rb * kb + 16 * seg);
-        }
-        cp.a_tail[i] = (uint32_t)(ra * kb + 16 * (seg & 1));
-        cp.b_tail[i] = (uint32_t)(rb * kb + 16 * (seg & 1));
+        // row pairs (code_offset): a stage's chunk of rows 2p, 2p + 1 in one
+        // 128-byte line; a one-group last stage is 32 bytes per row
+        cp.a_off[i] = (uint32_t)((ra >> 1) * 2 * kb + 64 * (ra & 1) + 16 * seg);
+        cp.b_off[i] = (uint32_t)((rb >> 1) * 2 * kb + 64 * (rb & 1) + 16 * seg);
+        cp.a_tail[i] = (uint32_t)((ra >> 1) * 2 * kb + 32 * (ra & 1) + 16 * (seg & 1));
+        cp.b_tail[i] = (uint32_t)((rb >> 1) * 2 * kb + 32 * (rb & 1) + 16 * (seg & 1));
     }
     MxScaleSrc ss{};
     if constexpr (MXF) {

@@ -32,13 +32,21 @@
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are
  *     row-major and contiguous.  Pointers marked "device" must point to
  *     memory of the current HIP device and be 16-byte aligned.
- *   - Packed INT4 codes (qa, qw): [rows, K/2] bytes, two per byte; in each
- *     block of 16 consecutive codes of a row (8 bytes), code e sits in
- *     nibble e (element 2j in the low nibble of byte j) and that nibble
- *     holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 16) in bit 3
- *     (zero is stored without sign).  With this layout the GEMM turns the
- *     codes into FP8 (E4M3) operands of the matrix unit with three bit
- *     operations per 8 codes.  Scales: fp32 [rows, K/64].
+ *   - Packed INT4 codes (qa, qw): kb = K/2 bytes per row, two codes per
+ *     byte; in each block of 16 consecutive codes of a row (8 bytes), code
+ *     e sits in nibble e (element 2j in the low nibble of byte j) and that
+ *     nibble holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 16) in
+ *     bit 3 (zero is stored without sign).  With this layout the GEMM turns
+ *     the codes into FP8 (E4M3) operands of the matrix unit with three bit
+ *     operations per 8 codes.  Rows are stored in pairs, [ceil(rows/2),
+ *     2 kb] = [ceil(rows/2), K] bytes: each 64-byte chunk of a row (128
+ *     codes, one stage of the GEMM) is followed by the same chunk of its
+ *     pair partner, so one 128-byte line holds a stage of both rows; when
+ *     kb is not a multiple of 64 (an odd group count) the last chunk is 32
+ *     bytes and the pair interleaves in 32-byte halves there.  Byte b of row
+ *     i sits at (i/2) 2 kb + (b/64) 128 + (i%2) w + b%64, with w = 64, or
+ *     kb - 64 (b/64) in a shorter last chunk.  An odd row count's last pair
+ *     has an unwritten half.  Scales: fp32 [rows, K/64], row-major.
  *   - The caller owns and allocates every buffer.  The library allocates
  *     nothing and keeps no state except a per-device architecture check.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
@@ -96,7 +104,7 @@ const char *svdq_last_error(void);
  * overview; the offline toolchain's "quantize, pack" steps in the blog's
  * section "Quantize your own model").
  *   R   device fp32 [N, K]  residual weight (nn.Linear orientation, out x in)
- *   qw  device u8   [N, K/2] packed 4-bit codes (out)
+ *   qw  device u8   [ceil(N/2), K] packed 4-bit codes, row pairs (out)
  *   sw  device fp32 [N, K/64] group scales (out)
  * Same quantizer as the activations, without smoothing.  N >= 0 (0: no-op),
  * K % 64 == 0, K >= 64.
@@ -118,7 +126,7 @@ size_t svdq_quantize_act_down_workspace_bytes(int64_t M, int64_t K, int32_t r);
  *   X       device bf16 [M, K]   activations
  *   lambda  device fp32 [K]      smoothing factors, finite and > 0
  *   L1      device bf16 [K, r]   low-rank down factor (NULL iff r == 0)
- *   qa      device u8   [M, K/2] packed codes of X diag(lambda)^-1 (out)
+ *   qa      device u8   [ceil(M/2), K] packed codes of X diag(lambda)^-1 (out)
  *   sa      device fp32 [M, K/64] group scales (out)
  *   xl1     device fp32 [M, r]   (X diag(lambda)^-1) L1, fp32 (out; NULL iff r == 0)
  *   workspace / ws_bytes  device scratch of at least
@@ -240,7 +248,7 @@ size_t svdq_w4a4_lr_gemm_quant_down_workspace_bytes(int64_t M, int64_t N, int32_
  * the next layer's activation step on Y:
  *   lambda_next  device fp32 [N]          the next layer's smoothing factors
  *   L1_next      device bf16 [N, r_next]  its down-projection (NULL if r_next == 0)
- *   qa_next      device u8   [M, N/2]     its codes (out)
+ *   qa_next      device u8   [ceil(M/2), N] its codes, row pairs (out)
  *   sa_next      device fp32 [M, N/64]    its scales (out)
  *   xl1_next     device fp32 [M, r_next]  its down-projection (out; NULL if r_next == 0)
  *   workspace    device, svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, r_next)
@@ -291,11 +299,9 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
  *     magnitudes above 6 to 6; zero is stored as +0;
  *   - E2M1 codes two per byte, element 2j in the low nibble of byte j of
  *     its row (the scaled matrix instruction takes them as they are); rows
- *     stored in pairs, [ceil(rows/2), K] bytes: byte b of row i sits at
- *     (i / 2) K + (b / 64) 128 + (i % 2) 64 + b % 64, so that each 64-byte
- *     chunk of a row (128 codes) is followed by the same chunk of its pair
- *     partner (one 128-byte line; a stage of the GEMM), and an odd row
- *     count's last pair has an unwritten half; scales u8 block-major, [K/32, P] with
+ *     stored in pairs as the INT4 codes (K % 128 == 0, so every chunk is 64
+ *     bytes): byte b of row i sits at (i / 2) K + (b / 64) 128 + (i % 2) 64
+ *     + b % 64; scales u8 block-major, [K/32, P] with
  *     P = rows rounded up to a multiple of 16: byte [b][i] scales k block b
  *     of row i; bytes [b][rows .. P) are padding, left unwritten and never
  *     read into a result.  (Row-major bytes would cost the GEMM one memory

@@ -20,6 +20,40 @@ def to_dev(a: np.ndarray | None, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
+def to_pairs(p: np.ndarray) -> np.ndarray:
+    """Row-major packed codes [rows, kb] (the oracle's) -> the device's row-pair layout
+    [ceil(rows/2), 2 kb]: each 64-byte chunk of a row followed by the same chunk of its
+    pair partner; a shorter last chunk (kb % 64 == 32) interleaves in 32-byte halves."""
+    rows, kb = p.shape
+    q = np.zeros(((rows + 1) // 2 * 2, kb), np.uint8)
+    q[:rows] = p
+    out = np.zeros(((rows + 1) // 2, 2 * kb), np.uint8)
+    for c0 in range(0, kb, 64):
+        w = min(64, kb - c0)
+        out[:, 2 * c0:2 * c0 + w] = q[0::2, c0:c0 + w]
+        out[:, 2 * c0 + w:2 * c0 + 2 * w] = q[1::2, c0:c0 + w]
+    return out
+
+
+def from_pairs(d, rows: int) -> np.ndarray:
+    """Inverse of to_pairs (the unwritten half of an odd count's last pair dropped)."""
+    d = d.cpu().numpy() if hasattr(d, "cpu") else np.asarray(d)
+    pairs, K = d.shape
+    assert pairs == (rows + 1) // 2, (pairs, rows)
+    kb = K // 2
+    q = np.zeros((2 * pairs, kb), np.uint8)
+    for c0 in range(0, kb, 64):
+        w = min(64, kb - c0)
+        q[0::2, c0:c0 + w] = d[:, 2 * c0:2 * c0 + w]
+        q[1::2, c0:c0 + w] = d[:, 2 * c0 + w:2 * c0 + 2 * w]
+    return q[:rows]
+
+
+def pdev(p: np.ndarray):
+    """Oracle codes -> device row-pair codes."""
+    return to_dev(to_pairs(p))
+
+
 def bf16_host(t: torch.Tensor) -> np.ndarray:
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 

@@ -1,11 +1,14 @@
-"""The packed INT4 code layout (include/svdq.h; the oracle packs the same way) and the
-property the GEMM relies on: one AND gives the E4M3 bytes of the even codes of a
-block of 16 and a funnel shift plus an AND those of the odd codes, each the E4M3
-subnormal code * 2^-9.  Host-side arithmetic only (no GPU)."""
+"""The packed INT4 code layout (include/svdq.h): within a row the oracle and the
+library store the same bytes; the library keeps rows in pairs, which the tests'
+converter maps to and from the oracle's row-major bytes.  Also the property the
+GEMM relies on: one AND gives the E4M3 bytes of the even codes of a block of 16
+and a funnel shift plus an AND those of the odd codes, each the E4M3 subnormal
+code * 2^-9.  Host-side arithmetic only (no GPU)."""
 import numpy as np
 import pytest
 
 import oracle
+from tests.helpers import from_pairs, to_pairs
 
 
 def _pack(codes):
@@ -58,3 +61,30 @@ def test_fp8_operand_form(seed):
     order = [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]
     want = np.concatenate([c[:16][order], c[16:32][order]])
     assert np.array_equal(got, want)
+
+
+def _pair_offset(i, kb, b):
+    """Byte b of row i in the row-pair layout, as include/svdq.h states it."""
+    c = b // 64
+    w = min(64, kb - 64 * c)
+    return (i // 2) * 2 * kb + 128 * c + (i % 2) * w + b % 64
+
+
+@pytest.mark.parametrize("rows,K", [(1, 64), (2, 128), (5, 192), (4, 256), (7, 1088), (3, 3072)])
+def test_row_pair_converter_matches_stated_offsets(rows, K):
+    rng = np.random.default_rng(rows * K)
+    kb = K // 2
+    p = rng.integers(0, 256, size=(rows, kb), dtype=np.uint8)
+    d = to_pairs(p)
+    assert d.shape == ((rows + 1) // 2, K)
+    flat = d.reshape(-1)
+    seen = np.zeros(flat.size, bool)
+    for i in range(rows):
+        for b in range(kb):
+            o = _pair_offset(i, kb, b)
+            assert flat[o] == p[i, b]
+            assert not seen[o]
+            seen[o] = True
+    # every byte of a full pair is used; an odd count leaves its last half unwritten
+    assert seen.sum() == rows * kb
+    assert np.array_equal(from_pairs(d, rows), p)

@@ -11,7 +11,7 @@ import pytest
 import bit_diffusion_transformer_amd as bdt
 import oracle
 from synth import CONFIGS, DIT_CHAIN, make_layer
-from tests.helpers import assert_y_close, bf16_host, to_dev, xl1_bound
+from tests.helpers import assert_y_close, bf16_host, from_pairs, to_dev, xl1_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -28,13 +28,13 @@ def test_full_size_config(name, spec, M):
 
     qw_o, sw_o = oracle.pack_weights(L.R)
     qw, sw = bdt.pack_weights(to_dev(L.R))
-    assert np.array_equal(qw.cpu().numpy(), qw_o)
+    assert np.array_equal(from_pairs(qw, N), qw_o)
     assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_o.view(np.uint32))
 
     X, lam, L1, L2, bias = to_dev(L.X), to_dev(L.lam), to_dev(L.L1), to_dev(L.L2), to_dev(L.bias)
     qa_o, sa_o, xh = oracle.quantize_act(L.X, L.lam)
     qa, sa, xl1 = bdt.quantize_act_down(X, lam, L1)
-    assert np.array_equal(qa.cpu().numpy(), qa_o)
+    assert np.array_equal(from_pairs(qa, M), qa_o)
     assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
     xl1_o = oracle.down_proj(xh, L.L1)
     assert np.all(np.abs(xl1.cpu().numpy().astype(np.float64) - xl1_o) <= xl1_bound(xh, L.L1))
@@ -44,7 +44,7 @@ def test_full_size_config(name, spec, M):
         tm, tn = min(128, M), min(128, N)
         m0 = int(rng.integers(0, M - tm + 1))
         n0 = int(rng.integers(0, N - tn + 1))
-        S = bdt.group_sums(qa, qw, m0, n0, tm, tn).cpu().numpy()
+        S = bdt.group_sums(qa, qw, M, N, m0, n0, tm, tn).cpu().numpy()
         assert np.array_equal(S, oracle.group_sums(qa_o, qw_o, K, m0, n0, tm, tn))
 
     Y = bdt.linear(X, lam, L1, qw, sw, L2, bias, act)

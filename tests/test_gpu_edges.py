@@ -10,7 +10,7 @@ import bit_diffusion_transformer_amd as bdt
 import oracle
 from bit_diffusion_transformer_amd import _binding
 from synth import LayerSpec, f32_to_bf16_bits, make_layer
-from tests.helpers import assert_y_close, bf16_host, to_dev
+from tests.helpers import assert_y_close, bf16_host, from_pairs, pdev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def test_empty_batch():
     L = _layer()
     X = to_dev(L.X)[:0]
     qa, sa, xl1 = bdt.quantize_act_down(X, to_dev(L.lam), to_dev(L.L1))
-    assert qa.shape == (0, 128) and sa.shape == (0, 4) and xl1.shape == (0, 32)
+    assert qa.shape == (0, 256) and sa.shape == (0, 4) and xl1.shape == (0, 32)
     qw, sw = bdt.pack_weights(to_dev(L.R))
     Y = bdt.linear(X, to_dev(L.lam), to_dev(L.L1), qw, sw, to_dev(L.L2), to_dev(L.bias))
     assert Y.shape == (0, 136)
@@ -42,7 +42,7 @@ def test_zero_and_subnormal_groups_bit_exact():
     lam[200:260] = np.float32(3e38)              # pushes those x / lam into subnormals
     qa_o, sa_o, _ = oracle.quantize_act(X, lam)
     qa, sa, _ = bdt.quantize_act_down(to_dev(X), to_dev(lam), None)
-    assert np.array_equal(qa.cpu().numpy(), qa_o)
+    assert np.array_equal(from_pairs(qa, M), qa_o)
     assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
     assert (sa_o == 0).any() and ((sa_o > 0) & (sa_o < 2.0 ** -126)).any()
     R = (rng.standard_normal((64, K)) * 0.05).astype(np.float32)
@@ -50,7 +50,7 @@ def test_zero_and_subnormal_groups_bit_exact():
     R[4, :64] = np.float32(1e-40)
     qw_o, sw_o = oracle.pack_weights(R)
     qw, sw = bdt.pack_weights(to_dev(R))
-    assert np.array_equal(qw.cpu().numpy(), qw_o)
+    assert np.array_equal(from_pairs(qw, 64), qw_o)
     assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_o.view(np.uint32))
 
 
@@ -62,9 +62,9 @@ def test_all_extreme_codes():
     R = np.where(np.arange(K) % 2 == 0, -0.5, 0.5)[None, :].repeat(N, 0).astype(np.float32)
     qa_o, sa_o, _ = oracle.quantize_act(X, lam)
     qw_o, sw_o = oracle.pack_weights(R)
-    S = bdt.group_sums(to_dev(qa_o), to_dev(qw_o), 0, 0, M, N).cpu().numpy()
+    S = bdt.group_sums(pdev(qa_o), pdev(qw_o), M, N, 0, 0, M, N).cpu().numpy()
     assert np.all(S == -3136)
-    Y = bdt.w4a4_lr_gemm(to_dev(qa_o), to_dev(sa_o), to_dev(qw_o), to_dev(sw_o), None, None, None)
+    Y = bdt.w4a4_lr_gemm(pdev(qa_o), to_dev(sa_o), pdev(qw_o), to_dev(sw_o), None, None, None)
     _, y_or = oracle.gemm_rows(qa_o, sa_o, qw_o, sw_o, None, None, None, 0, K)
     assert_y_close(bf16_host(Y), y_or)
 
@@ -79,7 +79,7 @@ def test_canaries_untouched():
     L = _layer(M=77, K=192, N=264, r=48, act=1, cid=1)
     M, K, N, r = 77, 192, 264, 48
     G = K // 64
-    qa_b, qa = _padded(M * K // 2, torch.uint8, 0xA5)
+    qa_b, qa = _padded(bdt.pair_rows(M) * K, torch.uint8, 0xA5)   # row pairs
     sa_b, sa = _padded(M * G, torch.float32, -123.0)
     x_b, x1 = _padded(M * r, torch.float32, -321.0)
     y_b, y = _padded(M * N, torch.int16, 0x5A5A)
@@ -95,7 +95,11 @@ def test_canaries_untouched():
         h = b.cpu()
         assert torch.all(h[:64] == fill) and torch.all(h[-64:] == fill)
     qa_o, sa_o, _ = oracle.quantize_act(L.X, L.lam)
-    assert np.array_equal(qa.cpu().numpy().reshape(M, K // 2), qa_o)
+    qa_h = qa.cpu().numpy().reshape(bdt.pair_rows(M), K)
+    assert np.array_equal(from_pairs(qa_h, M), qa_o)
+    # M odd: the second half of the last pair is left unwritten (K / 2 = 96 bytes per
+    # row: a 64-byte chunk and a 32-byte last chunk)
+    assert np.all(qa_h[-1, 64:128] == 0xA5) and np.all(qa_h[-1, 160:192] == 0xA5)
 
 
 def test_side_stream_matches_default_stream():

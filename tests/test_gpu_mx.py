@@ -13,7 +13,7 @@ import pytest
 import bit_diffusion_transformer_amd as bdt
 import oracle
 from synth import CONFIGS, LayerSpec, make_layer
-from tests.helpers import assert_y_close, bf16_host, to_dev, xl1_bound
+from tests.helpers import assert_y_close, bf16_host, from_pairs, to_dev, to_pairs, xl1_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -24,26 +24,6 @@ def to_block_major(s: np.ndarray) -> np.ndarray:
     out = np.zeros((s.shape[1], bdt.mx_scale_rows(rows)), np.uint8)
     out[:, :rows] = s.T
     return out
-
-
-def to_pairs(p: np.ndarray) -> np.ndarray:
-    """Oracle codes [rows, K/2] -> the device's row-pair layout [ceil(rows/2), K]: each
-    64-byte chunk of a row followed by the same chunk of its pair partner."""
-    rows, kb = p.shape
-    q = np.zeros(((rows + 1) // 2 * 2, kb), np.uint8)
-    q[:rows] = p
-    return np.ascontiguousarray(
-        q.reshape(-1, 2, kb // 64, 64).transpose(0, 2, 1, 3).reshape(-1, 2 * kb))
-
-
-def from_pairs(d, rows: int) -> np.ndarray:
-    """Inverse of to_pairs (the unwritten half of an odd count's last pair dropped)."""
-    d = d.cpu().numpy() if hasattr(d, "cpu") else d
-    pairs, K = d.shape
-    assert pairs == (rows + 1) // 2
-    kb = K // 2
-    return np.ascontiguousarray(
-        d.reshape(pairs, kb // 64, 2, 64).transpose(0, 2, 1, 3).reshape(2 * pairs, kb)[:rows])
 
 
 def from_block_major(d, rows: int) -> np.ndarray:

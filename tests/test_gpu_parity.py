@@ -12,7 +12,7 @@ import torch
 import bit_diffusion_transformer_amd as bdt
 import oracle
 from synth import LayerSpec, make_layer
-from tests.helpers import (assert_y_close, bf16_host, to_dev, xl1_bound)
+from tests.helpers import assert_y_close, bf16_host, from_pairs, pdev, to_dev, xl1_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -47,14 +47,14 @@ def case(request):
 
 def test_pack_weights_bit_exact(case):
     qw, sw = bdt.pack_weights(to_dev(case["L"].R))
-    assert np.array_equal(qw.cpu().numpy(), case["qw"])
+    assert np.array_equal(from_pairs(qw, case["N"]), case["qw"])
     assert np.array_equal(sw.cpu().numpy().view(np.uint32), case["sw"].view(np.uint32))
 
 
 def test_quantize_act_down(case):
     L, r = case["L"], case["r"]
     qa, sa, xl1 = bdt.quantize_act_down(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None)
-    assert np.array_equal(qa.cpu().numpy(), case["qa"])
+    assert np.array_equal(from_pairs(qa, case["M"]), case["qa"])
     assert np.array_equal(sa.cpu().numpy().view(np.uint32), case["sa"].view(np.uint32))
     if r:
         got = xl1.cpu().numpy().astype(np.float64)
@@ -65,9 +65,9 @@ def test_quantize_act_down(case):
 
 def test_group_sums_bit_exact(case):
     M, N, K = case["M"], case["N"], case["K"]
-    qa, qw = to_dev(case["qa"]), to_dev(case["qw"])
+    qa, qw = pdev(case["qa"]), pdev(case["qw"])
     for (m0, tm, n0, tn) in [(0, M, 0, N), (M // 3, M - M // 3, N // 5, min(37, N - N // 5))]:
-        S = bdt.group_sums(qa, qw, m0, n0, tm, tn).cpu().numpy()
+        S = bdt.group_sums(qa, qw, M, N, m0, n0, tm, tn).cpu().numpy()
         ref = oracle.group_sums(case["qa"], case["qw"], K, m0, n0, tm, tn)
         assert np.array_equal(S, ref)
 
@@ -83,7 +83,7 @@ def test_gemm_stagewise(case, tiles):
     # Same inputs on both sides: the oracle's codes/scales and its xl1 in fp32.
     L, r, K = case["L"], case["r"], case["K"]
     xl1_32 = case["xl1"].astype(np.float32) if r else None
-    Y = bdt.w4a4_lr_gemm(to_dev(case["qa"]), to_dev(case["sa"]), to_dev(case["qw"]),
+    Y = bdt.w4a4_lr_gemm(pdev(case["qa"]), to_dev(case["sa"]), pdev(case["qw"]),
                          to_dev(case["sw"]), to_dev(xl1_32), to_dev(L.L2) if r else None,
                          to_dev(L.bias), case["act"])
     _, y_or = oracle.gemm_rows(case["qa"], case["sa"], case["qw"], case["sw"],
@@ -94,7 +94,7 @@ def test_gemm_stagewise(case, tiles):
 
 def test_linear_end_to_end(case, tiles):
     L, r = case["L"], case["r"]
-    Y = bdt.linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
+    Y = bdt.linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, pdev(case["qw"]),
                    to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
     _, y_or = oracle.linear(L.X, L.lam, L.L1 if r else None, case["qw"], case["sw"],
                             L.L2 if r else None, L.bias, case["act"])
@@ -103,7 +103,7 @@ def test_linear_end_to_end(case, tiles):
 
 def test_linear_is_deterministic(case):
     L, r = case["L"], case["r"]
-    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
+    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, pdev(case["qw"]),
             to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
     y1 = bf16_host(bdt.linear(*args))
     y2 = bf16_host(bdt.linear(*args))
@@ -113,7 +113,7 @@ def test_linear_is_deterministic(case):
 def test_tile_policies_agree_bit_exact(case):
     # Both tile shapes run the same per-output arithmetic in the same order.
     L, r = case["L"], case["r"]
-    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, to_dev(case["qw"]),
+    args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, pdev(case["qw"]),
             to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
     out = []
     try:

@@ -13,7 +13,7 @@ import torch
 import bit_diffusion_transformer_amd as bdt
 import oracle
 from synth import CONFIGS, LayerSpec, make_layer, make_qkv_epilogue
-from tests.helpers import assert_y_close, bf16_f64, bf16_host, qkv_tolerance, to_dev
+from tests.helpers import assert_y_close, bf16_f64, bf16_host, pdev, qkv_tolerance, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +96,7 @@ def _xl1_32(o, r):
 
 def _gemm_qkv(case):
     o, L, epi, r = case["orc"], case["L"], case["epi"], case["r"]
-    return bdt.w4a4_lr_gemm_qkv(to_dev(o["qa"]), to_dev(o["sa"]), to_dev(o["qw"]), to_dev(o["sw"]),
+    return bdt.w4a4_lr_gemm_qkv(pdev(o["qa"]), to_dev(o["sa"]), pdev(o["qw"]), to_dev(o["sw"]),
                                 _xl1_32(o, r), to_dev(L.L2) if r else None,
                                 to_dev(L.bias), epi.heads, epi.head_dim, epi.seq,
                                 **_dev_epi(epi))
@@ -113,7 +113,7 @@ def test_gemm_qkv_matches_oracle(case):
 def test_linear_qkv_matches_oracle(case):
     L, epi, r = case["L"], case["epi"], case["r"]
     Q, Kt, V = bdt.linear_qkv(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None,
-                              to_dev(case["orc"]["qw"]), to_dev(case["orc"]["sw"]),
+                              pdev(case["orc"]["qw"]), to_dev(case["orc"]["sw"]),
                               to_dev(L.L2) if r else None, to_dev(L.bias), epi.heads,
                               epi.head_dim, epi.seq, **_dev_epi(epi))
     _check(Q, Kt, V, case["orc"], epi, np.arange(case["B"] * case["S"]), "linear_qkv")
@@ -123,7 +123,7 @@ def test_v_equals_plain_gemm_columns(case):
     """V comes from the same tile arithmetic as the plain GEMM: bit-identical."""
     o, L, r = case["orc"], case["L"], case["r"]
     _, _, V = _gemm_qkv(case)
-    Y = bdt.w4a4_lr_gemm(to_dev(o["qa"]), to_dev(o["sa"]), to_dev(o["qw"]), to_dev(o["sw"]),
+    Y = bdt.w4a4_lr_gemm(pdev(o["qa"]), to_dev(o["sa"]), pdev(o["qw"]), to_dev(o["sw"]),
                          _xl1_32(o, r), to_dev(L.L2) if r else None, to_dev(L.bias), 0)
     B, S, H, D = case["B"], case["S"], case["H"], case["D"]
     y = bf16_host(Y)[:, 2 * H * D:].reshape(B, S, H, D).transpose(0, 2, 1, 3)
