@@ -37,7 +37,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps before the timed ones; the GPU clocks take ~100-300 steps of this layer (25-70 ms) to settle after idle")
     ap.add_argument("--workload", default="qkv",
                     choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single",
                              "qkv_fused", "mlp_chain", "mx_qkv", "mx_mlp_up", "mx_mlp_down"])
