@@ -179,6 +179,21 @@ __device__ __forceinline__ void wait_stages(int n) {
     }
 }
 
+// The wait inside the K loop before stage s + 1 is published: at most
+// min(ns - 2 - s, 2) younger stages may stay in flight.  The steady state
+// (two) is one uniform branch to a constant count; only the last stages take
+// the general form (s_waitcnt takes an immediate, so a run-time count costs a
+// branch tree).
+template <int L>
+__device__ __forceinline__ void wait_next_stage(int s, int ns) {
+    if (__builtin_expect(s + 3 < ns, 1)) {
+        constexpr int v2 = 2 * L;
+        __builtin_amdgcn_s_waitcnt((v2 & 0xF) | ((v2 >> 4) << 14) | (0x7 << 4));
+    } else {
+        wait_stages<L>(s + 1 < ns ? ns - 2 - s : 0);
+    }
+}
+
 // Workgroup barrier without a memory fence: the copies of the other stages
 // stay in flight across it.  The clobber keeps the compiler from moving LDS
 // accesses across the barrier.
@@ -298,13 +313,16 @@ __device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p) {
 
 // The K loop.  The four ring buffers are separate restrict pointers so that
 // the compiler can tell a read of one stage from the copies still landing in
-// the others (otherwise every LDS read would wait for all copies).
-template <int WB>
+// the others (otherwise every LDS read would wait for all copies).  ODD: the
+// group count is odd, so the last stage holds one group (a compile-time
+// choice, so that an even count carries no per-stage selects for it).
+template <int WB, bool ODD>
 __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__restrict__ b1,
                                        uint8_t *__restrict__ b2, uint8_t *__restrict__ b3,
                                        const CopyPlan<WB> &cp, const ReadPlan &rp,
-                                       const Operands &op, int ns, bool odd,
+                                       const Operands &op, int ns,
                                        f32x16 (&acc)[WB * WB]) {
+    constexpr bool odd = ODD;
     constexpr int L = Cfg<WB>::LOADS;
     // prologue: stages 0..3 in flight, stage 0 visible, group 0 in registers
     issue_stage<WB>(b0, cp, op, 0, odd && ns == 1);
@@ -328,7 +346,7 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
         __builtin_amdgcn_sched_barrier(0);
         group_first<WB>(acc, p, f);
         make_frags<WB>(f, raw, rp.keep_b && !(odd && s == ns - 1));
-        wait_stages<L>(s + 1 < ns ? (ns - 2 - s < 2 ? ns - 2 - s : 2) : 0);
+        wait_next_stage<L>(s, ns);
         barrier();
         if (s + 4 < ns) issue_stage<WB>(cur, cp, op, s + 4, odd && s + 4 == ns - 1);
         // (after the last stage this reads a stale, unused buffer: no branch,
@@ -454,7 +472,7 @@ __device__ __forceinline__ void k_loop_mx(uint8_t *__restrict__ b0, uint8_t *__r
         read_mx<WB>(f1, cur, rp, 1);
         __builtin_amdgcn_sched_barrier(0);
         group_mx<WB>(acc, f0);
-        wait_stages<L>(s + 1 < ns ? (ns - 2 - s < 2 ? ns - 2 - s : 2) : 0);
+        wait_next_stage<L>(s, ns);
         barrier();
         if (s + 4 < ns) issue_stage_mx<WB>(cur, cp, op, ss, s + 4);
         // (after the last stage this reads a stale, unused buffer)
@@ -927,9 +945,12 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
     if constexpr (MXF)
         k_loop_mx<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ss, ns,
                       acc);
+    else if (odd)
+        k_loop<WB, true>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns,
+                         acc);
     else
-        k_loop<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns, odd,
-                   acc);
+        k_loop<WB, false>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns,
+                          acc);
     __syncthreads();
 
     // ---- epilogue: rank-r up-projection on the same tile (bf16 MFMA, the
