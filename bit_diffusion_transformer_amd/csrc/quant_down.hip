@@ -29,7 +29,7 @@ namespace svdq {
 // (16x16x32: lane l holds 8 consecutive k of row l % 16 in k-slot l / 16)
 // against the raw bf16 L1: every product is exact in fp32 and the split keeps
 // about 16 significant bits of x^.  A chunk's result is either xl1 itself
-// (one chunk) or a partial sum that xl1_reduce_kernel adds up in chunk order,
+// (one chunk) or a partial sum that xl1_reduce_kernel adds up in a fixed order,
 // so the result does not depend on scheduling.
 constexpr int K1_ROWS = 64;
 
@@ -197,17 +197,47 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
     }
 }
 
-// xl1 = sum over chunks of the partial sums, added in chunk order.
+// xl1 = the sum of the nc partial sums [nc][total].  A workgroup takes 64
+// consecutive f32x4 of the output and splits the partials into four slices
+// of ceil(nc / 4); wave j adds the partials of slice j in order (eight loads
+// in flight at a time), then the slice sums are added as ((s0 + s1) + s2) +
+// s3.  The order is fixed, so the result does not depend on scheduling.
+constexpr int kReduceCols = 64;   // f32x4 outputs per workgroup
 __global__ void __launch_bounds__(256)
 xl1_reduce_kernel(const float *__restrict__ part, int nc, int64_t total, float *__restrict__ xl1) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= total) return;
-    f32x4 s = *reinterpret_cast<const f32x4 *>(part + i);
-    for (int c = 1; c < nc; ++c) {
-        const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (int64_t)c * total + i);
-        s = f32x4{s.x + p.x, s.y + p.y, s.z + p.z, s.w + p.w};
+    __shared__ f32x4 red[3][kReduceCols];
+    const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int64_t i = ((int64_t)blockIdx.x * kReduceCols + lane) * 4;
+    const bool ok = i < total;
+    const int per = (nc + 3) / 4;
+    const int c0 = j * per < nc ? j * per : nc;
+    const int c1 = c0 + per < nc ? c0 + per : nc;
+    f32x4 s{0.0f, 0.0f, 0.0f, 0.0f};
+    if (ok) {
+        int c = c0;
+        for (; c + 8 <= c1; c += 8) {
+            f32x4 p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                p[e] = *reinterpret_cast<const f32x4 *>(part + (int64_t)(c + e) * total + i);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = f32x4{s.x + p[e].x, s.y + p[e].y, s.z + p[e].z, s.w + p[e].w};
+        }
+        for (; c < c1; ++c) {
+            const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (int64_t)c * total + i);
+            s = f32x4{s.x + p.x, s.y + p.y, s.z + p.z, s.w + p.w};
+        }
     }
-    *reinterpret_cast<f32x4 *>(xl1 + i) = s;
+    if (j > 0) red[j - 1][lane] = s;
+    __syncthreads();
+    if (j == 0 && ok) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const f32x4 p = red[q][lane];
+            s = f32x4{s.x + p.x, s.y + p.y, s.z + p.z, s.w + p.w};
+        }
+        *reinterpret_cast<f32x4 *>(xl1 + i) = s;
+    }
 }
 
 // ------------------------------------------------------------------ pack
@@ -280,7 +310,7 @@ hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint1
 #undef SVDQ_K1
     if (partial) {
         const int64_t total = M * (int64_t)r;
-        const unsigned rblocks = (unsigned)((total / 4 + 255) / 256);
+        const unsigned rblocks = (unsigned)((total / 4 + kReduceCols - 1) / kReduceCols);
         xl1_reduce_kernel<<<rblocks, 256, 0, stream>>>(ws.part, nc, total, xl1);
     }
     return hipGetLastError();
@@ -288,7 +318,7 @@ hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint1
 
 hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl1,
                              hipStream_t stream) {
-    const unsigned rblocks = (unsigned)((total / 4 + 255) / 256);
+    const unsigned rblocks = (unsigned)((total / 4 + kReduceCols - 1) / kReduceCols);
     xl1_reduce_kernel<<<rblocks, 256, 0, stream>>>(part, nc, total, xl1);
     return hipGetLastError();
 }

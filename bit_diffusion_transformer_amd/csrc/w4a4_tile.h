@@ -671,7 +671,7 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
 //   on v_mfma_f32_32x32x16_bf16 (rows: the lane's tokens, which is the
 //   operand layout the tile already has) against L1^T staged in LDS; the two
 //   column-half waves add their partials in LDS in a fixed order and the sum
-//   goes to the partial buffer [N/128][M][rn], reduced in column order later.
+//   goes to the partial buffer [N/128][M][rn], reduced in a fixed order later.
 template <int WB>
 __device__ __forceinline__ void
 mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma, int act,
