@@ -191,9 +191,15 @@ __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &p
 // e = clamp(floor(log2 max|v|) - 2, -127, 127) (v_frexp_exp gives
 // floor(log2) + 1 for normal and subnormal values), stored as the E8M0 byte
 // e + 127 (0 for an all-zero block); each value becomes the E2M1 number
-// nearest to v / X (v_ldexp: exact), ties to the even code, saturating at 6,
-// a zero magnitude as code 0.  The lane's 16 codes are packed element j in
-// nibble j of packed (element 2j in the low nibble of byte j).
+// nearest to v / X, ties to the even code, saturating at 6, a zero magnitude
+// as code 0.  y = v / X is formed exactly (v_ldexp) and rounded by the
+// hardware conversion v_cvt_scalef32_pk_fp4_f32 with scale 1: over every
+// fp32 |y| <= 8 (every y here, since |v| / X < 8) it gives the same codes as
+// rounding to nearest, ties to even, saturating at 6, except that a negative
+// value that rounds to zero comes out as -0 (code 8), which is cleared
+// afterwards.  Finite inputs only (a NaN gets a nonzero code).  The lane's 16 codes are
+// packed element j in nibble j of packed (element 2j in the low nibble of
+// byte j).
 __device__ __forceinline__ uint32_t mx_quantize16(const float (&v)[16], u32x2 &packed) {
     float amax = 0.0f;
 #pragma unroll
@@ -206,20 +212,24 @@ __device__ __forceinline__ uint32_t mx_quantize16(const float (&v)[16], u32x2 &p
     int e = __builtin_amdgcn_frexp_expf(amax) - 3;
     e = e < -127 ? -127 : (e > 127 ? 127 : e);
     const bool zero = !(amax > 0.0f);
-    uint32_t w0 = 0, w1 = 0;
+    uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float y = __builtin_amdgcn_ldexpf(v[j], -e);
-        const float m = fabsf(y);
-        uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
-                     (m >= 3.5f) + (m > 5.0f);
-        if (c != 0 && y < 0.0f) c |= 8u;
-        if (zero) c = 0;
-        if (j < 8) w0 |= c << (4 * j);
-        else w1 |= c << (4 * (j - 8));
+    for (int h = 0; h < 2; ++h) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_ldexpf(v[8 * h + j], -e);
+        // values 2b, 2b + 1 -> byte b (low, high nibble); the byte index is an immediate
+        w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[0], y[1], 1.0f, 0);
+        w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[2], y[3], 1.0f, 1);
+        w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[4], y[5], 1.0f, 2);
+        w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], y[6], y[7], 1.0f, 3);
+        // -0 (sign without magnitude) -> +0: a nibble keeps its sign bit
+        // only when its magnitude is not zero (m + 7 reaches bit 3 iff m > 0)
+        const uint32_t mag = w[h] & 0x77777777u;
+        w[h] = mag | (w[h] & (mag + 0x77777777u) & 0x88888888u);
     }
-    packed.x = w0;
-    packed.y = w1;
+    packed.x = w[0];
+    packed.y = w[1];
     return zero ? 0u : (uint32_t)(e + 127);
 }
 

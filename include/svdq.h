@@ -296,7 +296,8 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
  *     [-127, 127]; an all-zero block gets the byte 0 and zero codes;
  *   - each value becomes the E2M1 number (magnitudes 0, 0.5, 1, 1.5, 2, 3,
  *     4, 6; sign in bit 3) nearest to v / 2^e, ties to the even code,
- *     magnitudes above 6 to 6; zero is stored as +0;
+ *     magnitudes above 6 to 6; zero is stored as +0 (inputs must be
+ *     finite: a NaN or an infinity gives unspecified codes and scales);
  *   - E2M1 codes two per byte, element 2j in the low nibble of byte j of
  *     its row (the scaled matrix instruction takes them as they are); rows
  *     stored in pairs as the INT4 codes (K % 128 == 0, so every chunk is 64
