@@ -507,6 +507,15 @@ namespace {
 // caller's (cos, sin) of position s = m mod S.  V is only re-laid out.  The
 // results go to [B, H, S, D] through an LDS staging of the tile, as 16-byte
 // writes of eight consecutive d.
+// LDS use of the QKV epilogue besides the output staging: the per-wave
+// (cos, sin) regrouping areas (4 waves x 64 tokens x QKV_TP floats, inside
+// the L2^T region) and the D = 128 sum-of-squares exchange (past the output
+// staging).
+constexpr int QKV_TP = 34;                                  // floats per token row
+constexpr int QKV_XS_OFF = 2 * 128 * (SVDQ_MAX_RANK_DEV + 8) * 2;
+static_assert(4 * 64 * QKV_TP * 4 <= 128 * (SVDQ_MAX_RANK_DEV + 8) * 2, "regrouping fits");
+static_assert(QKV_XS_OFF + 2 * 2 * 2 * 32 * 4 <= (int)sizeof(Smem<2>), "exchange fits");
+
 template <int WB>
 __device__ __forceinline__ void
 qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk,
@@ -529,15 +538,6 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
             acc[t][4 * q + 2] += bf16_lo(b2.y);
             acc[t][4 * q + 3] += bf16_hi(b2.y);
         }
-    }
-    // sequence position of the lane's token in each column block bj (rows
-    // past M take the last token's; they are never stored)
-    int64_t spos[WB];
-#pragma unroll
-    for (int bj = 0; bj < WB; ++bj) {
-        const int64_t m = m0 + wm * 32 * WB + 32 * bj + r32;
-        const int64_t mc = m < M ? m : M - 1;
-        spos[bj] = mc - (mc / S) * S;
     }
     // The tile goes out through LDS (as the plain store): staged in [m][n]
     // order past the L2^T rows, then written as 16-byte segments of 8
@@ -568,6 +568,28 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
             }
         }
     } else if constexpr (WB == 2) {   // quarter tiles are only ever V tiles (a head needs the full tile width)
+    // The wave's (cos, sin) rows: its 64 tokens (m0 + 64 wm + tt) and its 32
+    // pairs, starting at pair pb of the head, one 128-byte line per token and
+    // table.  They are fetched as whole lines (lane l: token 8 j + l / 8,
+    // pairs 4 (l % 8) .. + 3) and regrouped through LDS, instead of 8-byte
+    // gathers that touch 32 lines per instruction.  Positions past M stay in
+    // the table (s = m mod S); their rows are never stored.
+    const int lane = 32 * ks2 + r32;
+    const int half = D / 2;
+    const int pb = (int)(((nsec + wn * 32 * WB) % D) / 2);
+    const int64_t tok0 = m0 + wm * 32 * WB;
+    u32x4 tc[8], tsn[8];
+    {
+        int64_t sp = (tok0 + (lane >> 3)) % S;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t at = sp * half + pb + 4 * (lane & 7);
+            tc[j] = *reinterpret_cast<const u32x4 *>(qk.cos_t + at);
+            tsn[j] = *reinterpret_cast<const u32x4 *>(qk.sin_t + at);
+            sp += 8;
+            if (sp >= S) sp = S >= 8 ? sp - S : sp % S;
+        }
+    }
     // sum of squares of each token over this wave's columns (and the partner
     // lane l ^ 32, which holds the other half of every 8-column group)
     float ss[WB];
@@ -582,9 +604,10 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
                                                         false, false);
         ss[bj] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
     }
+    __syncthreads();   // every wave is past its reads of the L2^T staging
     if (D == 128) {
-        __syncthreads();   // every wave is past its reads of the L2^T staging
-        float *xs = reinterpret_cast<float *>(&sm.u);   // [wn][wm][bj][32]
+        // past the output staging: [wn][wm][bj][32]
+        float *xs = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&sm) + QKV_XS_OFF);
         if (ks2 == 0) {
 #pragma unroll
             for (int bj = 0; bj < WB; ++bj) xs[((wn * 2 + wm) * WB + bj) * 32 + r32] = ss[bj];
@@ -597,24 +620,40 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
     float inv[WB];
 #pragma unroll
     for (int bj = 0; bj < WB; ++bj) inv[bj] = 1.0f / sqrtf(ss[bj] / (float)D + qk.eps);
+    // regroup: the wave's own [64 tokens][QKV_TP floats] area of the L2^T
+    // region (free now); cos first, then sin in the same place (one wave's
+    // LDS accesses complete in order)
+    float *tb = reinterpret_cast<float *>(&sm) + (wn * 2 + wm) * 64 * QKV_TP;
+    f32x2 cs[WB][4][WB], sn[WB][4][WB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const u32x4 v = t == 0 ? tc[j] : tsn[j];
+            float *w = tb + (8 * j + (lane >> 3)) * QKV_TP + 4 * (lane & 7);
+            *reinterpret_cast<u32x2 *>(w) = u32x2{v.x, v.y};
+            *reinterpret_cast<u32x2 *>(w + 2) = u32x2{v.z, v.w};
+        }
+#pragma unroll
+        for (int bi = 0; bi < WB; ++bi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int bj = 0; bj < WB; ++bj) {
+                    const f32x2 r = *reinterpret_cast<const f32x2 *>(
+                        tb + (32 * bj + r32) * QKV_TP + 16 * bi + 4 * q + 2 * ks2);
+                    if (t == 0) cs[bi][q][bj] = r;
+                    else sn[bi][q][bj] = r;
+                }
+    }
     const uint16_t *gam = sec == 0 ? qk.gq : qk.gk;
-    const int half = D / 2;
 #pragma unroll
     for (int bi = 0; bi < WB; ++bi) {
         u32x2 g4[4];
-        f32x2 cs[4][WB], sn[4][WB];
-        int64_t dd[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t nl = nsec + wn * 32 * WB + 32 * bi + 8 * q + 4 * ks2;
-            dd[q] = nl - (nl / D) * D;
-            g4[q] = *reinterpret_cast<const u32x2 *>(gam + dd[q]);
-#pragma unroll
-            for (int bj = 0; bj < WB; ++bj) {
-                const int64_t at = spos[bj] * half + dd[q] / 2;
-                cs[q][bj] = *reinterpret_cast<const f32x2 *>(qk.cos_t + at);
-                sn[q][bj] = *reinterpret_cast<const f32x2 *>(qk.sin_t + at);
-            }
+            g4[q] = *reinterpret_cast<const u32x2 *>(gam + (nl - (nl / D) * D));
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -626,10 +665,10 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
                 float v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = acc[t][4 * q + j] * inv[bj] * gv[j];
-                const float o0 = v[0] * cs[q][bj].x - v[1] * sn[q][bj].x;
-                const float o1 = v[0] * sn[q][bj].x + v[1] * cs[q][bj].x;
-                const float o2 = v[2] * cs[q][bj].y - v[3] * sn[q][bj].y;
-                const float o3 = v[2] * sn[q][bj].y + v[3] * cs[q][bj].y;
+                const float o0 = v[0] * cs[bi][q][bj].x - v[1] * sn[bi][q][bj].x;
+                const float o1 = v[0] * sn[bi][q][bj].x + v[1] * cs[bi][q][bj].x;
+                const float o2 = v[2] * cs[bi][q][bj].y - v[3] * sn[bi][q][bj].y;
+                const float o3 = v[2] * sn[bi][q][bj].y + v[3] * cs[bi][q][bj].y;
                 u32x2 out;
                 out.x = pack_bf16x2(o0, o1);
                 out.y = pack_bf16x2(o2, o3);
