@@ -790,18 +790,28 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
         }
         const auto pl = __builtin_amdgcn_permlane32_swap(last, last, false, false);
         const uint32_t other = pl[0] ^ pl[1] ^ last;   // the value of lane l ^ 32
-        if (m < M) {
+        // Stored 16-bit pieces: piece (bi, q) is bytes 16 bi + 4 q + 2 ks2 of
+        // the wave's 32 bytes of this token.  The partner lanes swap halves
+        // so that lane ks2 = 0 holds the four words of bi = 0 and lane ks2 = 1
+        // those of bi = 1: one 16-byte store each instead of eight 2-byte
+        // stores spread over 32 rows per instruction.
+        u32x4 words;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t st[WB];
 #pragma unroll
             for (int bi = 0; bi < WB; ++bi) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t w = wsm[bi][q];
-                    const uint32_t first = (other >> (4 * bi + (ks2 ? q : (q ^ 1)))) & 1u;
-                    const uint32_t st = (w & 0x7777u) | ((w << 4) & 0x8880u) | (first << 3);
-                    *reinterpret_cast<uint16_t *>(
-                        ma.qa + code_offset(m, kb, (nw + 32 * bi + 8 * q + 4 * ks2) / 2)) = (uint16_t)st;
-                }
+                const uint32_t w = wsm[bi][q];
+                const uint32_t first = (other >> (4 * bi + (ks2 ? q : (q ^ 1)))) & 1u;
+                st[bi] = (w & 0x7777u) | ((w << 4) & 0x8880u) | (first << 3);
             }
+            const uint32_t give = ks2 ? st[0] : st[1];           // what the partner keeps
+            const auto sw = __builtin_amdgcn_permlane32_swap(give, give, false, false);
+            const uint32_t got = sw[0] ^ sw[1] ^ give;           // the partner's piece
+            words[q] = ks2 ? (got | (st[1] << 16)) : (st[0] | (got << 16));
+        }
+        if (m < M) {
+            *reinterpret_cast<u32x4 *>(ma.qa + code_offset(m, kb, nw / 2 + 16 * ks2)) = words;
             if (ks2 == 0) ma.sa[m * G + nw / kGroup] = s;
         }
     }
