@@ -19,12 +19,17 @@ pytestmark = pytest.mark.gpu
 
 # (B, S, H, D, K, r, bias): one and two heads per tile (D = 128 / 64), ragged
 # token counts (sequences straddling 128-row tiles, a last tile of one row),
-# odd group counts, r = 0.
+# odd group counts, r = 0, and sequences shorter than 8 tokens (positions wrap
+# several times within the 8 tokens a lane steps over when it fetches the
+# rotary rows; S = 1: every token at position 0).
 SHAPES = [
     (1, 96, 2, 64, 256, 16, True),
     (2, 80, 2, 128, 320, 32, True),
     (3, 50, 4, 64, 512, 0, False),
     (1, 257, 1, 128, 192, 48, True),
+    (40, 5, 2, 64, 128, 16, True),
+    (43, 3, 1, 128, 128, 0, False),
+    (130, 1, 2, 64, 192, 32, True),
 ]
 
 
