@@ -1,8 +1,9 @@
 // w4a4_tile.h -- the tile code of the SVDQuant W4A4 GEMM on gfx950 (internal;
-// not part of the ABI): operand staging, the K loop, the rank-r epilogue and
-// the two output epilogues (plain [M, N] store; fused QKV).  Included by the
-// plain GEMM and the fused-QKV GEMM, each in its own translation unit, so that
-// each kernel is scheduled on its own.
+// not part of the ABI): operand staging, the K loops (INT4 and MXFP4), the
+// rank-r epilogue and the three output epilogues (plain [M, N] store; fused
+// QKV; the MLP chain's next-layer activation step).  Included by the plain,
+// fused-QKV, MLP-chain and MXFP4 GEMMs, each in its own translation unit, so
+// that each kernel is scheduled on its own.
 #pragma once
 
 // The W4A4 GEMM of the SVDQuant layer on gfx950 with the
@@ -13,8 +14,8 @@
 //
 // Output tiles are computed transposed, D[n][m] = Y[m][n]: the weight codes
 // are the MFMA A operand and the activation codes the B operand, so that an
-// output lane holds four consecutive n of one token row and stores them as
-// one 8-byte write.
+// output lane holds four consecutive n of one token row; the tile is staged
+// in LDS in [m][n] order and leaves as 16-byte row segments.
 //
 // Per group of 64 along K and per 32 x 32 output block the wave issues
 //   - one v_mfma_scale_f32_32x32x64_f8f6f4 on the codes as FP8 (the stored
@@ -30,10 +31,10 @@
 // the int8 instruction S came out as an integer and needed a convert per
 // output and group as well.
 //
-// Data movement: packed 4-bit codes and raw fp32 scales go from global
-// memory straight into a four-stage LDS ring with global_load_lds (no
-// registers, no LDS write instructions), up to three stages ahead of the one
-// being read; each wave reads its fragments with 16-byte LDS reads
+// Data movement: packed 4-bit codes (rows in pairs, so that a stage of two
+// rows is one 128-byte line) and raw fp32 scales go from global memory
+// straight into a four-stage LDS ring with global_load_lds (no registers, no
+// LDS write instructions), up to three stages ahead of the one being read; each wave reads its fragments with 16-byte LDS reads
 // (XOR-swizzled rows, no bank conflicts) and turns the codes into FP8 in
 // registers.
 #include "svdq_device.h"
