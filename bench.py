@@ -621,7 +621,7 @@ def main():
         (bench_awq if args.workload.startswith("awq") else extra[args.workload])(args)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the layer has no multi-GPU path in this build "
+        print("bench.py runs on one GPU only: the layer has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests run only when a GPU is present; on a CPU host they are skipped
-    # (the driver selects them with -m gpu on the GPU machine).
+    # (select them with -m gpu on a machine with the GPU).
     try:
         import torch
         have_gpu = torch.cuda.is_available()
