@@ -41,7 +41,8 @@ def parse():
                     help="untimed steps before the timed ones; the GPU clocks take ~100-300 steps of this layer (25-70 ms) to settle after idle")
     ap.add_argument("--workload", default="qkv",
                     choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single",
-                             "qkv_fused", "mlp_chain", "mx_qkv", "mx_mlp_up", "mx_mlp_down"])
+                             "qkv_fused", "mlp_chain", "block", "mx_qkv", "mx_mlp_up",
+                             "mx_mlp_down"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rank-overhead", action="store_true",
@@ -471,6 +472,119 @@ def cpu_baseline_mx(L, target_s):
             "sample": "first %d of %d token rows of the same MXFP4 layer, %.1f s" % (rows, M, t)}
 
 
+def bench_block(args):
+    """One DiT block's four linears back to back (QKV 3072 -> 9216, out 3072 -> 3072, MLP up
+    3072 -> 12288 with GELU, MLP down 12288 -> 3072; rank 32; 4608 tokens, or --M): one step =
+    four svdq_linear calls on one stream, each layer on its own seeded inputs (not chained).
+    Metric: the block's sum of 2 M N K over the step time; each layer's GEMM is also timed alone
+    with HIP events, and the roofline line is the four GEMMs together against the 8-bit peak."""
+    import torch
+
+    import bit_diffusion_transformer_amd as bdt
+    from synth import DIT_CHAIN, make_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    M = DIT_CHAIN[0].M if args.M is None else args.M
+    specs = [s.with_M(M) for s in DIT_CHAIN]
+
+    def d(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    layers = []
+    for spec in specs:
+        L = make_layer(spec, seed=0, M=M)
+        qw, sw = bdt.pack_weights(d(L.R))
+        layers.append(dict(spec=spec, X=d(L.X), lam=d(L.lam), L1=d(L.L1), L2=d(L.L2),
+                           bias=d(L.bias), qw=qw, sw=sw))
+        del L
+    torch.cuda.synchronize()
+    ws_bytes = max(bdt.svdq_linear_workspace_bytes(M, l["spec"].K, l["spec"].r) for l in layers)
+    set_bytes = sum(sum(v.numel() * v.element_size() for k, v in l.items()
+                        if k != "spec" and v is not None) + 2 * M * l["spec"].N for l in layers)
+    nsets = max(2, int(np.ceil(2 * CACHE_BYTES / (set_bytes + ws_bytes))))
+    bits = bdt._bits
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(
+            L=[{k: (v.clone() if (k != "spec" and v is not None) else v) for k, v in l.items()}
+               for l in layers],
+            Y=[torch.empty((M, l["spec"].N), dtype=torch.bfloat16, device=dev) for l in layers],
+            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def linear(st, j):
+        l, sp = st["L"][j], st["L"][j]["spec"]
+        bdt.svdq_linear(bits(l["X"]), l["lam"], bits(l["L1"]), l["qw"], l["sw"], bits(l["L2"]),
+                        bits(l["bias"]), sp.act, M, sp.N, sp.K, sp.r, bits(st["Y"][j]), st["ws"],
+                        ws_bytes, stream)
+
+    def step(i):
+        st = sets[i % nsets]
+        for j in range(len(layers)):
+            linear(st, j)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    ops = [2.0 * M * l["spec"].N * l["spec"].K for l in layers]
+
+    # each layer's GEMM alone (inputs from one K1 per set), HIP events on the stream
+    carved = [[bdt.quantize_act_down(l["X"], l["lam"], l["L1"]) for l in st["L"]] for st in sets]
+    torch.cuda.synchronize()
+    n_k = max(args.steps, 20)
+    per = []
+    for j, l0 in enumerate(layers):
+        sp = l0["spec"]
+
+        def gemm(i):
+            st = sets[i % nsets]
+            l, (qa, sa, xl1) = st["L"][j], carved[i % nsets][j]
+            bdt.svdq_w4a4_lr_gemm(qa, sa, l["qw"], l["sw"], xl1, bits(l["L2"]), bits(l["bias"]),
+                                  sp.act, M, sp.N, sp.K, sp.r, bits(st["Y"][j]), stream)
+
+        for i in range(20):
+            gemm(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_k):
+            gemm(i)
+        e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / n_k
+        per.append({"layer": sp.name.replace("chain_", ""), "M": M, "K": sp.K, "N": sp.N,
+                    "gemm_us": round(t * 1e6, 2), "gemm_tops": round(ops[j] / t / 1e12, 1)})
+    t_gemms = sum(p["gemm_us"] for p in per) / 1e6
+    achieved = sum(ops) / t_gemms / 1e12
+    out = {
+        "metric": "effective TOPS (sum of 2MNK / t) of one DiT block's four W4A4+rank-32 linears",
+        "value": round(sum(ops) / t_step / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic (seeded DiT-shaped inputs, random weights of the stated shapes)",
+        "config": {"workload": "block: qkv 3072->9216, out 3072->3072, up 3072->12288 (GELU), "
+                               "down 12288->3072; M=%d r=32 group=64" % M,
+                   "global_batch": M, "input_sets_rotated": nsets},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": None,
+                     "kernel": "w4a4_lr_gemm_kernel, the four layers' calls together",
+                     "avg_launch_us": round(t_gemms * 1e6, 2), "algorithmic_ops": sum(ops)},
+        "per_layer": per,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_mlp_chain(args):
     """One DiT block's MLP (3072 -> 12288 GELU -> 3072, rank 32, 4608 tokens): one step =
     one svdq_mlp call (the up GEMM runs the down layer's activation step in its epilogue).
@@ -611,7 +725,8 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    extra = {"qkv_fused": bench_qkv_fused, "mlp_chain": bench_mlp_chain, "mx_qkv": bench_mx,
+    extra = {"qkv_fused": bench_qkv_fused, "mlp_chain": bench_mlp_chain, "block": bench_block,
+             "mx_qkv": bench_mx,
              "mx_mlp_up": bench_mx, "mx_mlp_down": bench_mx}
     if args.workload.startswith("awq") or args.workload in extra:
         if args.gpus != 1:
