@@ -68,6 +68,18 @@ int32_t check_k(int64_t K) {
     if (K < SVDQ_GROUP || K % SVDQ_GROUP != 0)
         return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "K must be a positive multiple of 64 (got %lld)",
                     (long long)K);
+    if (K > SVDQ_MAX_K)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "K = %lld exceeds the limit %d", (long long)K,
+                    SVDQ_MAX_K);
+    return SVDQ_OK;
+}
+
+// Token and output-row counts: >= 0 (0: nothing to do) and within the limit.
+int32_t check_rows(int64_t n, const char *name) {
+    if (n < 0) return fail(SVDQ_ERR_INVALID_ARG, "%s must be >= 0 (got %lld)", name, (long long)n);
+    if (n > SVDQ_MAX_ROWS)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "%s = %lld exceeds the limit %d", name,
+                    (long long)n, SVDQ_MAX_ROWS);
     return SVDQ_OK;
 }
 
@@ -76,7 +88,7 @@ int32_t check_k_mx(int64_t K) {
     if (K < 128 || K % 128 != 0)
         return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
                     "K must be a positive multiple of 128 for MXFP4 (got %lld)", (long long)K);
-    return SVDQ_OK;
+    return check_k(K);
 }
 
 int32_t check_r(int32_t r) {
@@ -90,7 +102,7 @@ int32_t check_n(int64_t N) {
     if (N < 8 || N % 8 != 0)
         return fail(SVDQ_ERR_UNSUPPORTED_SHAPE, "N must be a positive multiple of 8 (got %lld)",
                     (long long)N);
-    return SVDQ_OK;
+    return check_rows(N, "N");
 }
 
 #define SVDQ_TRY(expr)                       \
@@ -118,7 +130,7 @@ int32_t lr_ptrs(const void *a, const char *an, const void *b, const char *bn, in
 int32_t validate_down(const uint16_t *X, const float *lambda, const uint16_t *L1, int64_t M,
                       int64_t K, int32_t r, const uint8_t *qa, const void *sa,
                       const float *xl1, const void *ws, size_t ws_bytes) {
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     SVDQ_TRY(check_k(K));
     SVDQ_TRY(check_r(r));
     if (M == 0) return SVDQ_OK;
@@ -137,7 +149,7 @@ int32_t validate_down(const uint16_t *X, const float *lambda, const uint16_t *L1
 int32_t validate_gemm(const uint8_t *qa, const void *sa, const uint8_t *qw, const void *sw,
                       const float *xl1, const uint16_t *L2, const uint16_t *bias, int32_t act,
                       int64_t M, int64_t N, int64_t K, int32_t r, const uint16_t *Y) {
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
         return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
     SVDQ_TRY(check_n(N));
@@ -227,7 +239,7 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r, bool m
 namespace {
 
 int32_t check_awq_pack_shape(int64_t N, int64_t K) {
-    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+    SVDQ_TRY(check_rows(N, "N"));
     SVDQ_TRY(check_k(K));
     if (N > 0) SVDQ_TRY(check_n(N));
     return SVDQ_OK;
@@ -323,7 +335,7 @@ const char *svdq_last_error(void) { return g_last_error; }
 int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
                           void *stream) {
     g_last_error[0] = 0;
-    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+    SVDQ_TRY(check_rows(N, "N"));
     SVDQ_TRY(check_k(K));
     if (N == 0) return SVDQ_OK;
     SVDQ_TRY(need_ptr(R, "R"));
@@ -370,7 +382,7 @@ int32_t svdq_w4a4_lr_gemm_qkv(const uint8_t *qa, const float *sa, const uint8_t 
                               const uint16_t *bias, int64_t M, int64_t K, int32_t r,
                               const svdq_qkv_epilogue *epi, void *stream) {
     g_last_error[0] = 0;
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     SVDQ_TRY(validate_qkv(epi, M));
     const int64_t N = 3 * (int64_t)epi->heads * epi->head_dim;
     // the plain GEMM's checks, with a stand-in for the [M, N] output
@@ -392,7 +404,7 @@ int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
                     const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
                     int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream) {
     g_last_error[0] = 0;
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
         return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
     SVDQ_TRY(check_n(N));
@@ -429,7 +441,7 @@ int32_t svdq_linear_qkv(const uint16_t *X, const float *lambda, const uint16_t *
                         const svdq_qkv_epilogue *epi, void *workspace, size_t ws_bytes,
                         void *stream) {
     g_last_error[0] = 0;
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     SVDQ_TRY(validate_qkv(epi, M));
     SVDQ_TRY(check_k(K));
     SVDQ_TRY(check_r(r));
@@ -470,7 +482,7 @@ int32_t svdq_w4a4_lr_gemm_quant_down(const uint8_t *qa, const float *sa, const u
                                      float *sa_next, float *xl1_next, void *workspace,
                                      size_t ws_bytes, void *stream) {
     g_last_error[0] = 0;
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     SVDQ_TRY(check_n(N));
     SVDQ_TRY(check_next_shape(N, r_next));
     // the plain GEMM's checks, with the next layer's codes standing in for Y
@@ -512,7 +524,7 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
                  int32_t r_up, int32_t r_down, uint16_t *Y, void *workspace, size_t ws_bytes,
                  void *stream) {
     g_last_error[0] = 0;
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
         return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
     SVDQ_TRY(check_k(K));
@@ -568,7 +580,7 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
 int32_t svdq_mx_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, uint8_t *sw,
                              void *stream) {
     g_last_error[0] = 0;
-    if (N < 0) return fail(SVDQ_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+    SVDQ_TRY(check_rows(N, "N"));
     SVDQ_TRY(check_k_mx(K));
     if (N == 0) return SVDQ_OK;
     SVDQ_TRY(need_ptr(R, "R"));
@@ -617,7 +629,7 @@ int32_t svdq_mx_linear(const uint16_t *X, const float *lambda, const uint16_t *L
                        const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
                        int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream) {
     g_last_error[0] = 0;
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
         return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
     SVDQ_TRY(check_n(N));
@@ -712,7 +724,7 @@ int32_t svdq_awq_repack(const uint8_t *codes, const float *scales, const uint8_t
 int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_t *bias,
                               int64_t M, int64_t N, int64_t K, uint16_t *Y, void *stream) {
     g_last_error[0] = 0;
-    if (M < 0) return fail(SVDQ_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    SVDQ_TRY(check_rows(M, "M"));
     SVDQ_TRY(check_n(N));
     SVDQ_TRY(check_k(K));
     if (M == 0) return SVDQ_OK;

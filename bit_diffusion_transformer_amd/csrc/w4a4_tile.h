@@ -413,7 +413,7 @@ __device__ __forceinline__ void issue_stage_mx(uint8_t *st, const CopyPlan<WB> &
         __builtin_amdgcn_global_load_lds(qws + cp.a_off[i], (lds_void *)(st + C::A_OFF + row * ROWP), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(qas + cp.b_off[i], (lds_void *)(st + C::B_OFF + row * ROWP), 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(ss.base + c * ss.stage + ss.off, (lds_void *)(st + ss.dst), 4,
+    __builtin_amdgcn_global_load_lds(ss.base + (int64_t)c * ss.stage + ss.off, (lds_void *)(st + ss.dst), 4,
                                      0, 0);
 }
 

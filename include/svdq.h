@@ -73,11 +73,17 @@ extern "C" {
 #define SVDQ_ABI_VERSION 1
 #define SVDQ_GROUP 64      /* quantization group along K */
 #define SVDQ_MAX_RANK 128  /* largest supported low-rank r */
+/* Size limits, so that every offset the kernels form within a tile fits its
+ * integer type: K (in-features) at most 2^20, and M (tokens) and N
+ * (out-features) at most 2^28 each.  Larger sizes are rejected with
+ * SVDQ_ERR_UNSUPPORTED_SHAPE. */
+#define SVDQ_MAX_K (1 << 20)
+#define SVDQ_MAX_ROWS (1 << 28)
 
 typedef enum {
     SVDQ_OK = 0,
     SVDQ_ERR_INVALID_ARG = 1,       /* NULL pointer where data is needed, negative size, bad act */
-    SVDQ_ERR_UNSUPPORTED_SHAPE = 2, /* K % 64 != 0, K < 64, N % 8 != 0, r not a multiple of 16 or > 128 */
+    SVDQ_ERR_UNSUPPORTED_SHAPE = 2, /* K % 64 != 0, K < 64, N % 8 != 0, r not a multiple of 16 or > 128, a size past SVDQ_MAX_K / SVDQ_MAX_ROWS */
     SVDQ_ERR_MISALIGNED = 3,        /* a device pointer not 16-byte aligned */
     SVDQ_ERR_WORKSPACE_TOO_SMALL = 4,
     SVDQ_ERR_UNSUPPORTED_DEVICE = 5, /* current device is not gfx950 (or no device) */

@@ -89,6 +89,7 @@ def _lin(lib, X=A, lam=A, L1=A, qw=A, sw=A, L2=A, bias=A, act=0, M=16, N=64, K=1
     (dict(r=0), INVALID),                      # L1/xl1 given although r == 0
     (dict(X=U), MISALIGNED), (dict(sa=U), MISALIGNED), (dict(L1=U), MISALIGNED),
     (dict(ws_bytes=16), WS_SMALL), (dict(ws=0), INVALID),
+    (dict(K=(1 << 20) + 64), SHAPE), (dict(M=(1 << 28) + 1), SHAPE),   # past the size limits
 ])
 def test_quantize_act_down_rejects(lib, kw, code):
     assert _down(lib, **kw) == code
@@ -98,6 +99,7 @@ def test_quantize_act_down_rejects(lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(M=-2), INVALID), (dict(act=2), INVALID), (dict(act=-1), INVALID),
     (dict(N=60), SHAPE), (dict(N=0), SHAPE), (dict(K=96), SHAPE), (dict(r=24), SHAPE),
+    (dict(N=(1 << 28) + 8), SHAPE), (dict(K=(1 << 20) + 64), SHAPE), (dict(M=(1 << 28) + 1), SHAPE),
     (dict(qa=0), INVALID), (dict(sw=0), INVALID), (dict(Y=0), INVALID),
     (dict(xl1=0), INVALID), (dict(L2=0), INVALID), (dict(r=0), INVALID),
     (dict(qw=U), MISALIGNED), (dict(Y=U), MISALIGNED), (dict(bias=U), MISALIGNED),
