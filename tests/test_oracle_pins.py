@@ -248,7 +248,8 @@ def test_zero_and_tiny_groups():
     packed, scales = oracle.quantize_groups(v)
     assert not packed.any()
     assert scales[1, 1] == 0.0
-    assert scales[2, 0] > 0 and not np.isfinite(np.float32(1) / scales[2, 0])
+    with np.errstate(over="ignore"):                  # the overflow is the point
+        assert scales[2, 0] > 0 and not np.isfinite(np.float32(1) / scales[2, 0])
 
 
 # ---------------------------------------------------------------- group sums
