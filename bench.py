@@ -36,9 +36,11 @@ METRIC = "effective TOPS (2MNK/t) of W4A4+rank-32 linear; % of INT8 MFMA / HBM p
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps before the timed ones; the GPU clocks take ~100-300 steps of this layer (25-70 ms) to settle after idle")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50, or enough for ~20 ms of a short workload)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: about 0.1 s of the "
+                         "workload's steps; the GPU clocks take 25-70 ms to settle after idle)")
     ap.add_argument("--workload", default="qkv",
                     choices=["tiny", "qkv", "mlp_up", "mlp_down", "awq_mod", "awq_mod_single",
                              "qkv_fused", "mlp_chain", "block", "mx_qkv", "mx_mlp_up",
@@ -51,7 +53,21 @@ def parse():
                     help="only run a plain device copy of a known size (counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.warmup is None:
+        # about 0.1 s of steps, so that the clocks have settled when the timed steps start
+        args.warmup = WARMUP_STEPS.get(args.workload, 300)
+    if args.steps is None:
+        # short steps: enough of them that the host's start and stop cost little
+        args.steps = TIMED_STEPS.get(args.workload, 50)
+    return args
+
+
+# Default warm-up steps per workload (≈ 0.1 s each at the measured step times).
+WARMUP_STEPS = {"tiny": 3000, "qkv": 300, "mlp_up": 300, "mlp_down": 300, "awq_mod": 10000,
+                "awq_mod_single": 10000, "qkv_fused": 300, "mlp_chain": 150, "block": 100,
+                "mx_qkv": 600, "mx_mlp_up": 600, "mx_mlp_down": 600}
+TIMED_STEPS = {"tiny": 1000, "awq_mod": 2000, "awq_mod_single": 2000}
 
 
 def k1_bytes(M, K, r):
