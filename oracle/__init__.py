@@ -25,7 +25,9 @@ _SRC = os.path.join(_HERE, "svdq_oracle.c")
 _SRC_AWQ = os.path.join(_HERE, "awq_oracle.c")
 _SRC_QKV = os.path.join(_HERE, "qkv_oracle.c")
 _SRC_MX = os.path.join(_HERE, "mxfp4_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# SVDQ_ORACLE_LIB points the binding at another build of the same sources (the
+# mutation test builds copies with one planted mistake each).
+_LIB = os.environ.get("SVDQ_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 GROUP = 64
