@@ -12,7 +12,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-@pytest.mark.parametrize("workload", ["qkv", "awq_mod", "mx_qkv", "block"])
+@pytest.mark.parametrize("workload", ["mlp_up", "qkv", "awq_mod", "mx_qkv", "block"])
 def test_more_than_one_gpu_is_refused(workload):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2",
                         "--workload", workload], capture_output=True, text=True, timeout=120)
@@ -32,7 +32,7 @@ def _parse(argv):
 
 def test_defaults_and_overrides():
     a = _parse([])
-    assert (a.workload, a.gpus, a.steps, a.warmup) == ("qkv", 1, 50, 300)
+    assert (a.workload, a.gpus, a.steps, a.warmup) == ("mlp_up", 1, 50, 300)
     a = _parse(["--workload", "awq_mod"])
     assert a.steps == 2000 and a.warmup == 10000
     a = _parse(["--workload", "awq_mod", "--steps", "7", "--warmup", "3"])
