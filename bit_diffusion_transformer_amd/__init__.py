@@ -22,7 +22,7 @@ from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError, 
                        svdq_awq_w4a16_linear, svdq_debug_group_sums,
                        svdq_debug_set_tile_policy,
                        svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
-                       svdq_pack_weights, svdq_quantize_act_down,
+                       svdq_pack_weights, svdq_repack_weights, svdq_quantize_act_down,
                        svdq_quantize_act_down_workspace_bytes, svdq_status_string,
                        svdq_w4a4_lr_gemm, svdq_w4a4_lr_gemm_qkv, svdq_linear_qkv,
                        svdq_w4a4_lr_gemm_quant_down,
@@ -72,6 +72,14 @@ def pack_weights(R: torch.Tensor):
     sw = torch.empty((N, K // GROUP), dtype=torch.float32, device=R.device)
     svdq_pack_weights(R, N, K, qw, sw)
     return qw, sw
+
+
+def repack_weights(codes: torch.Tensor) -> torch.Tensor:
+    """Row-major two's-complement INT4 codes uint8 [N, K/2] -> qw uint8 [ceil(N/2), K]."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    qw = torch.empty((pair_rows(N), K), dtype=torch.uint8, device=codes.device)
+    svdq_repack_weights(codes, N, K, qw)
+    return qw
 
 
 def awq_pack_weights(W: torch.Tensor) -> torch.Tensor:
@@ -220,14 +228,15 @@ def mlp(X, up: dict, down: dict, act: int = ACT_GELU,
     return Y
 
 
-def group_sums(qa, qw, M: int, N: int, m0: int, n0: int, tm: int, tn: int) -> torch.Tensor:
-    """Exact per-group int32 sums of a block (test hook) -> int32 [tm, tn, K/64]; qa, qw
-    row-pair codes of M and N rows."""
+def group_sums(qa, sa, qw, sw, M: int, N: int, m0: int, n0: int, tm: int,
+               tn: int) -> torch.Tensor:
+    """Exact per-group int32 sums of a block (test hook, through the GEMM's own tile code)
+    -> int32 [tm, tn, K/64]; qa, qw row-pair codes of M and N rows, sa, sw their scales."""
     K = qa.shape[1]
     _codes_of(qa, M, K, "qa")
     _codes_of(qw, N, K, "qw")
     S = torch.empty((tm, tn, K // GROUP), dtype=torch.int32, device=qa.device)
-    svdq_debug_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S)
+    svdq_debug_group_sums(qa, sa, qw, sw, M, N, K, m0, n0, tm, tn, S)
     return S
 
 

@@ -27,6 +27,7 @@ GROUP = 64
 # Every symbol declared in include/svdq.h.
 EXPORTS = (
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_pack_weights",
+    "svdq_repack_weights",
     "svdq_quantize_act_down_workspace_bytes", "svdq_quantize_act_down", "svdq_w4a4_lr_gemm",
     "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
     "svdq_debug_set_tile_policy", "svdq_awq_packed_bytes", "svdq_awq_pack_weights",
@@ -85,12 +86,13 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_status_string": ([I32], ctypes.c_char_p),
         "svdq_last_error": ([], ctypes.c_char_p),
         "svdq_pack_weights": ([P, I64, I64, P, P, P], I32),
+        "svdq_repack_weights": ([P, I64, I64, P, P], I32),
         "svdq_quantize_act_down_workspace_bytes": ([I64, I64, I32], SZ),
         "svdq_quantize_act_down": ([P, P, P, I64, I64, I32, P, P, P, P, SZ, P], I32),
         "svdq_w4a4_lr_gemm": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P], I32),
         "svdq_linear_workspace_bytes": ([I64, I64, I32], SZ),
         "svdq_linear": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, SZ, P], I32),
-        "svdq_debug_group_sums": ([P, P, I64, I64, I64, I64, I64, I64, I64, P, P], I32),
+        "svdq_debug_group_sums": ([P, P, P, P, I64, I64, I64, I64, I64, I64, I64, P, P], I32),
         "svdq_debug_set_tile_policy": ([I32], I32),
         "svdq_awq_packed_bytes": ([I64, I64], I64),
         "svdq_awq_pack_weights": ([P, I64, I64, P, P], I32),
@@ -157,6 +159,11 @@ def svdq_last_error() -> str:
     return load_library().svdq_last_error().decode(errors="replace")
 
 
+def svdq_repack_weights(codes, N, K, qw, stream=None):
+    _check(load_library().svdq_repack_weights(_p(codes), N, K, _p(qw), _stream(stream)),
+           "svdq_repack_weights")
+
+
 def svdq_pack_weights(R, N, K, qw, sw, stream=None):
     _check(load_library().svdq_pack_weights(_p(R), N, K, _p(qw), _p(sw), _stream(stream)),
            "svdq_pack_weights")
@@ -189,9 +196,9 @@ def svdq_linear(X, lam, L1, qw, sw, L2, bias, act, M, N, K, r, Y, workspace, ws_
         _p(workspace), ws_bytes, _stream(stream)), "svdq_linear")
 
 
-def svdq_debug_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S, stream=None):
+def svdq_debug_group_sums(qa, sa, qw, sw, M, N, K, m0, n0, tm, tn, S, stream=None):
     _check(load_library().svdq_debug_group_sums(
-        _p(qa), _p(qw), M, N, K, m0, n0, tm, tn, _p(S), _stream(stream)),
+        _p(qa), _p(sa), _p(qw), _p(sw), M, N, K, m0, n0, tm, tn, _p(S), _stream(stream)),
         "svdq_debug_group_sums")
 
 

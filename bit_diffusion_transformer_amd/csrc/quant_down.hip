@@ -283,6 +283,29 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
     }
 }
 
+// ------------------------------------------------------------------ repack
+// Already quantized weight codes in the common row-major form (two's
+// complement nibbles, element 2j in the low nibble of byte j, [N, K/2]) ->
+// the stored layout: one thread per block of 16 codes (8 bytes), the same
+// conversion as the quantizers' (store_code_words), written to the row-pair
+// position.  A nibble 8 (-8, outside the symmetric range) is stored as -7.
+__global__ void __launch_bounds__(256)
+repack_codes_kernel(const uint8_t *__restrict__ codes, int64_t N, int64_t K,
+                    uint8_t *__restrict__ qw) {
+    const int64_t kb = K / 2, per_row = K / 16;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= N * per_row) return;
+    const int64_t row = i / per_row, t = i - row * per_row;
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(codes + row * kb + 8 * t);
+    auto no_m8 = [](uint32_t x) {
+        // nibbles equal to 8: sign bit set, magnitude bits zero -> 9 (-7)
+        const uint32_t zero_mag = ~((x & 0x77777777u) + 0x77777777u) & 0x88888888u;
+        return x | ((x & zero_mag & 0x88888888u) >> 3);
+    };
+    *reinterpret_cast<u32x2 *>(qw + code_offset(row, kb, 8 * t)) =
+        store_code_words(no_m8(w.x), no_m8(w.y));
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
@@ -320,6 +343,13 @@ hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl
                              hipStream_t stream) {
     const unsigned rblocks = (unsigned)((total / 4 + kReduceCols - 1) / kReduceCols);
     xl1_reduce_kernel<<<rblocks, 256, 0, stream>>>(part, nc, total, xl1);
+    return hipGetLastError();
+}
+
+hipError_t launch_repack_codes(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
+                               hipStream_t stream) {
+    const int64_t threads = N * (K / 16);
+    repack_codes_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(codes, N, K, qw);
     return hipGetLastError();
 }
 

@@ -346,6 +346,19 @@ int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, flo
                       "pack_weights launch");
 }
 
+int32_t svdq_repack_weights(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
+                            void *stream) {
+    g_last_error[0] = 0;
+    SVDQ_TRY(check_rows(N, "N"));
+    SVDQ_TRY(check_k(K));
+    if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(codes, "codes"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(check_device());
+    return hip_status(svdq::launch_repack_codes(codes, N, K, qw, (hipStream_t)stream),
+                      "repack_weights launch");
+}
+
 size_t svdq_quantize_act_down_workspace_bytes(int64_t M, int64_t K, int32_t r) {
     if (M < 0 || K < 0 || r < 0) return 0;
     return svdq::down_workspace_bytes(M, K, r);
@@ -661,21 +674,26 @@ int32_t svdq_mx_linear(const uint16_t *X, const float *lambda, const uint16_t *L
                       "mx_lr_gemm launch");
 }
 
-int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
-                              int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
-                              int32_t *S, void *stream) {
+int32_t svdq_debug_group_sums(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                              const float *sw, int64_t M, int64_t N, int64_t K, int64_t m0,
+                              int64_t n0, int64_t tm, int64_t tn, int32_t *S, void *stream) {
     g_last_error[0] = 0;
     if (M < 0 || N < 0 || m0 < 0 || n0 < 0 || tm < 0 || tn < 0 || m0 + tm > M || n0 + tn > N)
         return fail(SVDQ_ERR_INVALID_ARG, "block [%lld,+%lld) x [%lld,+%lld) outside %lld x %lld",
                     (long long)m0, (long long)tm, (long long)n0, (long long)tn, (long long)M,
                     (long long)N);
     SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_rows(M, "M"));
+    SVDQ_TRY(check_rows(N, "N"));
     if (tm == 0 || tn == 0) return SVDQ_OK;
     SVDQ_TRY(need_ptr(qa, "qa"));
+    SVDQ_TRY(need_ptr(sa, "sa"));
     SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
     SVDQ_TRY(need_ptr(S, "S"));
     SVDQ_TRY(check_device());
-    return hip_status(svdq::launch_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, S,
+    return hip_status(svdq::launch_group_sums(qa, sa, qw, sw, M, N, K, m0, n0, tm, tn, S,
+                                              svdq::tile_policy() == SVDQ_TILES_QUARTER,
                                               (hipStream_t)stream),
                       "group_sums launch");
 }

@@ -63,6 +63,9 @@ hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint1
                              void *sa, float *xl1, hipStream_t stream, bool mx = false);
 hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, void *sw,
                                hipStream_t stream, bool mx = false);
+// row-major two's-complement INT4 codes [N, K/2] -> the stored row-pair layout
+hipError_t launch_repack_codes(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
+                               hipStream_t stream);
 // W4A16 records (16 columns x 4 groups each)
 int64_t awq_packed_bytes(int64_t N, int64_t K);
 int awq_rows_per_pass(int64_t K, size_t lds_limit);   // activation rows staged per workgroup
@@ -119,8 +122,11 @@ hipError_t launch_w4a4_mx_gemm(const uint8_t *qa, const uint8_t *sa, const uint8
                                const uint8_t *sw, const float *xl1, const uint16_t *L2,
                                const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
                                int r, uint16_t *Y, hipStream_t stream);
-hipError_t launch_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
-                             int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
-                             int32_t *S, hipStream_t stream);
+// Group-sum test hook: the production tile code (128 x 128 tiles, or 64 x 64
+// with `quarter`) over the tiles that meet the block, one launch per group.
+hipError_t launch_group_sums(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                             const float *sw, int64_t M, int64_t N, int64_t K, int64_t m0,
+                             int64_t n0, int64_t tm, int64_t tn, int32_t *S, bool quarter,
+                             hipStream_t stream);
 
 }  // namespace svdq

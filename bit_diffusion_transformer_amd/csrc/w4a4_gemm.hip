@@ -3,8 +3,7 @@
 // its single bf16 store (the "Nunchaku engine design" section of the
 // svdq-int4-flux.1-canny-dev model card fuses the up-projection with the
 // 4-bit compute because both produce the same output).  The tile code is in
-// w4a4_tile.h; this file holds the plain kernel, its launcher and the
-// group-sum test hook.
+// w4a4_tile.h; this file holds the plain kernel and its launcher.
 #include "w4a4_tile.h"
 
 #include <atomic>
@@ -44,33 +43,6 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
         raster(b, nbm, nbn, tm, tn);
         tile_body<2>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm.full, tm * TILE,
                      tn * TILE);
-    }
-}
-
-// Test hook: per-group integer sums with the GEMM's k split, FP8 operand
-// form and matrix instruction; one wave per 32 x 32 block of (n, m),
-// operands read from memory.  The sums are exact integers in fp32.
-__global__ void __launch_bounds__(64)
-group_sums_kernel(const uint8_t *__restrict__ qa, const uint8_t *__restrict__ qw, int64_t M,
-                  int64_t N, int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
-                  int32_t *__restrict__ S) {
-    const int lane = threadIdx.x;
-    const int r32 = lane & 31, ks2 = lane >> 5;
-    const int64_t nb = blockIdx.x, mb = blockIdx.y;
-    const int64_t G = K / kGroup;
-    int64_t n = n0 + nb * 32 + r32, m = m0 + mb * 32 + r32;
-    if (n >= N) n = N - 1;
-    if (m >= M) m = M - 1;
-    for (int64_t g = 0; g < G; ++g) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(qw + code_offset(n, K / 2, g * 32 + 16 * ks2));
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(qa + code_offset(m, K / 2, g * 32 + 16 * ks2));
-        const f32x16 D = mfma_codes_32x32x64(codes_to_fp8(a), codes_to_fp8(b));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t nl = nb * 32 + 8 * (i / 4) + 4 * ks2 + (i % 4);
-            const int64_t ml = mb * 32 + r32;
-            if (nl < tn && ml < tm) S[(ml * tn + nl) * G + g] = (int32_t)D[i];
-        }
     }
 }
 
@@ -117,14 +89,6 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
     const int64_t nq = 4 * rest;
     w4a4_lr_gemm_kernel<<<(unsigned)(nq + full), NTHR, 0, stream>>>(
         qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, nq, full, full);
-    return hipGetLastError();
-}
-
-hipError_t launch_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
-                             int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
-                             int32_t *S, hipStream_t stream) {
-    dim3 grid((unsigned)((tn + 31) / 32), (unsigned)((tm + 31) / 32));
-    group_sums_kernel<<<grid, 64, 0, stream>>>(qa, qw, M, N, K, m0, n0, tm, tn, S);
     return hipGetLastError();
 }
 

@@ -269,21 +269,50 @@ __device__ __forceinline__ void issue_block(Pipe &p, const Frags<WB> &f, int t, 
     p.P[k] = mfma_bf16_32x32x8(f.AS[bi], f.BS[bj], f32x16{});
 }
 
-template <int NB>
-__device__ __forceinline__ void valu_block(f32x16 (&acc)[NB], const Pipe &p, int t, int k) {
+// What the VALU does with the group sums of stream element jj (block jj % NB,
+// group jj / NB of the stage, result slot jj & 1).  NoSink: the rescale,
+// acc += S P (the product path).  TakeGroup: acc = S for the one group whose
+// stage-relative index is `gsel` (the exact sums of one group captured from
+// the production K loop, for the group-sum test hook); other groups leave
+// acc as it is.
+struct NoSink {
+    static constexpr bool on = false;
+    int gsel;
+};
+struct TakeGroup {
+    static constexpr bool on = true;
+    int gsel;   // the wanted group minus twice the current stage
+};
+
+template <int NB, class SK>
+__device__ __forceinline__ void valu_block(f32x16 (&acc)[NB], const Pipe &p, int jj, const SK &sk) {
+    const int t = jj % NB, k = jj & 1;
+    if constexpr (SK::on) {
+        // acc += S w with w = 1 for the wanted group and 0 for the others (acc
+        // starts at zero, so it ends as that group's sums).  w is taken
+        // through fma(P, 0, w), so that, as in the rescale, the VALU reads
+        // the scale product as well as the sums and waits for both results
+        // of the matrix unit.
+        const float w = jj / NB == sk.gsel ? 1.0f : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = __builtin_fmaf(p.S[k][i], p.P[k][i], acc[t][i]);
+        for (int i = 0; i < 16; ++i)
+            acc[t][i] = __builtin_fmaf(p.S[k][i], __builtin_fmaf(p.P[k][i], 0.0f, w), acc[t][i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = __builtin_fmaf(p.S[k][i], p.P[k][i], acc[t][i]);
+    }
 }
 
 // Issue stream element j while the VALU finishes element j - 1: one MFMA,
 // then half of the VALU work, twice.  The empty asm pins the updated
 // accumulator so later passes cannot sink the VALU work below the following
 // MFMAs.
-template <int WB>
-__device__ __forceinline__ void pair(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f, int j) {
+template <int WB, class SK>
+__device__ __forceinline__ void pair(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f, int j,
+                                     const SK &sk) {
     constexpr int NB = WB * WB;
     issue_block<WB>(p, f, j % NB, j & 1);
-    valu_block<NB>(acc, p, (j - 1) % NB, (j - 1) & 1);
+    valu_block<NB>(acc, p, j - 1, sk);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -292,22 +321,24 @@ __device__ __forceinline__ void pair(f32x16 (&acc)[WB * WB], Pipe &p, const Frag
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int WB>
-__device__ __forceinline__ void group_first(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f) {
+template <int WB, class SK>
+__device__ __forceinline__ void group_first(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f,
+                                            const SK &sk) {
     issue_block<WB>(p, f, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 1; j < WB * WB; ++j) pair<WB>(acc, p, f, j);
+    for (int j = 1; j < WB * WB; ++j) pair<WB>(acc, p, f, j, sk);
 }
-template <int WB>
-__device__ __forceinline__ void group_second(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f) {
+template <int WB, class SK>
+__device__ __forceinline__ void group_second(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f,
+                                             const SK &sk) {
 #pragma unroll
-    for (int j = WB * WB; j < 2 * WB * WB; ++j) pair<WB>(acc, p, f, j);
+    for (int j = WB * WB; j < 2 * WB * WB; ++j) pair<WB>(acc, p, f, j, sk);
 }
-template <int WB>
-__device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p) {
+template <int WB, class SK>
+__device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p, const SK &sk) {
     constexpr int NB = WB * WB;
-    valu_block<NB>(acc, p, NB - 1, 1);
+    valu_block<NB>(acc, p, 2 * NB - 1, sk);
     asm volatile("" : "+v"(acc[NB - 1]));
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -316,13 +347,15 @@ __device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p) {
 // the compiler can tell a read of one stage from the copies still landing in
 // the others (otherwise every LDS read would wait for all copies).  ODD: the
 // group count is odd, so the last stage holds one group (a compile-time
-// choice, so that an even count carries no per-stage selects for it).
-template <int WB, bool ODD>
+// choice, so that an even count carries no per-stage selects for it).  SK:
+// what the VALU does with the group sums (NoSink: the rescale; TakeGroup:
+// capture the sums of group sink.gsel).
+template <int WB, bool ODD, class SK = NoSink>
 __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__restrict__ b1,
                                        uint8_t *__restrict__ b2, uint8_t *__restrict__ b3,
                                        const CopyPlan<WB> &cp, const ReadPlan &rp,
                                        const Operands &op, int ns,
-                                       f32x16 (&acc)[WB * WB]) {
+                                       f32x16 (&acc)[WB * WB], SK sink = SK{}) {
     constexpr bool odd = ODD;
     constexpr int L = Cfg<WB>::LOADS;
     // prologue: stages 0..3 in flight, stage 0 visible, group 0 in registers
@@ -343,9 +376,11 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
     // while the first group of stage s + 1 is read.
     auto step = [&](int s, uint8_t *cur, uint8_t *nxt) {
         Pipe p;
+        SK sk = sink;
+        if constexpr (SK::on) sk.gsel = sink.gsel - 2 * s;
         read_raw<WB>(raw, cur, rp, 1);
         __builtin_amdgcn_sched_barrier(0);
-        group_first<WB>(acc, p, f);
+        group_first<WB>(acc, p, f, sk);
         make_frags<WB>(f, raw, rp.keep_b && !(odd && s == ns - 1));
         wait_next_stage<L>(s, ns);
         barrier();
@@ -354,9 +389,9 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
         // so the fragments carry no merge of old and new values)
         read_raw<WB>(raw, nxt, rp, 0);
         __builtin_amdgcn_sched_barrier(0);
-        group_second<WB>(acc, p, f);
+        group_second<WB>(acc, p, f, sk);
         make_frags<WB>(f, raw, rp.keep_b);
-        group_drain<WB>(acc, p);
+        group_drain<WB>(acc, p, sk);
     };
     for (int s = 0; s < ns; s += 4) {
         step(s, b0, b1);
@@ -887,8 +922,16 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
     }
 }
 
-// Output epilogues of a tile.
-enum { EPI_STORE = 0, EPI_QKV = 1, EPI_MLP = 2 };
+// Output epilogues of a tile.  EPI_SUMS is the group-sum test hook: the K
+// loop captures the exact sums of one group (TakeGroup) and the tile stores
+// them as int32 instead of running the rescale and the epilogue.
+enum { EPI_STORE = 0, EPI_QKV = 1, EPI_MLP = 2, EPI_SUMS = 3 };
+
+struct SumsArgs {
+    int32_t *S;             // [btm, btn, G]: S[i][j][g] of rows bm0 + i, columns bn0 + j
+    int64_t bm0, bn0, btm, btn;
+    int G, g;               // group count, the group this launch captures
+};
 
 // One output tile: 128 x 128 (WB = 2) or 64 x 64 (WB = 1) at (m0, n0).
 // EPI_STORE: bias, activation, the [M, N] bf16 store; EPI_QKV: the fused QKV
@@ -992,7 +1035,30 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
 #pragma unroll
     for (int t = 0; t < NB; ++t) acc[t] = f32x16{};
 
-    if constexpr (MXF)
+    if constexpr (EPI == EPI_SUMS) {
+        // the production K loop, with the sums of group sg.g kept instead of
+        // rescaled; stored as exact int32 for the requested block
+        const SumsArgs &sg = *static_cast<const SumsArgs *>(epi);
+        const TakeGroup tg{sg.g};
+        if (odd)
+            k_loop<WB, true, TakeGroup>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3],
+                                        cp, rp, op, ns, acc, tg);
+        else
+            k_loop<WB, false, TakeGroup>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3],
+                                         cp, rp, op, ns, acc, tg);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            const int bi = t / WB, bj = t % WB;
+            const int64_t mi = m0 + wm * 32 * WB + 32 * bj + r32 - sg.bm0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int64_t ni = n0 + wn * 32 * WB + 32 * bi + 8 * (i / 4) + 4 * ks2 + (i % 4) - sg.bn0;
+                if (mi >= 0 && mi < sg.btm && ni >= 0 && ni < sg.btn)
+                    sg.S[(mi * sg.btn + ni) * sg.G + sg.g] = (int32_t)acc[t][i];
+            }
+        }
+        return;
+    } else if constexpr (MXF)
         k_loop_mx<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ss, ns,
                       acc);
     else if (odd)

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 1
+#define SVDQ_ABI_VERSION 2
 #define SVDQ_GROUP 64      /* quantization group along K */
 #define SVDQ_MAX_RANK 128  /* largest supported low-rank r */
 /* Size limits, so that every offset the kernels form within a tile fits its
@@ -117,6 +117,21 @@ const char *svdq_last_error(void);
  */
 int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, float *sw,
                           void *stream);
+
+/*
+ * Weight codes already quantized elsewhere (e.g. a checkpoint's packed INT4
+ * residual) in the common row-major form -> the stored layout above.
+ *   codes  device u8 [N, K/2]  two's-complement nibbles, element 2j in the
+ *                              low nibble of byte j, codes in [-7, 7] (a -8
+ *                              nibble is stored as -7)
+ *   qw     device u8 [ceil(N/2), K] packed codes, row pairs (out)
+ * The group scales keep their layout (fp32 [N, K/64]) and are used as they
+ * are.  A pure re-arrangement: svdq_pack_weights(R) equals this applied to
+ * the row-major codes of the same quantization.  N >= 0 (0: no-op),
+ * K % 64 == 0, K >= 64.
+ */
+int32_t svdq_repack_weights(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
+                            void *stream);
 
 /*
  * Workspace bytes svdq_quantize_act_down needs: when K spans more than one
@@ -353,14 +368,19 @@ int32_t svdq_mx_linear(const uint16_t *X, const float *lambda, const uint16_t *L
                        int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * Test hook: the exact per-group integer sums of a block, computed with the
- * same operand unpacking and int8 matrix instructions as the GEMM.
+ * Test hook: the exact per-group integer sums of a block, taken from the
+ * GEMM's own tile code (the same global -> LDS staging, code layout, FP8
+ * operand form and matrix instruction as svdq_w4a4_lr_gemm; 128 x 128 tiles,
+ * or 64 x 64 under SVDQ_TILES_QUARTER), one launch per group of 64.
+ *   qa, sa, qw, sw  device codes and scales as svdq_w4a4_lr_gemm takes them
+ *                   (the scales are staged as in the GEMM; the sums do not
+ *                   depend on them)
  *   S  device int32 [tm, tn, K/64]: S[i][j][g] = sum_{k in g} qa[m0+i][k] qw[n0+j][k]
  * Requires 0 <= m0, m0 + tm <= M, 0 <= n0, n0 + tn <= N.
  */
-int32_t svdq_debug_group_sums(const uint8_t *qa, const uint8_t *qw, int64_t M, int64_t N,
-                              int64_t K, int64_t m0, int64_t n0, int64_t tm, int64_t tn,
-                              int32_t *S, void *stream);
+int32_t svdq_debug_group_sums(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                              const float *sw, int64_t M, int64_t N, int64_t K, int64_t m0,
+                              int64_t n0, int64_t tm, int64_t tn, int32_t *S, void *stream);
 
 /* ------------------------------------------------------------------
  * 4-bit weights, 16-bit activations (W4A16).  The blog "Bringing Nunchaku
@@ -436,8 +456,8 @@ int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *packed, const ui
  *                      of at most three quarters of them (the default)
  *   SVDQ_TILES_FULL    128 x 128 tiles only
  *   SVDQ_TILES_QUARTER 64 x 64 tiles only
- * Process-wide; results are identical under every policy (it only moves
- * tiles between two kernels that compute the same thing).  Returns
+ * Process-wide; results are identical under every policy (both tile shapes
+ * run the same per-output arithmetic in the same order).  Returns
  * SVDQ_ERR_INVALID_ARG for any other value.
  */
 #define SVDQ_TILES_AUTO 0

@@ -35,14 +35,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     decl = declared_functions()
-    assert len(decl) == 26, decl
+    assert len(decl) == 27, decl
     assert sorted(_binding.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings(lib):
-    assert bdt.svdq_abi_version() == 1
+    assert bdt.svdq_abi_version() == 2
     assert bdt.svdq_status_string(0) == "ok"
     assert bdt.svdq_status_string(MISALIGNED) == "misaligned pointer"
     assert bdt.svdq_status_string(99) == "unknown status"
@@ -122,8 +122,14 @@ def test_pack_and_debug_reject(lib):
     assert lib.svdq_pack_weights(P(A), 8, 100, P(A), P(A), None) == SHAPE
     assert lib.svdq_pack_weights(P(0), 8, 128, P(A), P(A), None) == INVALID
     assert lib.svdq_pack_weights(P(A), 8, 128, P(U), P(A), None) == MISALIGNED
-    assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 128, 8, 0, 16, 16, P(A), None) == INVALID
-    assert lib.svdq_debug_group_sums(P(A), P(A), 16, 16, 100, 0, 0, 16, 16, P(A), None) == SHAPE
+    assert lib.svdq_repack_weights(P(A), -1, 128, P(A), None) == INVALID
+    assert lib.svdq_repack_weights(P(A), 8, 96, P(A), None) == SHAPE
+    assert lib.svdq_repack_weights(P(0), 8, 128, P(A), None) == INVALID
+    assert lib.svdq_repack_weights(P(A), 8, 128, P(U), None) == MISALIGNED
+    assert lib.svdq_debug_group_sums(P(A), P(A), P(A), P(A), 16, 16, 128, 8, 0, 16, 16, P(A), None) == INVALID
+    assert lib.svdq_debug_group_sums(P(A), P(A), P(A), P(A), 16, 16, 100, 0, 0, 16, 16, P(A), None) == SHAPE
+    assert lib.svdq_debug_group_sums(P(A), P(0), P(A), P(A), 16, 16, 128, 0, 0, 16, 16, P(A), None) == INVALID
+    assert lib.svdq_debug_group_sums(P(A), P(A), P(A), P(U), 16, 16, 128, 0, 0, 16, 16, P(A), None) == MISALIGNED
     ap = lib.svdq_awq_pack_weights
     assert ap(P(A), -1, 128, P(A), None) == INVALID
     assert ap(P(A), 8, 96, P(A), None) == SHAPE
@@ -160,7 +166,8 @@ def test_empty_inputs_are_noops(lib):
     assert _gemm(lib, qa=0, sa=0, qw=0, sw=0, xl1=0, L2=0, bias=0, Y=0, M=0) == OK
     assert _lin(lib, X=0, lam=0, L1=0, qw=0, sw=0, L2=0, bias=0, Y=0, ws=0, M=0) == OK
     assert lib.svdq_pack_weights(P(0), 0, 128, P(0), P(0), None) == OK
-    assert lib.svdq_debug_group_sums(P(0), P(0), 16, 16, 128, 0, 0, 0, 5, P(0), None) == OK
+    assert lib.svdq_repack_weights(P(0), 0, 128, P(0), None) == OK
+    assert lib.svdq_debug_group_sums(P(0), P(0), P(0), P(0), 16, 16, 128, 0, 0, 0, 5, P(0), None) == OK
     assert lib.svdq_awq_pack_weights(P(0), 0, 128, P(0), None) == OK
     assert lib.svdq_awq_repack(P(0), P(0), P(0), 0, 128, P(0), None) == OK
     assert lib.svdq_awq_w4a16_linear(P(0), P(0), P(0), 0, 64, 128, P(0), None) == OK

@@ -62,7 +62,7 @@ def test_all_extreme_codes():
     R = np.where(np.arange(K) % 2 == 0, -0.5, 0.5)[None, :].repeat(N, 0).astype(np.float32)
     qa_o, sa_o, _ = oracle.quantize_act(X, lam)
     qw_o, sw_o = oracle.pack_weights(R)
-    S = bdt.group_sums(pdev(qa_o), pdev(qw_o), M, N, 0, 0, M, N).cpu().numpy()
+    S = bdt.group_sums(pdev(qa_o), to_dev(sa_o), pdev(qw_o), to_dev(sw_o), M, N, 0, 0, M, N).cpu().numpy()
     assert np.all(S == -3136)
     Y = bdt.w4a4_lr_gemm(pdev(qa_o), to_dev(sa_o), pdev(qw_o), to_dev(sw_o), None, None, None)
     _, y_or = oracle.gemm_rows(qa_o, sa_o, qw_o, sw_o, None, None, None, 0, K)
@@ -125,3 +125,55 @@ def test_errors_surface_through_binding():
     qw, sw = bdt.pack_weights(to_dev(L.R))
     torch.cuda.synchronize()
     assert bdt.svdq_last_error() == ""
+
+
+def test_repack_minus_eight_is_stored_as_minus_seven():
+    # -8 is outside the symmetric code range; the repack stores it as -7
+    rng = np.random.default_rng(12)
+    N, K = 6, 256
+    c = rng.integers(-7, 8, size=(N, K))
+    c[:, ::64] = 7                                   # scale 1 per group in the reference packing
+    m8 = rng.random((N, K)) < 0.1
+    m8[:, ::64] = False
+    raw = np.where(m8, -8, c)
+    tc = ((raw[:, 0::2] & 0xF) | ((raw[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+    want, scales = oracle.quantize_groups(np.where(m8, -7, c).astype(np.float32))
+    assert np.all(scales == 1.0)
+    qw = bdt.repack_weights(to_dev(tc))
+    assert np.array_equal(from_pairs(qw, N), want)
+
+
+@pytest.mark.parametrize("eta", [0.3, 0.1, 0.03])
+def test_rescale_precision_under_cancelling_groups(eta):
+    # Per-group terms sa sw S of alternating sign and nearly equal size, so that the
+    # output is a small remainder of large terms: with |S_g| ~ 3000 for every group,
+    # sa = a (1 + e), sw = b (1 + d), e, d ~ U(-eta, eta), sum_g |term| / rms(Y) is about
+    # 17 / eta (57x, 170x, 570x).  The GPU forms sw sa as a bf16 hi/lo product on the
+    # matrix unit (relative error ~2^-17, at most 2^-15 per term); the expected
+    # |err| / tol is about 0.01 / eta, so these cases stay inside the tolerance, and the
+    # observed error must also stay inside that product's own bound.
+    rng = np.random.default_rng(int(eta * 1000))
+    M, N, K = 64, 64, 12288
+    G = K // 64
+    a = rng.choice([-7, -6, 6, 7], size=(1, K))                # one code row for every token
+    a[:, ::64] = 7
+    qa_codes = np.repeat(a, M, axis=0)
+    sign = np.where(np.arange(G) % 2 == 0, 1, -1)
+    w = np.repeat(a * np.repeat(sign, 64)[None, :], N, axis=0)   # S_g = (-1)^g sum a_g^2
+    qa_o, s1 = oracle.quantize_groups(qa_codes.astype(np.float32))
+    qw_o, s2 = oracle.quantize_groups(w.astype(np.float32))
+    assert np.all(s1 == 1.0) and np.all(s2 == 1.0)
+    sa = (rng.uniform(0.5, 2.0, (M, 1)) * (1 + rng.uniform(-eta, eta, (M, G)))).astype(np.float32)
+    sw = (rng.uniform(0.5, 2.0, (N, 1)) * (1 + rng.uniform(-eta, eta, (N, G)))).astype(np.float32)
+    Y = bdt.w4a4_lr_gemm(pdev(qa_o), to_dev(sa), pdev(qw_o), to_dev(sw), None, None, None)
+    acc, y_or = oracle.gemm_rows(qa_o, sa, qw_o, sw, None, None, None, 0, K)
+    S = (qa_codes.reshape(M, G, 64)[0] ** 2).sum(axis=1) * sign          # [G]
+    terms = np.abs(sa.astype(np.float64))[:, None, :] * np.abs(sw.astype(np.float64))[None, :, :] \
+        * np.abs(S)[None, None, :]
+    yg = bf16_host(Y)
+    worst = assert_y_close(yg, y_or, "cancelling groups")
+    yv = (yg.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = 2.0 ** -15 * terms.sum(axis=2) + np.abs(acc) * 2.0 ** -8 + 1e-30
+    assert np.all(np.abs(yv - acc) <= bound)
+    ratio = float(terms.sum(axis=2).mean() / np.sqrt(np.mean(acc ** 2)))
+    print("eta %.2f: sum|terms| / rms(Y) = %.0f, worst |err|/tol = %.3f" % (eta, ratio, worst))

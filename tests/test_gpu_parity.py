@@ -51,6 +51,21 @@ def test_pack_weights_bit_exact(case):
     assert np.array_equal(sw.cpu().numpy().view(np.uint32), case["sw"].view(np.uint32))
 
 
+def _twos_complement_bytes(codes):
+    """Integer codes [rows, K] -> the common row-major INT4 form: two's-complement nibbles,
+    element 2j in the low nibble of byte j."""
+    c = np.asarray(codes, np.int64)
+    return ((c[:, 0::2] & 0xF) | ((c[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+
+
+def test_repack_weights_bit_exact(case):
+    # codes of the oracle's quantization in the common row-major form -> the stored layout
+    N, K = case["N"], case["K"]
+    tc = _twos_complement_bytes(oracle.unpack(case["qw"], K))
+    qw = bdt.repack_weights(to_dev(tc))
+    assert np.array_equal(from_pairs(qw, N), case["qw"])
+
+
 def test_quantize_act_down(case):
     L, r = case["L"], case["r"]
     qa, sa, xl1 = bdt.quantize_act_down(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None)
@@ -63,20 +78,23 @@ def test_quantize_act_down(case):
         assert xl1 is None
 
 
-def test_group_sums_bit_exact(case):
-    M, N, K = case["M"], case["N"], case["K"]
-    qa, qw = pdev(case["qa"]), pdev(case["qw"])
-    for (m0, tm, n0, tn) in [(0, M, 0, N), (M // 3, M - M // 3, N // 5, min(37, N - N // 5))]:
-        S = bdt.group_sums(qa, qw, M, N, m0, n0, tm, tn).cpu().numpy()
-        ref = oracle.group_sums(case["qa"], case["qw"], K, m0, n0, tm, tn)
-        assert np.array_equal(S, ref)
-
-
 @pytest.fixture(params=[bdt.TILES_FULL, bdt.TILES_QUARTER], ids=["full_tiles", "quarter_tiles"])
 def tiles(request):
     bdt.svdq_debug_set_tile_policy(request.param)
     yield request.param
     bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
+
+
+def test_group_sums_bit_exact(case, tiles):
+    # the sums come out of the GEMM's own K loop (LDS ring, swizzle, row-pair copies,
+    # odd-group tail stage) on 128 x 128 or 64 x 64 tiles
+    M, N, K = case["M"], case["N"], case["K"]
+    qa, qw = pdev(case["qa"]), pdev(case["qw"])
+    sa, sw = to_dev(case["sa"]), to_dev(case["sw"])
+    for (m0, tm, n0, tn) in [(0, M, 0, N), (M // 3, M - M // 3, N // 5, min(37, N - N // 5))]:
+        S = bdt.group_sums(qa, sa, qw, sw, M, N, m0, n0, tm, tn).cpu().numpy()
+        ref = oracle.group_sums(case["qa"], case["qw"], K, m0, n0, tm, tn)
+        assert np.array_equal(S, ref)
 
 
 def test_gemm_stagewise(case, tiles):
