@@ -21,7 +21,7 @@ from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError, 
                        svdq_awq_packed_bytes, svdq_awq_repack,
                        svdq_awq_w4a16_linear, svdq_debug_group_sums,
                        svdq_debug_set_tile_policy,
-                       svdq_last_error, svdq_linear, svdq_linear_workspace_bytes,
+                       svdq_last_error, svdq_linear, svdq_linear_noalloc, svdq_linear_workspace_bytes,
                        svdq_pack_weights, svdq_repack_weights, svdq_quantize_act_down,
                        svdq_quantize_act_down_workspace_bytes, svdq_status_string,
                        svdq_w4a4_lr_gemm, svdq_w4a4_lr_gemm_qkv, svdq_linear_qkv,

@@ -27,7 +27,7 @@ GROUP = 64
 # Every symbol declared in include/svdq.h.
 EXPORTS = (
     "svdq_abi_version", "svdq_status_string", "svdq_last_error", "svdq_pack_weights",
-    "svdq_repack_weights",
+    "svdq_repack_weights", "svdq_linear_noalloc",
     "svdq_quantize_act_down_workspace_bytes", "svdq_quantize_act_down", "svdq_w4a4_lr_gemm",
     "svdq_linear_workspace_bytes", "svdq_linear", "svdq_debug_group_sums",
     "svdq_debug_set_tile_policy", "svdq_awq_packed_bytes", "svdq_awq_pack_weights",
@@ -92,6 +92,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_w4a4_lr_gemm": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P], I32),
         "svdq_linear_workspace_bytes": ([I64, I64, I32], SZ),
         "svdq_linear": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P, SZ, P], I32),
+        "svdq_linear_noalloc": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P], I32),
         "svdq_debug_group_sums": ([P, P, P, P, I64, I64, I64, I64, I64, I64, I64, P, P], I32),
         "svdq_debug_set_tile_policy": ([I32], I32),
         "svdq_awq_packed_bytes": ([I64, I64], I64),
@@ -194,6 +195,15 @@ def svdq_linear(X, lam, L1, qw, sw, L2, bias, act, M, N, K, r, Y, workspace, ws_
     _check(load_library().svdq_linear(
         _p(X), _p(lam), _p(L1), _p(qw), _p(sw), _p(L2), _p(bias), act, M, N, K, r, _p(Y),
         _p(workspace), ws_bytes, _stream(stream)), "svdq_linear")
+
+
+def svdq_linear_noalloc(X, lam, L1, qw, sw, L2, bias, act, M, N, K, r, Y, stream=None):
+    _check(load_library().svdq_linear_noalloc(
+        _p(X), _p(lam), _p(L1), _p(qw), _p(sw), _p(L2), _p(bias), act, M, N, K, r, _p(Y),
+        _stream(stream)), "svdq_linear_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def svdq_debug_group_sums(qa, sa, qw, sw, M, N, K, m0, n0, tm, tn, S, stream=None):

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "svdq.h"
 #include "svdq_internal.h"
@@ -236,6 +237,38 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r, bool m
 
 }  // namespace
 
+// Scratch of svdq_linear_noalloc: the layer's intermediates (codes, scales,
+// x^ L1 and the down-projection's partial sums) for callers that cannot
+// allocate.  Each device holds its own copy from module load to process end.
+// Host code uses only the per-device address from hipGetSymbolAddress, never
+// the array's name (which is a host-side stand-in).
+static __device__ __align__(256) uint8_t scratch[SVDQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) on its first use.
+int32_t scratch_address(void **out) {
+    int dev = -1;
+    SVDQ_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SVDQ_ERR_HIP, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        SVDQ_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                            "hipGetSymbolAddress(scratch)"));
+        if (!p) return fail(SVDQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SVDQ_OK;
+}
+
+}  // namespace
+
 namespace {
 
 int32_t check_awq_pack_shape(int64_t N, int64_t K) {
@@ -439,6 +472,45 @@ int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
     SVDQ_TRY(check_device());
     hipStream_t s = (hipStream_t)stream;
     const LinearWorkspace w = carve_linear(workspace, M, K, r);
+    const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.down, M, K, r);
+    SVDQ_TRY(hip_status(svdq::launch_quant_down(X, lambda, L1, M, K, r, dw, w.qa, w.sa, w.xl1,
+                                                s),
+                        "quantize_act_down launch"));
+    return hip_status(svdq::launch_w4a4_gemm(w.qa, w.sa, qw, sw, w.xl1, L2, bias, act, M, N, K,
+                                             r, Y, s),
+                      "w4a4_lr_gemm launch");
+}
+
+int32_t svdq_linear_noalloc(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                            const uint8_t *qw, const float *sw, const uint16_t *L2,
+                            const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                            int32_t r, uint16_t *Y, void *stream) {
+    g_last_error[0] = 0;
+    SVDQ_TRY(check_rows(M, "M"));
+    if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU)
+        return fail(SVDQ_ERR_INVALID_ARG, "unknown activation %d", act);
+    SVDQ_TRY(check_n(N));
+    SVDQ_TRY(check_k(K));
+    SVDQ_TRY(check_r(r));
+    if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(need_ptr(X, "X"));
+    SVDQ_TRY(need_ptr(lambda, "lambda"));
+    SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
+    SVDQ_TRY(need_ptr(Y, "Y"));
+    SVDQ_TRY(lr_ptrs(L1, "L1", L2, "L2", r));
+    if (bias && !aligned16(bias)) return fail(SVDQ_ERR_MISALIGNED, "bias is not 16-byte aligned");
+    const size_t need = carve_linear(nullptr, M, K, r).bytes;
+    if (need > (size_t)SVDQ_NOALLOC_SCRATCH_BYTES)
+        return fail(SVDQ_ERR_WORKSPACE_TOO_SMALL,
+                    "M = %lld, K = %lld, r = %d needs %zu bytes of scratch; the allocation-free "
+                    "entry point holds %zu (use svdq_linear with a workspace)",
+                    (long long)M, (long long)K, r, need, (size_t)SVDQ_NOALLOC_SCRATCH_BYTES);
+    SVDQ_TRY(check_device());
+    void *base = nullptr;
+    SVDQ_TRY(scratch_address(&base));
+    hipStream_t s = (hipStream_t)stream;
+    const LinearWorkspace w = carve_linear(base, M, K, r);
     const svdq::DownWorkspace dw = svdq::carve_down_workspace(w.down, M, K, r);
     SVDQ_TRY(hip_status(svdq::launch_quant_down(X, lambda, L1, M, K, r, dw, w.qa, w.sa, w.xl1,
                                                 s),

@@ -195,6 +195,27 @@ int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
                     const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
                     int32_t r, uint16_t *Y, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * svdq_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the intermediates that svdq_linear carves out of the caller's workspace
+ * live instead in a static device array of SVDQ_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, one per device, held from the library's load until the
+ * process ends.  The call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine).  Arguments as svdq_linear, without the
+ * workspace.  Shapes whose svdq_linear_workspace_bytes(M, K, r) exceeds
+ * SVDQ_NOALLOC_SCRATCH_BYTES are rejected with SVDQ_ERR_WORKSPACE_TOO_SMALL
+ * before anything runs.  Every call on one device shares that device's
+ * array: calls that overlap in time on one device (other streams, other
+ * threads) race and must be serialized by the caller.  No part of the array
+ * needs to start at zero.  Results are bitwise identical to svdq_linear's.
+ */
+#define SVDQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int32_t svdq_linear_noalloc(const uint16_t *X, const float *lambda, const uint16_t *L1,
+                            const uint8_t *qw, const float *sw, const uint16_t *L2,
+                            const uint16_t *bias, int32_t act, int64_t M, int64_t N, int64_t K,
+                            int32_t r, uint16_t *Y, void *stream);
+
 /* ------------------------------------------------------------------
  * Fused QKV epilogue.  The blog "Bringing Nunchaku 4-bit inference to
  * Diffusers" (its section on the structural rewrites, the to_q / to_k /

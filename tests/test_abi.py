@@ -35,7 +35,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     decl = declared_functions()
-    assert len(decl) == 27, decl
+    assert len(decl) == 28, decl
     assert sorted(_binding.EXPORTS) == decl
     for name in decl:
         assert hasattr(lib, name), name
@@ -152,6 +152,27 @@ def test_pack_and_debug_reject(lib):
     assert aw(P(A), P(A), P(A), 2, 64, 128, P(U), None) == MISALIGNED
     assert lib.svdq_debug_set_tile_policy(3) == INVALID
     assert lib.svdq_debug_set_tile_policy(-1) == INVALID
+
+
+def test_noalloc_rejects(lib):
+    nl = lib.svdq_linear_noalloc
+
+    def call(X=A, lam=A, L1=A, qw=A, sw=A, L2=A, bias=0, act=0, M=16, N=16, K=128, r=16, Y=A):
+        return nl(P(X), P(lam), P(L1), P(qw), P(sw), P(L2), P(bias), act, M, N, K, r, P(Y), None)
+
+    assert call(M=-1) == INVALID
+    assert call(act=3) == INVALID
+    assert call(N=12) == SHAPE
+    assert call(r=17) == SHAPE
+    assert call(X=0) == INVALID
+    assert call(L2=0) == INVALID
+    assert call(Y=U) == MISALIGNED
+    assert call(M=0, X=0, lam=0, L1=0, qw=0, sw=0, L2=0, Y=0) == OK
+    # more intermediates than the library's static scratch holds: refused before any launch
+    big_m = 1 << 20
+    assert lib.svdq_linear_workspace_bytes(big_m, 3072, 32) > _binding.NOALLOC_SCRATCH_BYTES
+    assert call(M=big_m, K=3072, r=32, N=3072) == WS_SMALL
+    assert b"scratch" in lib.svdq_last_error()
 
 
 def test_tile_policy_values_accepted(lib):
