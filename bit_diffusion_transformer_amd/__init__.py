@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 from ._binding import (ACT_GELU, ACT_NONE, EXPORTS, GROUP, LIB_PATH, SVDQError,  # noqa: F401
-                       QkvEpilogue, TILES_AUTO, TILES_FULL, TILES_QUARTER, qkv_epilogue,
+                       QkvEpilogue, TILES_AUTO, TILES_FULL, TILES_QUARTER, TILES_KSPLIT,
+                       TILES_KSPLIT_QUARTER, qkv_epilogue,
                        load_library, svdq_abi_version, svdq_awq_pack_weights,
                        svdq_awq_packed_bytes, svdq_awq_repack,
                        svdq_awq_w4a16_linear, svdq_debug_group_sums,
@@ -59,6 +60,17 @@ def pair_rows(rows: int) -> int:
     return (rows + 1) // 2
 
 
+def scale_shape(rows: int, K: int):
+    """Shape of INT4 group scales stored stage-major: [ceil(K/128), rows, 2] fp32 (the scale
+    of (row i, group g) at [g // 2, i, g % 2]; an odd group count's last pair padded)."""
+    return ((K // GROUP + 1) // 2, int(rows), 2)
+
+
+def scale_rows(s: torch.Tensor) -> int:
+    """Row count of stage-major INT4 group scales."""
+    return int(s.shape[1])
+
+
 def _codes_of(q: torch.Tensor, rows: int, K: int, what: str) -> None:
     if tuple(q.shape) != (pair_rows(rows), K) or q.dtype != torch.uint8:
         raise ValueError("%s: expected uint8 row-pair codes of shape %s, got %s %s"
@@ -66,20 +78,23 @@ def _codes_of(q: torch.Tensor, rows: int, K: int, what: str) -> None:
 
 
 def pack_weights(R: torch.Tensor):
-    """Residual fp32 [N, K] -> (qw uint8 [ceil(N/2), K] row pairs, sw fp32 [N, K/64])."""
+    """Residual fp32 [N, K] -> (qw uint8 [ceil(N/2), K] row pairs, sw fp32 stage-major
+    [ceil(K/128), N, 2])."""
     N, K = R.shape
     qw = torch.empty((pair_rows(N), K), dtype=torch.uint8, device=R.device)
-    sw = torch.empty((N, K // GROUP), dtype=torch.float32, device=R.device)
+    sw = torch.empty(scale_shape(N, K), dtype=torch.float32, device=R.device)
     svdq_pack_weights(R, N, K, qw, sw)
     return qw, sw
 
 
-def repack_weights(codes: torch.Tensor) -> torch.Tensor:
-    """Row-major two's-complement INT4 codes uint8 [N, K/2] -> qw uint8 [ceil(N/2), K]."""
+def repack_weights(codes: torch.Tensor, scales: torch.Tensor):
+    """Row-major two's-complement INT4 codes uint8 [N, K/2] and fp32 scales [N, K/64] ->
+    (qw uint8 [ceil(N/2), K], sw fp32 stage-major [ceil(K/128), N, 2])."""
     N, K = codes.shape[0], codes.shape[1] * 2
     qw = torch.empty((pair_rows(N), K), dtype=torch.uint8, device=codes.device)
-    svdq_repack_weights(codes, N, K, qw)
-    return qw
+    sw = torch.empty(scale_shape(N, K), dtype=torch.float32, device=codes.device)
+    svdq_repack_weights(codes, scales, N, K, qw, sw)
+    return qw, sw
 
 
 def awq_pack_weights(W: torch.Tensor) -> torch.Tensor:
@@ -107,13 +122,13 @@ def awq_linear(X: torch.Tensor, packed: torch.Tensor, N: int, bias=None) -> torc
 
 
 def quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Tensor]):
-    """X bf16 [M, K] -> (qa uint8 [ceil(M/2), K] row pairs, sa fp32 [M, K/64], xl1 fp32 [M, r]
-    or None)."""
+    """X bf16 [M, K] -> (qa uint8 [ceil(M/2), K] row pairs, sa fp32 stage-major
+    [ceil(K/128), M, 2], xl1 fp32 [M, r] or None)."""
     M, K = X.shape
     r = _rank(L1, 1)
     dev = X.device
     qa = torch.empty((pair_rows(M), K), dtype=torch.uint8, device=dev)
-    sa = torch.empty((M, K // GROUP), dtype=torch.float32, device=dev)
+    sa = torch.empty(scale_shape(M, K), dtype=torch.float32, device=dev)
     xl1 = torch.empty((M, r), dtype=torch.float32, device=dev) if r > 0 else None
     ws_bytes = svdq_quantize_act_down_workspace_bytes(M, K, r)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -124,7 +139,7 @@ def quantize_act_down(X: torch.Tensor, lam: torch.Tensor, L1: Optional[torch.Ten
 
 def w4a4_lr_gemm(qa, sa, qw, sw, xl1, L2, bias, act: int = ACT_NONE) -> torch.Tensor:
     """The W4A4 GEMM with the low-rank up-projection, bias and act -> Y bf16 [M, N]."""
-    M, N, K = sa.shape[0], sw.shape[0], qa.shape[1]
+    M, N, K = scale_rows(sa), scale_rows(sw), qa.shape[1]
     _codes_of(qa, M, K, "qa")
     _codes_of(qw, N, K, "qw")
     r = _rank(L2, 0)
@@ -138,7 +153,7 @@ def linear(X, lam, L1, qw, sw, L2, bias, act: int = ACT_NONE,
            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer (svdq_linear) -> Y bf16 [M, N]."""
     M, K = X.shape
-    N = sw.shape[0]
+    N = scale_rows(sw)
     _codes_of(qw, N, K, "qw")
     r = _rank(L1, 1)
     need = svdq_linear_workspace_bytes(M, K, r)
@@ -159,9 +174,9 @@ def _qkv_out(M, heads, head_dim, seq, device):
 def w4a4_lr_gemm_qkv(qa, sa, qw, sw, xl1, L2, bias, heads: int, head_dim: int, seq: int,
                      gamma_q, gamma_k, eps: float, cos_t, sin_t):
     """The GEMM with the fused QKV epilogue -> (Q, K, V) bf16 [M/seq, heads, seq, head_dim]."""
-    M, K = sa.shape[0], qa.shape[1]
+    M, K = scale_rows(sa), qa.shape[1]
     _codes_of(qa, M, K, "qa")
-    _codes_of(qw, sw.shape[0], K, "qw")
+    _codes_of(qw, scale_rows(sw), K, "qw")
     r = _rank(L2, 0)
     Q, Kt, V = _qkv_out(M, heads, head_dim, seq, qa.device)
     epi = qkv_epilogue(heads, head_dim, seq, _bits(gamma_q), _bits(gamma_k), eps, cos_t, sin_t,
@@ -175,7 +190,7 @@ def linear_qkv(X, lam, L1, qw, sw, L2, bias, heads: int, head_dim: int, seq: int
                gamma_k, eps: float, cos_t, sin_t, workspace: Optional[torch.Tensor] = None):
     """The whole fused QKV layer (svdq_linear_qkv) -> (Q, K, V) bf16 [M/seq, heads, seq, D]."""
     M, K = X.shape
-    _codes_of(qw, sw.shape[0], K, "qw")
+    _codes_of(qw, scale_rows(sw), K, "qw")
     r = _rank(L1, 1)
     need = svdq_linear_workspace_bytes(M, K, r)
     if workspace is None or workspace.numel() < need:
@@ -190,14 +205,14 @@ def linear_qkv(X, lam, L1, qw, sw, L2, bias, heads: int, head_dim: int, seq: int
 
 def w4a4_lr_gemm_quant_down(qa, sa, qw, sw, xl1, L2, bias, act, lambda_next, L1_next):
     """The GEMM whose output feeds the next layer -> that layer's (qa, sa, xl1)."""
-    M, N, K = sa.shape[0], sw.shape[0], qa.shape[1]
+    M, N, K = scale_rows(sa), scale_rows(sw), qa.shape[1]
     _codes_of(qa, M, K, "qa")
     _codes_of(qw, N, K, "qw")
     r = _rank(L2, 0)
     rn = _rank(L1_next, 1)
     dev = qa.device
     qa_n = torch.empty((pair_rows(M), N), dtype=torch.uint8, device=dev)
-    sa_n = torch.empty((M, N // GROUP), dtype=torch.float32, device=dev)
+    sa_n = torch.empty(scale_shape(M, N), dtype=torch.float32, device=dev)
     xl1_n = torch.empty((M, rn), dtype=torch.float32, device=dev) if rn > 0 else None
     need = svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, rn)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -212,7 +227,7 @@ def mlp(X, up: dict, down: dict, act: int = ACT_GELU,
         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = down(act(up(X))) through svdq_mlp; up / down: dicts with lam, L1, qw, sw, L2, bias."""
     M, K = X.shape
-    Nh = up["sw"].shape[0]
+    Nh = scale_rows(up["sw"])
     _codes_of(up["qw"], Nh, K, "up qw")
     _codes_of(down["qw"], K, Nh, "down qw")
     ru, rd = _rank(up["L1"], 1), _rank(down["L1"], 1)
@@ -264,7 +279,7 @@ class SVDQLinear:
 
     @property
     def out_features(self) -> int:
-        return self.sw.shape[0]
+        return scale_rows(self.sw)
 
     def __call__(self, X: torch.Tensor) -> torch.Tensor:
         M, K = X.shape

@@ -86,7 +86,7 @@ def load_library(build_if_missing: bool = True) -> ctypes.CDLL:
         "svdq_status_string": ([I32], ctypes.c_char_p),
         "svdq_last_error": ([], ctypes.c_char_p),
         "svdq_pack_weights": ([P, I64, I64, P, P, P], I32),
-        "svdq_repack_weights": ([P, I64, I64, P, P], I32),
+        "svdq_repack_weights": ([P, P, I64, I64, P, P, P], I32),
         "svdq_quantize_act_down_workspace_bytes": ([I64, I64, I32], SZ),
         "svdq_quantize_act_down": ([P, P, P, I64, I64, I32, P, P, P, P, SZ, P], I32),
         "svdq_w4a4_lr_gemm": ([P, P, P, P, P, P, P, I32, I64, I64, I64, I32, P, P], I32),
@@ -160,9 +160,9 @@ def svdq_last_error() -> str:
     return load_library().svdq_last_error().decode(errors="replace")
 
 
-def svdq_repack_weights(codes, N, K, qw, stream=None):
-    _check(load_library().svdq_repack_weights(_p(codes), N, K, _p(qw), _stream(stream)),
-           "svdq_repack_weights")
+def svdq_repack_weights(codes, scales, N, K, qw, sw, stream=None):
+    _check(load_library().svdq_repack_weights(_p(codes), _p(scales), N, K, _p(qw), _p(sw),
+                                              _stream(stream)), "svdq_repack_weights")
 
 
 def svdq_pack_weights(R, N, K, qw, sw, stream=None):
@@ -212,7 +212,7 @@ def svdq_debug_group_sums(qa, sa, qw, sw, M, N, K, m0, n0, tm, tn, S, stream=Non
         "svdq_debug_group_sums")
 
 
-TILES_AUTO, TILES_FULL, TILES_QUARTER = 0, 1, 2
+TILES_AUTO, TILES_FULL, TILES_QUARTER, TILES_KSPLIT, TILES_KSPLIT_QUARTER = 0, 1, 2, 3, 4
 
 
 def svdq_debug_set_tile_policy(policy):

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsvdq.so")
 SOURCES = ["svdq_api.hip", "quant_down.hip", "w4a4_gemm.hip", "w4a4_gemm_qkv.hip", "w4a4_gemm_mlp.hip",
-           "w4a4_mx_gemm.hip", "awq_w4a16.hip", "w4a4_gemm_sums.hip"]
+           "w4a4_mx_gemm.hip", "awq_w4a16.hip", "w4a4_gemm_sums.hip", "w4a4_gemm_ks.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

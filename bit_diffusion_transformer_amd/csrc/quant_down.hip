@@ -155,7 +155,11 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
                 const float s = quantize_group16(v, packed);
                 if (row_ok) {
                     *reinterpret_cast<u32x2 *>(qa + code_offset(row, K / 2, g * (kGroup / 2) + 8 * ks)) = packed;
-                    if (ks == 0) static_cast<float *>(sa)[row * G + g] = s;
+                    if (ks == 0) {
+                        float *sp = static_cast<float *>(sa);
+                        sp[scale_index(row, g, M)] = s;
+                        if ((G & 1) && g == G - 1) sp[scale_index(row, G, M)] = 0.0f;   // pad
+                    }
                 }
             }
             if (NT > 0) {
@@ -277,22 +281,28 @@ pack_weights_kernel(const float *__restrict__ R, int64_t N, int64_t K,
             const float s = quantize_group16(v, packed);
             if (row_ok) {
                 *reinterpret_cast<u32x2 *>(qw + code_offset(row, K / 2, g * (kGroup / 2) + 8 * ks)) = packed;
-                if (ks == 0) static_cast<float *>(sw)[row * G + g] = s;
+                if (ks == 0) {
+                    float *sp = static_cast<float *>(sw);
+                    sp[scale_index(row, g, N)] = s;
+                    if ((G & 1) && g == G - 1) sp[scale_index(row, G, N)] = 0.0f;   // pad
+                }
             }
         }
     }
 }
 
 // ------------------------------------------------------------------ repack
-// Already quantized weight codes in the common row-major form (two's
-// complement nibbles, element 2j in the low nibble of byte j, [N, K/2]) ->
-// the stored layout: one thread per block of 16 codes (8 bytes), the same
-// conversion as the quantizers' (store_code_words), written to the row-pair
-// position.  A nibble 8 (-8, outside the symmetric range) is stored as -7.
+// Already quantized weights in the common row-major form (codes: two's
+// complement nibbles, element 2j in the low nibble of byte j, [N, K/2];
+// scales fp32 [N, K/64]) -> the stored layouts: one thread per block of 16
+// codes (8 bytes), the same conversion as the quantizers' (store_code_words),
+// written to the row-pair position; the thread of a group's first block also
+// moves the group's scale (and, for an odd group count, zeroes the pad).  A
+// nibble 8 (-8, outside the symmetric range) is stored as -7.
 __global__ void __launch_bounds__(256)
-repack_codes_kernel(const uint8_t *__restrict__ codes, int64_t N, int64_t K,
-                    uint8_t *__restrict__ qw) {
-    const int64_t kb = K / 2, per_row = K / 16;
+repack_codes_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
+                    int64_t N, int64_t K, uint8_t *__restrict__ qw, float *__restrict__ sw) {
+    const int64_t kb = K / 2, per_row = K / 16, G = K / kGroup;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= N * per_row) return;
     const int64_t row = i / per_row, t = i - row * per_row;
@@ -304,6 +314,11 @@ repack_codes_kernel(const uint8_t *__restrict__ codes, int64_t N, int64_t K,
     };
     *reinterpret_cast<u32x2 *>(qw + code_offset(row, kb, 8 * t)) =
         store_code_words(no_m8(w.x), no_m8(w.y));
+    if ((t & 3) == 0) {
+        const int64_t g = t >> 2;
+        sw[scale_index(row, g, N)] = scales[row * G + g];
+        if ((G & 1) && g == G - 1) sw[scale_index(row, G, N)] = 0.0f;
+    }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -346,10 +361,11 @@ hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl
     return hipGetLastError();
 }
 
-hipError_t launch_repack_codes(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
-                               hipStream_t stream) {
+hipError_t launch_repack_codes(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                               uint8_t *qw, float *sw, hipStream_t stream) {
     const int64_t threads = N * (K / 16);
-    repack_codes_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(codes, N, K, qw);
+    repack_codes_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(codes, scales, N, K,
+                                                                             qw, sw);
     return hipGetLastError();
 }
 

@@ -226,7 +226,7 @@ LinearWorkspace carve_linear(void *base, int64_t M, int64_t K, int32_t r, bool m
     off += align256((size_t)((M + 1) / 2) * (size_t)K);   // row-pair codes
     w.sa = reinterpret_cast<float *>(p + off);
     off += align256(mx ? (size_t)svdq::mx_scale_rows(M) * (size_t)(K / 32)
-                       : (size_t)M * (size_t)(K / SVDQ_GROUP) * 4);
+                       : svdq::scale_floats(M, K / SVDQ_GROUP) * 4);
     w.xl1 = r > 0 ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256((size_t)M * (size_t)r * 4);
     w.down = p + off;
@@ -335,7 +335,7 @@ MlpWorkspace carve_mlp(void *base, int64_t M, int64_t K, int64_t Nh, int32_t r_u
     w.qa_h = reinterpret_cast<uint8_t *>(p + off);
     off += align256((size_t)((M + 1) / 2) * (size_t)Nh);   // row-pair codes
     w.sa_h = reinterpret_cast<float *>(p + off);
-    off += align256((size_t)M * (size_t)(Nh / SVDQ_GROUP) * 4);
+    off += align256(svdq::scale_floats(M, Nh / SVDQ_GROUP) * 4);
     w.xl1_h = r_down > 0 ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256((size_t)M * (size_t)r_down * 4);
     w.part = reinterpret_cast<float *>(p + off);
@@ -379,16 +379,18 @@ int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, flo
                       "pack_weights launch");
 }
 
-int32_t svdq_repack_weights(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
-                            void *stream) {
+int32_t svdq_repack_weights(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                            uint8_t *qw, float *sw, void *stream) {
     g_last_error[0] = 0;
     SVDQ_TRY(check_rows(N, "N"));
     SVDQ_TRY(check_k(K));
     if (N == 0) return SVDQ_OK;
     SVDQ_TRY(need_ptr(codes, "codes"));
+    SVDQ_TRY(need_ptr(scales, "scales"));
     SVDQ_TRY(need_ptr(qw, "qw"));
+    SVDQ_TRY(need_ptr(sw, "sw"));
     SVDQ_TRY(check_device());
-    return hip_status(svdq::launch_repack_codes(codes, N, K, qw, (hipStream_t)stream),
+    return hip_status(svdq::launch_repack_codes(codes, scales, N, K, qw, sw, (hipStream_t)stream),
                       "repack_weights launch");
 }
 
@@ -773,8 +775,8 @@ int32_t svdq_debug_group_sums(const uint8_t *qa, const float *sa, const uint8_t 
 
 int32_t svdq_debug_set_tile_policy(int32_t policy) {
     g_last_error[0] = 0;
-    if (policy != SVDQ_TILES_AUTO && policy != SVDQ_TILES_FULL && policy != SVDQ_TILES_QUARTER)
-        return fail(SVDQ_ERR_INVALID_ARG, "tile policy %d is not one of 0, 1, 2", (int)policy);
+    if (policy < SVDQ_TILES_AUTO || policy > SVDQ_TILES_KSPLIT_QUARTER)
+        return fail(SVDQ_ERR_INVALID_ARG, "tile policy %d is not one of 0 .. 4", (int)policy);
     svdq::set_tile_policy(policy);
     return SVDQ_OK;
 }

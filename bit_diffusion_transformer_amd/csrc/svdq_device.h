@@ -86,6 +86,27 @@ __device__ __forceinline__ f32x16 mfma_mxfp4_32x32x64(u32x4 a, uint32_t sa, u32x
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
+// ---------------------------------------------------------------- GELU
+
+// GELU, erf form: 0.5 x (1 + erf(x / sqrt 2)), with erf from the rational
+// approximation of Abramowitz and Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (after Hastings): for z >= 0,
+//   erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2),
+//   t = 1 / (1 + p z), |error| <= 1.5e-7,
+// and erf(-z) = -erf(z); in fp32 with the hardware reciprocal and 2^x, the
+// result is within about 3e-7 |x| of the exact GELU (far below a bf16 ulp of
+// the output), for a fraction of the instructions of a full-precision erf.
+__device__ __forceinline__ float gelu_erf(float x) {
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
+    float p = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+    p = __builtin_fmaf(t, p, 1.421413741f);
+    p = __builtin_fmaf(t, p, -0.284496736f);
+    p = __builtin_fmaf(t, p, 0.254829592f);
+    const float q = p * t * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);   // 1 - erf(z)
+    return 0.5f * x * (x >= 0.0f ? 2.0f - q : q);
+}
+
 // ---------------------------------------------------------------- 4-bit operands
 // Stored layout of the INT4 codes (qa, qw): two per byte, code e of each block
 // of 16 consecutive codes in nibble e of the block's 8 bytes (element 2j in

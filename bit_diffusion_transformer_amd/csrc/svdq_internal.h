@@ -27,6 +27,16 @@ __host__ __device__ inline int64_t code_offset(int64_t row, int64_t kb, int64_t 
     return (row >> 1) * 2 * kb + (c << 7) + (row & 1) * w + (b & 63);
 }
 
+// INT4 group scales (sa, sw) are stored stage-major: for R rows and G groups,
+// fp32 [ceil(G/2)][R][2], the scale of (row, group g) at
+// ((g / 2) R + row) 2 + g % 2, so that one GEMM stage (two groups) of a tile's
+// rows is one contiguous run of 8 bytes per row.  With an odd G the slots
+// (row, G) of the last stage are padding, written as zero.
+__host__ __device__ inline int64_t scale_index(int64_t row, int64_t g, int64_t R) {
+    return ((g >> 1) * R + row) * 2 + (g & 1);
+}
+inline size_t scale_floats(int64_t R, int64_t G) { return (size_t)((G + 1) / 2) * (size_t)R * 2; }
+
 // svdq_quantize_act_down splits K into chunks of kc groups (one workgroup per
 // 64 rows and chunk); with more than one chunk and r > 0 the chunks' partial
 // x^ L1 sums go to the workspace and a second kernel adds them up.  kc keeps
@@ -63,9 +73,10 @@ hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint1
                              void *sa, float *xl1, hipStream_t stream, bool mx = false);
 hipError_t launch_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, void *sw,
                                hipStream_t stream, bool mx = false);
-// row-major two's-complement INT4 codes [N, K/2] -> the stored row-pair layout
-hipError_t launch_repack_codes(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
-                               hipStream_t stream);
+// row-major two's-complement INT4 codes [N, K/2] and fp32 scales [N, K/64] ->
+// the stored row-pair codes and stage-major scales
+hipError_t launch_repack_codes(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                               uint8_t *qw, float *sw, hipStream_t stream);
 // W4A16 records (16 columns x 4 groups each)
 int64_t awq_packed_bytes(int64_t N, int64_t K);
 int awq_rows_per_pass(int64_t K, size_t lds_limit);   // activation rows staged per workgroup
@@ -107,7 +118,15 @@ hipError_t launch_w4a4_gemm_mlp(const uint8_t *qa, const float *sa, const uint8_
 hipError_t launch_xl1_reduce(const float *part, int nc, int64_t total, float *xl1,
                              hipStream_t stream);
 
-// 0 auto, 1 full tiles only, 2 quarter tiles only (process-wide test hook)
+// k-split tiles (two four-wave halves per workgroup, each on half of K):
+// 128 x 128, or 64 x 64 with `quarter`; needs K / 64 >= 3
+hipError_t launch_w4a4_gemm_ks(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                               const float *sw, const float *xl1, const uint16_t *L2,
+                               const uint16_t *bias, int act, int64_t M, int64_t N, int64_t K,
+                               int r, uint16_t *Y, bool quarter, hipStream_t stream);
+
+// 0 auto, 1 full tiles only, 2 quarter tiles only, 3 k-split full tiles only,
+// 4 k-split quarter tiles only (process-wide test hook)
 void set_tile_policy(int policy);
 int tile_policy();
 int64_t wg_slots();   // 128 x 128 workgroup slots of the current device

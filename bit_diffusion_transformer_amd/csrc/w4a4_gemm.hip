@@ -77,6 +77,19 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
                             int r, uint16_t *Y, hipStream_t stream) {
     const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
     const int policy = tile_policy();
+    // Grids of at most one 128 x 128 tile per compute unit run as k-split
+    // tiles (two waves per SIMD on half the K loop each instead of one on all
+    // of it); at most a quarter of a tile per compute unit, as k-split
+    // 64 x 64 tiles.  Needs three groups or more (each half gets one).
+    const int64_t cus = wg_slots() / 2;
+    const bool ks_ok = K / kGroup >= 3;
+    if (policy == 3 || policy == 4 || (policy == 0 && ks_ok && tiles <= cus)) {
+        if (ks_ok) {
+            const bool quarter = policy == 4 || (policy == 0 && 4 * tiles <= cus);
+            return launch_w4a4_gemm_ks(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, quarter,
+                                       stream);
+        }
+    }
     int64_t rest = 0;
     if (policy == 2) {
         rest = tiles;

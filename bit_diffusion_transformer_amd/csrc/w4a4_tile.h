@@ -125,6 +125,7 @@ struct CopyPlan {
 struct Operands {
     const uint8_t *qw0, *qa0;      // first row of the tile
     const uint8_t *sw0, *sa0;      // (scales, as bytes)
+    int64_t sws, sas;              // INT4: bytes per stage of the stage-major scales (8 rows)
 };
 
 template <int WB>
@@ -141,15 +142,15 @@ __device__ __forceinline__ void issue_copies(uint8_t *st, const Operands &op, in
         __builtin_amdgcn_global_load_lds(qas + bo[i], (lds_void *)(st + C::B_OFF + row * ROWP), 16, 0, 0);
     }
     if (WB == 2) {
-        __builtin_amdgcn_global_load_lds(op.sw0 + c * GC * 4 + so[0],
+        __builtin_amdgcn_global_load_lds(op.sw0 + c * op.sws + so[0],
                                          (lds_void *)(st + C::SA_OFF + 32 * wave * GC * 4), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(op.sa0 + c * GC * 4 + so[1],
+        __builtin_amdgcn_global_load_lds(op.sa0 + c * op.sas + so[1],
                                          (lds_void *)(st + C::SB_OFF + 32 * wave * GC * 4), 4, 0, 0);
     } else if (wave < 2) {
-        __builtin_amdgcn_global_load_lds(op.sw0 + c * GC * 4 + so[0],
+        __builtin_amdgcn_global_load_lds(op.sw0 + c * op.sws + so[0],
                                          (lds_void *)(st + C::SA_OFF + 32 * wave * GC * 4), 4, 0, 0);
     } else {
-        __builtin_amdgcn_global_load_lds(op.sa0 + c * GC * 4 + so[1],
+        __builtin_amdgcn_global_load_lds(op.sa0 + c * op.sas + so[1],
                                          (lds_void *)(st + C::SB_OFF + 32 * (wave - 2) * GC * 4), 4, 0, 0);
     }
 }
@@ -346,23 +347,40 @@ __device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p, con
 // The K loop.  The four ring buffers are separate restrict pointers so that
 // the compiler can tell a read of one stage from the copies still landing in
 // the others (otherwise every LDS read would wait for all copies).  ODD: the
-// group count is odd, so the last stage holds one group (a compile-time
+// last real stage holds one group (an odd group count; a compile-time
 // choice, so that an even count carries no per-stage selects for it).  SK:
 // what the VALU does with the group sums (NoSink: the rescale; TakeGroup:
-// capture the sums of group sink.gsel).
-template <int WB, bool ODD, class SK = NoSink>
+// capture the sums of group sink.gsel).  NULLS: the loop runs ns stages of
+// which only the first nr are real (the halves of a k-split workgroup run
+// the same number of stages, so that their barriers pair up); a stage past
+// nr re-reads the last real one and adds nothing (its token scales are
+// zero, so every fma adds S * 0).
+// With NULLS the tail is a run-time choice (nodd), so that both halves of a
+// k-split workgroup share one instance of the loop.
+template <int WB, bool ODD, class SK = NoSink, bool NULLS = false>
 __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__restrict__ b1,
                                        uint8_t *__restrict__ b2, uint8_t *__restrict__ b3,
                                        const CopyPlan<WB> &cp, const ReadPlan &rp,
                                        const Operands &op, int ns,
-                                       f32x16 (&acc)[WB * WB], SK sink = SK{}) {
-    constexpr bool odd = ODD;
+                                       f32x16 (&acc)[WB * WB], SK sink = SK{}, int nr = 0,
+                                       bool nodd = false) {
+    const bool odd = NULLS ? nodd : ODD;
     constexpr int L = Cfg<WB>::LOADS;
+    // the stage whose data loop stage c copies, and whether that is the
+    // one-group tail
+    auto src = [&](int c) {
+        if constexpr (NULLS) return c < nr ? c : nr - 1;
+        else return c;
+    };
+    auto tail = [&](int c) {
+        if constexpr (NULLS) return odd && src(c) == nr - 1;
+        else return odd && c == ns - 1;
+    };
     // prologue: stages 0..3 in flight, stage 0 visible, group 0 in registers
-    issue_stage<WB>(b0, cp, op, 0, odd && ns == 1);
-    if (ns > 1) issue_stage<WB>(b1, cp, op, 1, odd && ns == 2);
-    if (ns > 2) issue_stage<WB>(b2, cp, op, 2, odd && ns == 3);
-    if (ns > 3) issue_stage<WB>(b3, cp, op, 3, odd && ns == 4);
+    issue_stage<WB>(b0, cp, op, src(0), tail(0));
+    if (ns > 1) issue_stage<WB>(b1, cp, op, src(1), tail(1));
+    if (ns > 2) issue_stage<WB>(b2, cp, op, src(2), tail(2));
+    if (ns > 3) issue_stage<WB>(b3, cp, op, src(3), tail(3));
     wait_stages<L>(ns < 4 ? ns - 1 : 3);
     barrier();
     Raw<WB> raw;
@@ -381,16 +399,22 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
         read_raw<WB>(raw, cur, rp, 1);
         __builtin_amdgcn_sched_barrier(0);
         group_first<WB>(acc, p, f, sk);
-        make_frags<WB>(f, raw, rp.keep_b && !(odd && s == ns - 1));
+        if constexpr (NULLS)
+            make_frags<WB>(f, raw, rp.keep_b && s < nr && !(odd && s == nr - 1));
+        else
+            make_frags<WB>(f, raw, rp.keep_b && !(odd && s == ns - 1));
         wait_next_stage<L>(s, ns);
         barrier();
-        if (s + 4 < ns) issue_stage<WB>(cur, cp, op, s + 4, odd && s + 4 == ns - 1);
+        if (s + 4 < ns) issue_stage<WB>(cur, cp, op, src(s + 4), tail(s + 4));
         // (after the last stage this reads a stale, unused buffer: no branch,
         // so the fragments carry no merge of old and new values)
         read_raw<WB>(raw, nxt, rp, 0);
         __builtin_amdgcn_sched_barrier(0);
         group_second<WB>(acc, p, f, sk);
-        make_frags<WB>(f, raw, rp.keep_b);
+        if constexpr (NULLS)
+            make_frags<WB>(f, raw, rp.keep_b && s + 1 < nr);
+        else
+            make_frags<WB>(f, raw, rp.keep_b);
         group_drain<WB>(acc, p, sk);
     };
     for (int s = 0; s < ns; s += 4) {
@@ -775,7 +799,7 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
 #pragma unroll
                 for (int bj = 0; bj < WB; ++bj) {
                     float x = acc[bi * WB + bj][4 * q + j] + bv[j];
-                    if (act == 1) x = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+                    if (act == 1) x = gelu_erf(x);
                     const float h = bf16_lo(pack_bf16x2(x, 0.0f));
                     acc[bi * WB + bj][4 * q + j] = h * inv;
                 }
@@ -848,7 +872,7 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
         }
         if (m < M) {
             *reinterpret_cast<u32x4 *>(ma.qa + code_offset(m, kb, nw / 2 + 16 * ks2)) = words;
-            if (ks2 == 0) ma.sa[m * G + nw / kGroup] = s;
+            if (ks2 == 0) ma.sa[scale_index(m, nw / kGroup, M)] = s;
         }
     }
     if (ma.rn == 0) return;
@@ -939,7 +963,16 @@ struct SumsArgs {
 // (epi -> MlpArgs).  The last two need WB = 2.  MXF: the operands are MXFP4
 // (sa, sw point to E8M0 bytes [rows, K / 32]; K % 128 == 0); otherwise INT4
 // with fp32 group scales [rows, K / 64].
-template <int WB, int EPI = EPI_STORE, bool MXF = false>
+//
+// KS = 2 (k-split tiles, 512 threads, EPI_STORE, INT4): two halves of four
+// waves each run the K loop of the same tile over the two halves of K, each
+// in its own LDS ring (sm is the first of two Smem<WB>): half 0 the first
+// 2 ceil(G/4) groups (whole stages), half 1 the rest; both run as many
+// stages (half 1 pads with null stages), so that their barriers pair up.
+// Half 1 then hands its partial sums to half 0 through LDS, and half 0
+// runs the epilogue on acc0 + acc1.  For grids that leave compute units
+// idle: two waves per SIMD instead of one, with no partial sums in memory.
+template <int WB, int EPI = EPI_STORE, bool MXF = false, int KS = 1>
 __device__ __forceinline__ void
 tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
           const uint8_t *__restrict__ qw, const void *__restrict__ sw,
@@ -947,9 +980,11 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
           const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N, int64_t K, int r,
           uint16_t *__restrict__ Y, Smem<WB> &sm, int64_t m0, int64_t n0,
           const void *epi = nullptr) {
+    static_assert(KS == 1 || (KS == 2 && EPI == EPI_STORE && !MXF), "k-split: plain INT4 tiles");
     using C = Cfg<WB>;
     constexpr int BT = C::BT, NB = C::NB;
-    const int tid = threadIdx.x;
+    const int tid = KS == 2 ? (int)(threadIdx.x & (NTHR - 1)) : (int)threadIdx.x;
+    const int half = KS == 2 ? (int)(threadIdx.x / NTHR) : 0;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wn = wave >> 1, wm = wave & 1;
@@ -960,16 +995,28 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
     const bool odd = (G & 1) != 0;
     const int nlast = (int)((N - n0 < BT ? N - n0 : BT) - 1);
     const int mlast = (int)((M - m0 < BT ? M - m0 : BT) - 1);
+    // k-split: this half's loop length, real stages and first stage
+    int ksl = ns, ksr = ns, ks0 = 0;
+    if constexpr (KS == 2) {
+        const int gh = 2 * ((G + 3) / 4);
+        ksl = gh / 2;
+        ks0 = half ? ksl : 0;
+        ksr = half ? (G - gh + 1) / 2 : ksl;
+    }
 
     Operands op;
-    op.qw0 = qw + n0 * (int64_t)kb;
-    op.qa0 = qa + m0 * (int64_t)kb;
+    op.qw0 = qw + n0 * (int64_t)kb + ks0 * PAIRP;
+    op.qa0 = qa + m0 * (int64_t)kb + ks0 * PAIRP;
     if constexpr (MXF) {                       // block-major bytes [K/32][P]: column offset
         op.sw0 = static_cast<const uint8_t *>(sw) + n0;
         op.sa0 = static_cast<const uint8_t *>(sa) + m0;
-    } else {                                   // an fp32 per group: 4 G bytes per row
-        op.sw0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sw) + n0 * (int64_t)G);
-        op.sa0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sa) + m0 * (int64_t)G);
+    } else {                                   // stage-major fp32 pairs: 8 R bytes per stage
+        op.sws = 8 * N;
+        op.sas = 8 * M;
+        op.sw0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sw) + 2 * n0) +
+                 ks0 * op.sws;
+        op.sa0 = reinterpret_cast<const uint8_t *>(static_cast<const float *>(sa) + 2 * m0) +
+                 ks0 * op.sas;
     }
 
     CopyPlan<WB> cp;
@@ -1005,10 +1052,12 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
         const int blk = WB == 2 ? wave : (wave & 1);
         const int row = 32 * blk + (lane >> 1);
         const int g = lane & 1;
-        cp.s_off[0] = (uint32_t)(4 * (min(row, nlast) * G + g));
-        cp.s_off[1] = (uint32_t)(4 * (min(row, mlast) * G + g));
-        cp.s_tail[0] = (uint32_t)(4 * min(row, nlast) * G);
-        cp.s_tail[1] = (uint32_t)(4 * min(row, mlast) * G);
+        // a stage's two scales of a row are adjacent (stage-major pairs); the
+        // pad of an odd count's last stage is zero, so the tail reads it too
+        cp.s_off[0] = (uint32_t)(4 * (2 * min(row, nlast) + g));
+        cp.s_off[1] = (uint32_t)(4 * (2 * min(row, mlast) + g));
+        cp.s_tail[0] = cp.s_off[0];
+        cp.s_tail[1] = cp.s_off[1];
     }
 
     ReadPlan rp;
@@ -1061,13 +1110,50 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
     } else if constexpr (MXF)
         k_loop_mx<WB>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ss, ns,
                       acc);
-    else if (odd)
+    else if constexpr (KS == 2) {
+        Smem<WB> &rs = (&sm)[half];
+        // only half 1 can end on the one-group stage
+        k_loop<WB, false, NoSink, true>(rs.u.ring[0], rs.u.ring[1], rs.u.ring[2], rs.u.ring[3], cp,
+                                        rp, op, ksl, acc, NoSink{}, ksr, half == 1 && odd);
+    } else if (odd)
         k_loop<WB, true>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns,
                          acc);
     else
         k_loop<WB, false>(sm.u.ring[0], sm.u.ring[1], sm.u.ring[2], sm.u.ring[3], cp, rp, op, ns,
                           acc);
     __syncthreads();
+    if constexpr (KS == 2) {
+        // Half 1 leaves its partial sums in its own (now idle) ring, as
+        // [t][q][thread] 16-byte pieces (elements 4q .. 4q + 3 of block t;
+        // conflict-free 16-byte accesses), and retires after the barriers that
+        // pair with half 0's; half 0 adds them and runs the epilogue alone.
+        // The barriers half 1 skips to must match the EPI_STORE epilogue
+        // below one for one: the exchange, the L2^T staging (r > 0) and the
+        // output staging.
+        static_assert(NB * 16 * NTHR * 4 <= (int)sizeof(Smem<WB>), "partials fit in a ring");
+        f32x4 *xch = reinterpret_cast<f32x4 *>(&(&sm)[1]);
+        if (half == 1) {
+#pragma unroll
+            for (int t = 0; t < NB; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xch[(t * 4 + q) * NTHR + tid] =
+                        f32x4{acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
+            __syncthreads();            // the exchange
+            if (r > 0) __syncthreads(); // the L2^T staging
+            __syncthreads();            // the output staging
+            return;
+        }
+        __syncthreads();                // the exchange
+#pragma unroll
+        for (int t = 0; t < NB; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 o = xch[(t * 4 + q) * NTHR + tid];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[t][4 * q + j] += o[j];
+            }
+    }
 
     // ---- epilogue: rank-r up-projection on the same tile (bf16 MFMA, the
     // fp32 xl1 split into a bf16 hi/lo pair), then bias, activation, store.
@@ -1205,7 +1291,7 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float x = acc[t][4 * q + j] + bv[j];
-                if (act == 1) x = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+                if (act == 1) x = gelu_erf(x);
                 o[j] = x;
             }
             u32x2 out;

@@ -46,7 +46,14 @@
  *     bytes and the pair interleaves in 32-byte halves there.  Byte b of row
  *     i sits at (i/2) 2 kb + (b/64) 128 + (i%2) w + b%64, with w = 64, or
  *     kb - 64 (b/64) in a shorter last chunk.  An odd row count's last pair
- *     has an unwritten half.  Scales: fp32 [rows, K/64], row-major.
+ *     has an unwritten half.
+ *   - Group scales (sa, sw) are stored stage-major in pairs: for R rows and
+ *     G = K/64 groups, fp32 [ceil(G/2), R, 2]; the scale of (row i, group g)
+ *     is element ((g/2) R + i) 2 + g%2, so that the scales of two consecutive
+ *     groups of consecutive rows (one stage of the GEMM's K loop for one tile)
+ *     are one contiguous run of 8 bytes per row.  With an odd G the elements
+ *     (i, G) of the last stage are padding, written as zero by the producers
+ *     of sa and sw.  ceil(G/2) R 2 floats in all.
  *   - The caller owns and allocates every buffer.  The library allocates
  *     nothing and keeps no state except a per-device architecture check.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
@@ -70,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 2
+#define SVDQ_ABI_VERSION 3
 #define SVDQ_GROUP 64      /* quantization group along K */
 #define SVDQ_MAX_RANK 128  /* largest supported low-rank r */
 /* Size limits, so that every offset the kernels form within a tile fits its
@@ -111,7 +118,7 @@ const char *svdq_last_error(void);
  * section "Quantize your own model").
  *   R   device fp32 [N, K]  residual weight (nn.Linear orientation, out x in)
  *   qw  device u8   [ceil(N/2), K] packed 4-bit codes, row pairs (out)
- *   sw  device fp32 [N, K/64] group scales (out)
+ *   sw  device fp32 [ceil(K/128), N, 2] group scales, stage-major (out)
  * Same quantizer as the activations, without smoothing.  N >= 0 (0: no-op),
  * K % 64 == 0, K >= 64.
  */
@@ -119,19 +126,20 @@ int32_t svdq_pack_weights(const float *R, int64_t N, int64_t K, uint8_t *qw, flo
                           void *stream);
 
 /*
- * Weight codes already quantized elsewhere (e.g. a checkpoint's packed INT4
- * residual) in the common row-major form -> the stored layout above.
- *   codes  device u8 [N, K/2]  two's-complement nibbles, element 2j in the
- *                              low nibble of byte j, codes in [-7, 7] (a -8
- *                              nibble is stored as -7)
- *   qw     device u8 [ceil(N/2), K] packed codes, row pairs (out)
- * The group scales keep their layout (fp32 [N, K/64]) and are used as they
- * are.  A pure re-arrangement: svdq_pack_weights(R) equals this applied to
- * the row-major codes of the same quantization.  N >= 0 (0: no-op),
+ * Weights already quantized elsewhere (e.g. a checkpoint's packed INT4
+ * residual) in the common row-major form -> the stored layouts above.
+ *   codes   device u8   [N, K/2]  two's-complement nibbles, element 2j in the
+ *                                 low nibble of byte j, codes in [-7, 7] (a -8
+ *                                 nibble is stored as -7)
+ *   scales  device fp32 [N, K/64] group scales, row-major
+ *   qw      device u8   [ceil(N/2), K] packed codes, row pairs (out)
+ *   sw      device fp32 [ceil(K/128), N, 2] group scales, stage-major (out)
+ * A pure re-arrangement: svdq_pack_weights(R) equals this applied to the
+ * row-major codes and scales of the same quantization.  N >= 0 (0: no-op),
  * K % 64 == 0, K >= 64.
  */
-int32_t svdq_repack_weights(const uint8_t *codes, int64_t N, int64_t K, uint8_t *qw,
-                            void *stream);
+int32_t svdq_repack_weights(const uint8_t *codes, const float *scales, int64_t N, int64_t K,
+                            uint8_t *qw, float *sw, void *stream);
 
 /*
  * Workspace bytes svdq_quantize_act_down needs: when K spans more than one
@@ -148,7 +156,7 @@ size_t svdq_quantize_act_down_workspace_bytes(int64_t M, int64_t K, int32_t r);
  *   lambda  device fp32 [K]      smoothing factors, finite and > 0
  *   L1      device bf16 [K, r]   low-rank down factor (NULL iff r == 0)
  *   qa      device u8   [ceil(M/2), K] packed codes of X diag(lambda)^-1 (out)
- *   sa      device fp32 [M, K/64] group scales (out)
+ *   sa      device fp32 [ceil(K/128), M, 2] group scales, stage-major (out)
  *   xl1     device fp32 [M, r]   (X diag(lambda)^-1) L1, fp32 (out; NULL iff r == 0)
  *   workspace / ws_bytes  device scratch of at least
  *           svdq_quantize_act_down_workspace_bytes(M, K, r) bytes (may be
@@ -291,7 +299,7 @@ size_t svdq_w4a4_lr_gemm_quant_down_workspace_bytes(int64_t M, int64_t N, int32_
  *   lambda_next  device fp32 [N]          the next layer's smoothing factors
  *   L1_next      device bf16 [N, r_next]  its down-projection (NULL if r_next == 0)
  *   qa_next      device u8   [ceil(M/2), N] its codes, row pairs (out)
- *   sa_next      device fp32 [M, N/64]    its scales (out)
+ *   sa_next      device fp32 [N/128, M, 2] its scales, stage-major (out)
  *   xl1_next     device fp32 [M, r_next]  its down-projection (out; NULL if r_next == 0)
  *   workspace    device, svdq_w4a4_lr_gemm_quant_down_workspace_bytes(M, N, r_next)
  * Needs N % 128 == 0 and r_next in {0, 16, 32}; otherwise as svdq_w4a4_lr_gemm.
@@ -471,19 +479,31 @@ int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *packed, const ui
                               int64_t M, int64_t N, int64_t K, uint16_t *Y, void *stream);
 
 /*
- * Test hook: how svdq_w4a4_lr_gemm (and svdq_linear) tile the output.
- *   SVDQ_TILES_AUTO    128 x 128 tiles for whole rounds of the device's
- *                      workgroup slots, 64 x 64 tiles for a partial last round
- *                      of at most three quarters of them (the default)
+ * Test hook: how svdq_w4a4_lr_gemm (and svdq_linear, svdq_linear_noalloc)
+ * tile the output.
+ *   SVDQ_TILES_AUTO    the default: for grids of more 128 x 128 tiles than
+ *                      the device has compute units, 128 x 128 tiles for
+ *                      whole rounds of the workgroup slots and 64 x 64 tiles
+ *                      for a partial last round of at most three quarters of
+ *                      them; for smaller grids (K / 64 >= 3), k-split tiles
+ *                      (each workgroup's two halves run half of the K loop
+ *                      each and add their partial sums in LDS): 128 x 128, or
+ *                      64 x 64 when four of those still fit one per unit
  *   SVDQ_TILES_FULL    128 x 128 tiles only
  *   SVDQ_TILES_QUARTER 64 x 64 tiles only
- * Process-wide; results are identical under every policy (both tile shapes
- * run the same per-output arithmetic in the same order).  Returns
+ *   SVDQ_TILES_KSPLIT, SVDQ_TILES_KSPLIT_QUARTER  k-split 128 x 128 / 64 x 64
+ *                      tiles only (K / 64 >= 3; otherwise as SVDQ_TILES_AUTO)
+ * Process-wide.  FULL and QUARTER (and AUTO where it picks them) give
+ * identical results (both tile shapes run the same per-output arithmetic in
+ * the same order); the k-split tiles add the two halves' partial sums, a
+ * different fp32 order, within the same tolerance.  Returns
  * SVDQ_ERR_INVALID_ARG for any other value.
  */
 #define SVDQ_TILES_AUTO 0
 #define SVDQ_TILES_FULL 1
 #define SVDQ_TILES_QUARTER 2
+#define SVDQ_TILES_KSPLIT 3
+#define SVDQ_TILES_KSPLIT_QUARTER 4
 int32_t svdq_debug_set_tile_policy(int32_t policy);
 
 #ifdef __cplusplus

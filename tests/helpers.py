@@ -54,6 +54,34 @@ def pdev(p: np.ndarray):
     return to_dev(to_pairs(p))
 
 
+def to_stage_major(s: np.ndarray) -> np.ndarray:
+    """Row-major group scales [R, G] (the oracle's) -> the device's stage-major pairs
+    [ceil(G/2), R, 2]: the scale of (row i, group g) at [g // 2, i, g % 2]; an odd G's
+    last-stage pad is zero."""
+    R, G = s.shape
+    out = np.zeros(((G + 1) // 2, R, 2), np.float32)
+    for g in range(G):
+        out[g // 2, :, g % 2] = s[:, g]
+    return out
+
+
+def from_stage_major(d, R: int, G: int) -> np.ndarray:
+    """Inverse of to_stage_major; also checks that an odd G's pad is zero."""
+    d = d.cpu().numpy() if hasattr(d, "cpu") else np.asarray(d)
+    d = d.reshape((G + 1) // 2, R, 2)
+    if G % 2:
+        assert np.all(d[-1, :, 1].view(np.uint32) == 0), "pad of the last stage is not +0"
+    out = np.empty((R, G), np.float32)
+    for g in range(G):
+        out[:, g] = d[g // 2, :, g % 2]
+    return out
+
+
+def sdev(s: np.ndarray):
+    """Oracle group scales -> device stage-major scales."""
+    return to_dev(to_stage_major(s))
+
+
 def bf16_host(t: torch.Tensor) -> np.ndarray:
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 

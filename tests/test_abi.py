@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bdt.svdq_abi_version() == 2
+    assert bdt.svdq_abi_version() == 3
     assert bdt.svdq_status_string(0) == "ok"
     assert bdt.svdq_status_string(MISALIGNED) == "misaligned pointer"
     assert bdt.svdq_status_string(99) == "unknown status"
@@ -122,10 +122,13 @@ def test_pack_and_debug_reject(lib):
     assert lib.svdq_pack_weights(P(A), 8, 100, P(A), P(A), None) == SHAPE
     assert lib.svdq_pack_weights(P(0), 8, 128, P(A), P(A), None) == INVALID
     assert lib.svdq_pack_weights(P(A), 8, 128, P(U), P(A), None) == MISALIGNED
-    assert lib.svdq_repack_weights(P(A), -1, 128, P(A), None) == INVALID
-    assert lib.svdq_repack_weights(P(A), 8, 96, P(A), None) == SHAPE
-    assert lib.svdq_repack_weights(P(0), 8, 128, P(A), None) == INVALID
-    assert lib.svdq_repack_weights(P(A), 8, 128, P(U), None) == MISALIGNED
+    rp = lib.svdq_repack_weights
+    assert rp(P(A), P(A), -1, 128, P(A), P(A), None) == INVALID
+    assert rp(P(A), P(A), 8, 96, P(A), P(A), None) == SHAPE
+    assert rp(P(0), P(A), 8, 128, P(A), P(A), None) == INVALID
+    assert rp(P(A), P(0), 8, 128, P(A), P(A), None) == INVALID
+    assert rp(P(A), P(A), 8, 128, P(U), P(A), None) == MISALIGNED
+    assert rp(P(A), P(A), 8, 128, P(A), P(U), None) == MISALIGNED
     assert lib.svdq_debug_group_sums(P(A), P(A), P(A), P(A), 16, 16, 128, 8, 0, 16, 16, P(A), None) == INVALID
     assert lib.svdq_debug_group_sums(P(A), P(A), P(A), P(A), 16, 16, 100, 0, 0, 16, 16, P(A), None) == SHAPE
     assert lib.svdq_debug_group_sums(P(A), P(0), P(A), P(A), 16, 16, 128, 0, 0, 16, 16, P(A), None) == INVALID
@@ -150,7 +153,7 @@ def test_pack_and_debug_reject(lib):
     assert aw(P(A), P(0), P(A), 2, 64, 128, P(A), None) == INVALID
     assert aw(P(A), P(A), P(U), 2, 64, 128, P(A), None) == MISALIGNED
     assert aw(P(A), P(A), P(A), 2, 64, 128, P(U), None) == MISALIGNED
-    assert lib.svdq_debug_set_tile_policy(3) == INVALID
+    assert lib.svdq_debug_set_tile_policy(5) == INVALID
     assert lib.svdq_debug_set_tile_policy(-1) == INVALID
 
 
@@ -177,7 +180,8 @@ def test_noalloc_rejects(lib):
 
 def test_tile_policy_values_accepted(lib):
     # host-side setting only (no launch); restored to the default
-    for pol in (bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_AUTO):
+    for pol in (bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_KSPLIT, bdt.TILES_KSPLIT_QUARTER,
+                bdt.TILES_AUTO):
         assert lib.svdq_debug_set_tile_policy(pol) == OK
 
 
@@ -187,7 +191,7 @@ def test_empty_inputs_are_noops(lib):
     assert _gemm(lib, qa=0, sa=0, qw=0, sw=0, xl1=0, L2=0, bias=0, Y=0, M=0) == OK
     assert _lin(lib, X=0, lam=0, L1=0, qw=0, sw=0, L2=0, bias=0, Y=0, ws=0, M=0) == OK
     assert lib.svdq_pack_weights(P(0), 0, 128, P(0), P(0), None) == OK
-    assert lib.svdq_repack_weights(P(0), 0, 128, P(0), None) == OK
+    assert lib.svdq_repack_weights(P(0), P(0), 0, 128, P(0), P(0), None) == OK
     assert lib.svdq_debug_group_sums(P(0), P(0), P(0), P(0), 16, 16, 128, 0, 0, 0, 5, P(0), None) == OK
     assert lib.svdq_awq_pack_weights(P(0), 0, 128, P(0), None) == OK
     assert lib.svdq_awq_repack(P(0), P(0), P(0), 0, 128, P(0), None) == OK

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.helpers import from_pairs, to_pairs
+from tests.helpers import from_pairs, from_stage_major, to_pairs, to_stage_major
 
 
 def _pack(codes):
@@ -88,3 +88,20 @@ def test_row_pair_converter_matches_stated_offsets(rows, K):
     # every byte of a full pair is used; an odd count leaves its last half unwritten
     assert seen.sum() == rows * kb
     assert np.array_equal(from_pairs(d, rows), p)
+
+
+@pytest.mark.parametrize("R,G", [(1, 1), (3, 2), (5, 3), (8, 48), (7, 25)])
+def test_stage_major_scale_converter_matches_stated_index(R, G):
+    # include/svdq.h: the scale of (row i, group g) is element ((g/2) R + i) 2 + g%2 of a
+    # [ceil(G/2), R, 2] array; an odd G's last-stage pad is zero
+    rng = np.random.default_rng(R * 100 + G)
+    s = rng.standard_normal((R, G)).astype(np.float32)
+    d = to_stage_major(s)
+    assert d.shape == ((G + 1) // 2, R, 2)
+    flat = d.reshape(-1)
+    for i in range(R):
+        for g in range(G):
+            assert flat[((g // 2) * R + i) * 2 + g % 2] == s[i, g]
+    if G % 2:
+        assert not flat.reshape((G + 1) // 2, R, 2)[-1, :, 1].any()
+    assert np.array_equal(from_stage_major(d, R, G), s)

@@ -12,7 +12,7 @@ import pytest
 import bit_diffusion_transformer_amd as bdt
 import oracle
 from synth import CONFIGS, DIT_CHAIN, make_layer
-from tests.helpers import assert_y_close, bf16_host, from_pairs, to_dev, xl1_bound
+from tests.helpers import assert_y_close, bf16_host, from_pairs, from_stage_major, to_dev, xl1_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -38,13 +38,13 @@ def test_full_size_config(name, spec, M):
     qw_o, sw_o = oracle.pack_weights(L.R)
     qw, sw = bdt.pack_weights(to_dev(L.R))
     assert np.array_equal(from_pairs(qw, N), qw_o)
-    assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_o.view(np.uint32))
+    assert np.array_equal(from_stage_major(sw, N, K // 64).view(np.uint32), sw_o.view(np.uint32))
 
     X, lam, L1, L2, bias = to_dev(L.X), to_dev(L.lam), to_dev(L.L1), to_dev(L.L2), to_dev(L.bias)
     qa_o, sa_o, xh = oracle.quantize_act(L.X, L.lam)
     qa, sa, xl1 = bdt.quantize_act_down(X, lam, L1)
     assert np.array_equal(from_pairs(qa, M), qa_o)
-    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
+    assert np.array_equal(from_stage_major(sa, M, K // 64).view(np.uint32), sa_o.view(np.uint32))
     xl1_o = oracle.down_proj(xh, L.L1)
     assert np.all(np.abs(xl1.cpu().numpy().astype(np.float64) - xl1_o) <= xl1_bound(xh, L.L1))
 

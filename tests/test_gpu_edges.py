@@ -10,7 +10,7 @@ import bit_diffusion_transformer_amd as bdt
 import oracle
 from bit_diffusion_transformer_amd import _binding
 from synth import LayerSpec, f32_to_bf16_bits, make_layer
-from tests.helpers import assert_y_close, bf16_host, from_pairs, pdev, to_dev
+from tests.helpers import assert_y_close, bf16_host, from_pairs, from_stage_major, pdev, sdev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,7 @@ def test_empty_batch():
     L = _layer()
     X = to_dev(L.X)[:0]
     qa, sa, xl1 = bdt.quantize_act_down(X, to_dev(L.lam), to_dev(L.L1))
-    assert qa.shape == (0, 256) and sa.shape == (0, 4) and xl1.shape == (0, 32)
+    assert qa.shape == (0, 256) and sa.shape == (2, 0, 2) and xl1.shape == (0, 32)
     qw, sw = bdt.pack_weights(to_dev(L.R))
     Y = bdt.linear(X, to_dev(L.lam), to_dev(L.L1), qw, sw, to_dev(L.L2), to_dev(L.bias))
     assert Y.shape == (0, 136)
@@ -43,7 +43,8 @@ def test_zero_and_subnormal_groups_bit_exact():
     qa_o, sa_o, _ = oracle.quantize_act(X, lam)
     qa, sa, _ = bdt.quantize_act_down(to_dev(X), to_dev(lam), None)
     assert np.array_equal(from_pairs(qa, M), qa_o)
-    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
+    assert np.array_equal(from_stage_major(sa, sa_o.shape[0], sa_o.shape[1]).view(np.uint32),
+                          sa_o.view(np.uint32))
     assert (sa_o == 0).any() and ((sa_o > 0) & (sa_o < 2.0 ** -126)).any()
     R = (rng.standard_normal((64, K)) * 0.05).astype(np.float32)
     R[2] = 0.0
@@ -51,7 +52,8 @@ def test_zero_and_subnormal_groups_bit_exact():
     qw_o, sw_o = oracle.pack_weights(R)
     qw, sw = bdt.pack_weights(to_dev(R))
     assert np.array_equal(from_pairs(qw, 64), qw_o)
-    assert np.array_equal(sw.cpu().numpy().view(np.uint32), sw_o.view(np.uint32))
+    assert np.array_equal(from_stage_major(sw, sw_o.shape[0], sw_o.shape[1]).view(np.uint32),
+                          sw_o.view(np.uint32))
 
 
 def test_all_extreme_codes():
@@ -62,9 +64,9 @@ def test_all_extreme_codes():
     R = np.where(np.arange(K) % 2 == 0, -0.5, 0.5)[None, :].repeat(N, 0).astype(np.float32)
     qa_o, sa_o, _ = oracle.quantize_act(X, lam)
     qw_o, sw_o = oracle.pack_weights(R)
-    S = bdt.group_sums(pdev(qa_o), to_dev(sa_o), pdev(qw_o), to_dev(sw_o), M, N, 0, 0, M, N).cpu().numpy()
+    S = bdt.group_sums(pdev(qa_o), sdev(sa_o), pdev(qw_o), sdev(sw_o), M, N, 0, 0, M, N).cpu().numpy()
     assert np.all(S == -3136)
-    Y = bdt.w4a4_lr_gemm(pdev(qa_o), to_dev(sa_o), pdev(qw_o), to_dev(sw_o), None, None, None)
+    Y = bdt.w4a4_lr_gemm(pdev(qa_o), sdev(sa_o), pdev(qw_o), sdev(sw_o), None, None, None)
     _, y_or = oracle.gemm_rows(qa_o, sa_o, qw_o, sw_o, None, None, None, 0, K)
     assert_y_close(bf16_host(Y), y_or)
 
@@ -80,7 +82,7 @@ def test_canaries_untouched():
     M, K, N, r = 77, 192, 264, 48
     G = K // 64
     qa_b, qa = _padded(bdt.pair_rows(M) * K, torch.uint8, 0xA5)   # row pairs
-    sa_b, sa = _padded(M * G, torch.float32, -123.0)
+    sa_b, sa = _padded((G + 1) // 2 * M * 2, torch.float32, -123.0)   # stage-major pairs
     x_b, x1 = _padded(M * r, torch.float32, -321.0)
     y_b, y = _padded(M * N, torch.int16, 0x5A5A)
     ws_bytes = bdt.svdq_quantize_act_down_workspace_bytes(M, K, r)
@@ -139,8 +141,9 @@ def test_repack_minus_eight_is_stored_as_minus_seven():
     tc = ((raw[:, 0::2] & 0xF) | ((raw[:, 1::2] & 0xF) << 4)).astype(np.uint8)
     want, scales = oracle.quantize_groups(np.where(m8, -7, c).astype(np.float32))
     assert np.all(scales == 1.0)
-    qw = bdt.repack_weights(to_dev(tc))
+    qw, sw = bdt.repack_weights(to_dev(tc), to_dev(scales))
     assert np.array_equal(from_pairs(qw, N), want)
+    assert np.array_equal(from_stage_major(sw, N, K // 64), scales)
 
 
 @pytest.mark.parametrize("eta", [0.3, 0.1, 0.03])
@@ -165,7 +168,7 @@ def test_rescale_precision_under_cancelling_groups(eta):
     assert np.all(s1 == 1.0) and np.all(s2 == 1.0)
     sa = (rng.uniform(0.5, 2.0, (M, 1)) * (1 + rng.uniform(-eta, eta, (M, G)))).astype(np.float32)
     sw = (rng.uniform(0.5, 2.0, (N, 1)) * (1 + rng.uniform(-eta, eta, (N, G)))).astype(np.float32)
-    Y = bdt.w4a4_lr_gemm(pdev(qa_o), to_dev(sa), pdev(qw_o), to_dev(sw), None, None, None)
+    Y = bdt.w4a4_lr_gemm(pdev(qa_o), sdev(sa), pdev(qw_o), sdev(sw), None, None, None)
     acc, y_or = oracle.gemm_rows(qa_o, sa, qw_o, sw, None, None, None, 0, K)
     S = (qa_codes.reshape(M, G, 64)[0] ** 2).sum(axis=1) * sign          # [G]
     terms = np.abs(sa.astype(np.float64))[:, None, :] * np.abs(sw.astype(np.float64))[None, :, :] \
@@ -177,3 +180,26 @@ def test_rescale_precision_under_cancelling_groups(eta):
     assert np.all(np.abs(yv - acc) <= bound)
     ratio = float(terms.sum(axis=2).mean() / np.sqrt(np.mean(acc ** 2)))
     print("eta %.2f: sum|terms| / rms(Y) = %.0f, worst |err|/tol = %.3f" % (eta, ratio, worst))
+
+
+def test_gelu_epilogue_accuracy():
+    # Zero codes and scales leave acc = bias, so Y = bf16(GELU(bias)) elementwise: the
+    # epilogue's GELU (a rational erf approximation with |error| <= 1.5e-7, evaluated in
+    # fp32) must be within 0.5 bf16 ulp of the output plus 4e-7 |x| of the exact erf-form
+    # GELU over a sweep of pre-activations, including the far tails.
+    from synth import f32_to_bf16_bits
+    M, K, N = 8, 64, 4096
+    xs = np.concatenate([np.linspace(-12.0, 12.0, N - 8), [0.0, -0.0, 1e-30, -1e-30, 40.0, -40.0,
+                                                             3e-5, -3e-5]])
+    bias = f32_to_bf16_bits(xs.astype(np.float32))
+    b = (bias.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    qa = torch.zeros((bdt.pair_rows(M), K), dtype=torch.uint8, device="cuda:0")
+    sa = torch.zeros(bdt.scale_shape(M, K), dtype=torch.float32, device="cuda:0")
+    qw = torch.zeros((bdt.pair_rows(N), K), dtype=torch.uint8, device="cuda:0")
+    sw = torch.zeros(bdt.scale_shape(N, K), dtype=torch.float32, device="cuda:0")
+    Y = bf16_host(bdt.w4a4_lr_gemm(qa, sa, qw, sw, None, None, to_dev(bias), 1))
+    y = (Y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exact = np.array([oracle.gelu(v) for v in b])
+    bound = 0.5 * oracle.bf16_ulp(exact) + 4e-7 * np.abs(b) + 1e-38
+    assert np.all(np.abs(y - exact[None, :]) <= bound[None, :])
+    assert np.all(y == y[0:1])                     # every row the same

@@ -15,7 +15,8 @@ import torch
 import bit_diffusion_transformer_amd as bdt
 import oracle
 from synth import DIT_CHAIN, LayerSpec, make_layer
-from tests.helpers import assert_y_close, bf16_host, from_pairs, pdev, to_dev, xl1_bound
+from tests.helpers import (assert_y_close, bf16_host, from_pairs, from_stage_major, pdev, sdev,
+                           to_dev, xl1_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +41,7 @@ def _pair(M, K, Nh, ru, rd, act, bias, cid):
 def _dev_layer(L, r):
     qw, sw = oracle.pack_weights(L.R)
     return dict(lam=to_dev(L.lam), L1=to_dev(L.L1) if r else None, L2=to_dev(L.L2) if r else None,
-                bias=to_dev(L.bias), qw=pdev(qw), sw=to_dev(sw))
+                bias=to_dev(L.bias), qw=pdev(qw), sw=sdev(sw))
 
 
 @pytest.fixture(scope="module", params=list(enumerate(SHAPES)),
@@ -56,7 +57,7 @@ def case(request):
 
 def _up_operands(case):
     ru = case["ru"]
-    return (pdev(case["qa"]), to_dev(case["sa"]), case["U"]["qw"], case["U"]["sw"],
+    return (pdev(case["qa"]), sdev(case["sa"]), case["U"]["qw"], case["U"]["sw"],
             to_dev(case["xl1"].astype(np.float32)) if ru else None, case["U"]["L2"],
             case["U"]["bias"])
 
@@ -64,11 +65,18 @@ def _up_operands(case):
 def test_gemm_quant_down_matches_quantizer_of_plain_output(case):
     ops = _up_operands(case)
     D, rd = case["D"], case["rd"]
-    h = bf16_host(bdt.w4a4_lr_gemm(*ops, case["act"]))          # what the plain GEMM stores
+    # what the plain GEMM stores on whole-K tiles (the fused kernel's tile arithmetic; the
+    # k-split tiles the plain GEMM picks for small grids add two partial sums instead)
+    bdt.svdq_debug_set_tile_policy(bdt.TILES_FULL)
+    try:
+        h = bf16_host(bdt.w4a4_lr_gemm(*ops, case["act"]))
+    finally:
+        bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
     qa_n, sa_n, xl1_n = bdt.w4a4_lr_gemm_quant_down(*ops, case["act"], D["lam"], D["L1"])
     qa_o, sa_o, xh = oracle.quantize_act(h, case["down"].lam)
     assert np.array_equal(from_pairs(qa_n, case["M"]), qa_o)
-    assert np.array_equal(sa_n.cpu().numpy().view(np.uint32), sa_o.view(np.uint32))
+    assert np.array_equal(from_stage_major(sa_n, sa_o.shape[0], sa_o.shape[1]).view(np.uint32),
+                          sa_o.view(np.uint32))
     if rd:
         want = oracle.down_proj(xh, case["down"].L1)
         got = xl1_n.cpu().numpy().astype(np.float64)

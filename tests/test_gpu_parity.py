@@ -12,7 +12,8 @@ import torch
 import bit_diffusion_transformer_amd as bdt
 import oracle
 from synth import LayerSpec, make_layer
-from tests.helpers import assert_y_close, bf16_host, from_pairs, pdev, to_dev, xl1_bound
+from tests.helpers import (assert_y_close, bf16_host, from_pairs, from_stage_major, pdev, sdev,
+                           to_dev, xl1_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +49,9 @@ def case(request):
 def test_pack_weights_bit_exact(case):
     qw, sw = bdt.pack_weights(to_dev(case["L"].R))
     assert np.array_equal(from_pairs(qw, case["N"]), case["qw"])
-    assert np.array_equal(sw.cpu().numpy().view(np.uint32), case["sw"].view(np.uint32))
+    G = case["K"] // 64
+    assert np.array_equal(from_stage_major(sw, case["N"], G).view(np.uint32),
+                          case["sw"].view(np.uint32))
 
 
 def _twos_complement_bytes(codes):
@@ -62,15 +65,18 @@ def test_repack_weights_bit_exact(case):
     # codes of the oracle's quantization in the common row-major form -> the stored layout
     N, K = case["N"], case["K"]
     tc = _twos_complement_bytes(oracle.unpack(case["qw"], K))
-    qw = bdt.repack_weights(to_dev(tc))
+    qw, sw = bdt.repack_weights(to_dev(tc), to_dev(case["sw"]))
     assert np.array_equal(from_pairs(qw, N), case["qw"])
+    assert np.array_equal(from_stage_major(sw, N, K // 64).view(np.uint32),
+                          case["sw"].view(np.uint32))
 
 
 def test_quantize_act_down(case):
     L, r = case["L"], case["r"]
     qa, sa, xl1 = bdt.quantize_act_down(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None)
     assert np.array_equal(from_pairs(qa, case["M"]), case["qa"])
-    assert np.array_equal(sa.cpu().numpy().view(np.uint32), case["sa"].view(np.uint32))
+    assert np.array_equal(from_stage_major(sa, case["M"], case["K"] // 64).view(np.uint32),
+                          case["sa"].view(np.uint32))
     if r:
         got = xl1.cpu().numpy().astype(np.float64)
         assert np.all(np.abs(got - case["xl1"]) <= xl1_bound(case["xh"], L.L1))
@@ -85,24 +91,33 @@ def tiles(request):
     bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
 
 
+@pytest.fixture(params=[bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_KSPLIT,
+                        bdt.TILES_KSPLIT_QUARTER],
+                ids=["full_tiles", "quarter_tiles", "ksplit_tiles", "ksplit_quarter_tiles"])
+def all_tiles(request):
+    bdt.svdq_debug_set_tile_policy(request.param)
+    yield request.param
+    bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
+
+
 def test_group_sums_bit_exact(case, tiles):
     # the sums come out of the GEMM's own K loop (LDS ring, swizzle, row-pair copies,
     # odd-group tail stage) on 128 x 128 or 64 x 64 tiles
     M, N, K = case["M"], case["N"], case["K"]
     qa, qw = pdev(case["qa"]), pdev(case["qw"])
-    sa, sw = to_dev(case["sa"]), to_dev(case["sw"])
+    sa, sw = sdev(case["sa"]), sdev(case["sw"])
     for (m0, tm, n0, tn) in [(0, M, 0, N), (M // 3, M - M // 3, N // 5, min(37, N - N // 5))]:
         S = bdt.group_sums(qa, sa, qw, sw, M, N, m0, n0, tm, tn).cpu().numpy()
         ref = oracle.group_sums(case["qa"], case["qw"], K, m0, n0, tm, tn)
         assert np.array_equal(S, ref)
 
 
-def test_gemm_stagewise(case, tiles):
+def test_gemm_stagewise(case, all_tiles):
     # Same inputs on both sides: the oracle's codes/scales and its xl1 in fp32.
     L, r, K = case["L"], case["r"], case["K"]
     xl1_32 = case["xl1"].astype(np.float32) if r else None
-    Y = bdt.w4a4_lr_gemm(pdev(case["qa"]), to_dev(case["sa"]), pdev(case["qw"]),
-                         to_dev(case["sw"]), to_dev(xl1_32), to_dev(L.L2) if r else None,
+    Y = bdt.w4a4_lr_gemm(pdev(case["qa"]), sdev(case["sa"]), pdev(case["qw"]),
+                         sdev(case["sw"]), to_dev(xl1_32), to_dev(L.L2) if r else None,
                          to_dev(L.bias), case["act"])
     _, y_or = oracle.gemm_rows(case["qa"], case["sa"], case["qw"], case["sw"],
                                None if xl1_32 is None else xl1_32.astype(np.float64),
@@ -110,10 +125,10 @@ def test_gemm_stagewise(case, tiles):
     assert_y_close(bf16_host(Y), y_or, "gemm")
 
 
-def test_linear_end_to_end(case, tiles):
+def test_linear_end_to_end(case, all_tiles):
     L, r = case["L"], case["r"]
     Y = bdt.linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, pdev(case["qw"]),
-                   to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
+                   sdev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
     _, y_or = oracle.linear(L.X, L.lam, L.L1 if r else None, case["qw"], case["sw"],
                             L.L2 if r else None, L.bias, case["act"])
     assert_y_close(bf16_host(Y), y_or, "linear")
@@ -122,22 +137,28 @@ def test_linear_end_to_end(case, tiles):
 def test_linear_is_deterministic(case):
     L, r = case["L"], case["r"]
     args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, pdev(case["qw"]),
-            to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
+            sdev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
     y1 = bf16_host(bdt.linear(*args))
     y2 = bf16_host(bdt.linear(*args))
     assert np.array_equal(y1, y2)
 
 
 def test_tile_policies_agree_bit_exact(case):
-    # Both tile shapes run the same per-output arithmetic in the same order.
+    # 128 x 128 and 64 x 64 tiles run the same per-output arithmetic in the same order, and
+    # so do the two k-split shapes (the same split of K, then acc0 + acc1); the default
+    # picks one of the two families
     L, r = case["L"], case["r"]
     args = (to_dev(L.X), to_dev(L.lam), to_dev(L.L1) if r else None, pdev(case["qw"]),
-            to_dev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
-    out = []
+            sdev(case["sw"]), to_dev(L.L2) if r else None, to_dev(L.bias), case["act"])
+    out = {}
     try:
-        for pol in (bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_AUTO):
+        for pol in (bdt.TILES_FULL, bdt.TILES_QUARTER, bdt.TILES_KSPLIT, bdt.TILES_KSPLIT_QUARTER,
+                    bdt.TILES_AUTO):
             bdt.svdq_debug_set_tile_policy(pol)
-            out.append(bf16_host(bdt.linear(*args)))
+            out[pol] = bf16_host(bdt.linear(*args))
     finally:
         bdt.svdq_debug_set_tile_policy(bdt.TILES_AUTO)
-    assert np.array_equal(out[0], out[1]) and np.array_equal(out[0], out[2])
+    assert np.array_equal(out[bdt.TILES_FULL], out[bdt.TILES_QUARTER])
+    assert np.array_equal(out[bdt.TILES_KSPLIT], out[bdt.TILES_KSPLIT_QUARTER])
+    assert (np.array_equal(out[bdt.TILES_AUTO], out[bdt.TILES_FULL])
+            or np.array_equal(out[bdt.TILES_AUTO], out[bdt.TILES_KSPLIT]))
