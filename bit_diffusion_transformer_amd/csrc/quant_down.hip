@@ -33,19 +33,16 @@ namespace svdq {
 // so the result does not depend on scheduling.
 constexpr int K1_ROWS = 64;
 
-// Chunk size for a tile count: the staged L1 chunk is 64 KC x 16 NT bf16.
-template <int NT> struct K1Chunk { static constexpr int KC = NT <= 2 ? 8 : (NT <= 4 ? 4 : 2); };
-
+// KC groups per chunk (k1_chunk_groups); the staged L1 chunk is 64 KC x 16 NT bf16.
 // MX: the 4-bit float (MXFP4) variant -- the same smoothing and
 // down-projection, the MX quantizer per 32-value block, E8M0 scale bytes block-major in sa
 // ([K/32][mx_scale_rows(M)]).
-template <int NT, bool MX = false>
+template <int NT, int KC, bool MX = false>
 __global__ void __launch_bounds__(256)
 quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
                   const uint16_t *__restrict__ L1, int64_t M, int64_t K, int r, int nc,
                   uint8_t *__restrict__ qa, void *__restrict__ sa, float *__restrict__ out,
                   int64_t out_chunk_stride) {
-    constexpr int KC = K1Chunk<NT>::KC;
     constexpr int S = KC * kGroup + 8;                 // LDS row of the L1 chunk, bf16
     constexpr int NLAM = (KC * kGroup + 255) / 256;    // lambda loads per thread
     constexpr int NL1 = NT > 0 ? KC * NT / 2 : 0;      // 16-byte L1 pieces per thread
@@ -326,25 +323,33 @@ repack_codes_kernel(const uint8_t *__restrict__ codes, const float *__restrict__
 hipError_t launch_quant_down(const uint16_t *X, const float *lambda, const uint16_t *L1,
                              int64_t M, int64_t K, int r, const DownWorkspace &ws, uint8_t *qa,
                              void *sa, float *xl1, hipStream_t stream, bool mx) {
-    const int nc = k1_chunks(K, r);
+    const int nc = k1_chunks(M, K, r);
+    const int kc = k1_chunk_groups(M, K, r);
     const int64_t rbs = (M + K1_ROWS - 1) / K1_ROWS;
     const unsigned blocks = (unsigned)(rbs * nc);
     const bool partial = r > 0 && nc > 1;
     float *out = partial ? ws.part : xl1;
     const int64_t stride = partial ? M * (int64_t)r : 0;
-#define SVDQ_K1(NTV)                                                                       \
+#define SVDQ_K1(NTV, KCV)                                                                  \
     do {                                                                                   \
         if (mx)                                                                            \
-            quant_down_kernel<NTV, true><<<blocks, 256, 0, stream>>>(X, lambda, L1, M, K, r, \
-                                                                    nc, qa, sa, out, stride); \
+            quant_down_kernel<NTV, KCV, true><<<blocks, 256, 0, stream>>>(                  \
+                X, lambda, L1, M, K, r, nc, qa, sa, out, stride);                          \
         else                                                                               \
-            quant_down_kernel<NTV><<<blocks, 256, 0, stream>>>(X, lambda, L1, M, K, r, nc,  \
-                                                              qa, sa, out, stride);        \
+            quant_down_kernel<NTV, KCV><<<blocks, 256, 0, stream>>>(                        \
+                X, lambda, L1, M, K, r, nc, qa, sa, out, stride);                          \
     } while (0)
-    if (r == 0) SVDQ_K1(0);
-    else if (r <= 32) SVDQ_K1(2);
-    else if (r <= 64) SVDQ_K1(4);
-    else SVDQ_K1(8);
+#define SVDQ_K1_KC(NTV)                                                                    \
+    do {                                                                                   \
+        if (kc == 8) SVDQ_K1(NTV, 8);                                                      \
+        else if (kc == 4) SVDQ_K1(NTV, 4);                                                 \
+        else SVDQ_K1(NTV, 2);                                                              \
+    } while (0)
+    if (r == 0) SVDQ_K1_KC(0);
+    else if (r <= 32) SVDQ_K1_KC(2);
+    else if (r <= 64) SVDQ_K1(4, 4);
+    else SVDQ_K1(8, 2);
+#undef SVDQ_K1_KC
 #undef SVDQ_K1
     if (partial) {
         const int64_t total = M * (int64_t)r;

@@ -41,11 +41,19 @@ inline size_t scale_floats(int64_t R, int64_t G) { return (size_t)((G + 1) / 2) 
 // 64 rows and chunk); with more than one chunk and r > 0 the chunks' partial
 // x^ L1 sums go to the workspace and a second kernel adds them up.  kc keeps
 // the chunk of L1 staged in LDS (kc x 64 x r bf16, r rounded up to 32, 64 or
-// 128) at 32 KB; the last chunk may hold fewer groups.
-inline int k1_chunk_groups(int r) { return r <= 32 ? 8 : (r <= 64 ? 4 : 2); }
-inline int k1_chunks(int64_t K, int r) {
+// 128) at 32 KB or less; below that, shorter chunks give more and shorter
+// waves (each wave runs its chunk's groups one after another): 4 groups
+// unless K is long (more than 64 groups, where the partial sums would grow),
+// 2 for a few hundred tokens.  The last chunk may hold fewer groups.
+inline int k1_chunk_groups(int64_t M, int64_t K, int r) {
+    if (r > 64) return 2;
+    if (r > 32) return 4;
+    if (M <= 512) return 2;
+    return K / 64 > 64 ? 8 : 4;
+}
+inline int k1_chunks(int64_t M, int64_t K, int r) {
     const int64_t G = K / 64;
-    const int kc = k1_chunk_groups(r);
+    const int kc = k1_chunk_groups(M, K, r);
     return (int)((G + kc - 1) / kc);
 }
 
@@ -56,7 +64,7 @@ struct DownWorkspace {
 
 inline size_t down_workspace_bytes(int64_t M, int64_t K, int r) {
     if (r <= 0 || M <= 0 || K < 64) return 0;
-    const int nc = k1_chunks(K, r);
+    const int nc = k1_chunks(M, K, r);
     return nc > 1 ? align256((size_t)nc * (size_t)M * (size_t)r * 4) : 0;
 }
 

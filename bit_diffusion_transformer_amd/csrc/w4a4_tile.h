@@ -21,15 +21,17 @@
 //   - one v_mfma_scale_f32_32x32x64_f8f6f4 on the codes as FP8 (the stored
 //     code layout turns them into E4M3 subnormals with three VALU ops per
 //     8 codes, svdq_device.h): S, the group's exact integer sums, in fp32;
-//   - one v_mfma_f32_32x32x8_bf16 that forms the scale products
-//     P[n][m] = sw[n] sa[m] as an outer product of bf16 hi/lo pairs
-//     ((sw_hi + sw_lo)(sa_hi + sa_lo), exact bf16 products, fp32 sums,
-//     ~2^-16 relative to the fp32 product) in the same output layout;
-// and the VALU does only acc = fma(S, P, acc).  The rescale is what bounds
+//   - half of a v_mfma_f32_32x32x1_2b_f32, which forms the scale products
+//     P[n][m] = fl32(sw[n] sa[m]) of two 32 x 32 blocks at once (fp32
+//     outer products, straight from the fp32 scales in LDS) in the same
+//     output layout;
+// and the VALU does only acc = fma(S, P, acc): the fp32 product of the two
+// scales, then one fp32 fma per output and group.  The VALU is what bounds
 // this kernel on this chip (one group of 64 MACs per output costs 1/64 of a
-// 32x32x64 MFMA but a wave-wide VALU op), so it is kept to the minimum: with
-// the int8 instruction S came out as an integer and needed a convert per
-// output and group as well.
+// 32x32x64 MFMA but a wave-wide VALU op), so the matrix unit takes every
+// step it can: with the int8 instruction S came out as an integer and
+// needed a convert per output and group, and forming P on the VALU, or its
+// bf16 operands, would cost as much again.
 //
 // Data movement: packed 4-bit codes (rows in pairs, so that a stage of two
 // rows is one 128-byte line) and raw fp32 scales go from global memory
@@ -201,24 +203,29 @@ __device__ __forceinline__ void wait_next_stage(int s, int ns) {
 // accesses across the barrier.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Loop-invariant LDS offsets of one lane's fragment reads.
+// Loop-invariant LDS offsets of one lane's fragment reads.  Scales (the
+// operands of the two-block outer product): WB = 2, per group: the weight
+// scale of row l of the wave's 64 rows (a_scale), the token scale of column
+// l (b_scale) and of column l ^ 32 (b_scale1) of its 64 columns; WB = 1, per
+// stage: the scales of row / column l % 32 for group l / 32 of the stage.
 struct ReadPlan {
     int a_code[GC], b_code[GC];    // block 0; block j is 32 j rows further
-    int a_scale, b_scale;          // group 0 of block 0
-    bool keep_b;                   // k-slot 0 lanes carry the token scale
+    int a_scale, b_scale, b_scale1;
 };
 
 template <int WB>
 struct Raw {
     u32x4 a[WB], b[WB];
-    float sa[WB], sb[WB];
+    float sw, sa0, sa1;
 };
 template <int WB>
 struct Frags {
     i32x8 A[WB], B[WB];            // FP8 codes of the group, per block
-    u32x2 AS[WB], BS[WB];
+    float PA, PB0, PB1;            // outer-product operands (weight, token scales)
 };
 
+// Group gi of a stage: the code fragments, and (WB = 2: every group; WB = 1:
+// group 0, for both groups of the stage) the scale operands.
 template <int WB>
 __device__ __forceinline__ void read_raw(Raw<WB> &rw, const uint8_t *st, const ReadPlan &rp,
                                          int gi) {
@@ -226,48 +233,72 @@ __device__ __forceinline__ void read_raw(Raw<WB> &rw, const uint8_t *st, const R
     for (int blk = 0; blk < WB; ++blk) {
         rw.a[blk] = *reinterpret_cast<const u32x4 *>(st + rp.a_code[gi] + blk * 32 * ROWP);
         rw.b[blk] = *reinterpret_cast<const u32x4 *>(st + rp.b_code[gi] + blk * 32 * ROWP);
-        rw.sa[blk] = *reinterpret_cast<const float *>(st + rp.a_scale + blk * 32 * GC * 4 + 4 * gi);
-        rw.sb[blk] = *reinterpret_cast<const float *>(st + rp.b_scale + blk * 32 * GC * 4 + 4 * gi);
+    }
+    if (WB == 2) {
+        rw.sw = *reinterpret_cast<const float *>(st + rp.a_scale + 4 * gi);
+        rw.sa0 = *reinterpret_cast<const float *>(st + rp.b_scale + 4 * gi);
+        rw.sa1 = *reinterpret_cast<const float *>(st + rp.b_scale1 + 4 * gi);
+    } else if (gi == 0) {
+        rw.sw = *reinterpret_cast<const float *>(st + rp.a_scale);
+        rw.sa0 = *reinterpret_cast<const float *>(st + rp.b_scale);
     }
 }
 
-// FP8 codes and the scale operands.  A lane holds 32 codes of its row (the
-// group's k half ks2), the same 32 k in both operands.  Weight scale
-// operand: bf16 (hi, hi, lo, lo) of sw.  Token operand: (hi, lo, hi, lo) of sa
-// on k-slot 0 lanes and zero elsewhere; `keep` false also zeroes a group past
-// K, which then adds exactly nothing.
+// FP8 codes and the outer-product operands.  A lane holds 32 codes of its
+// row (the group's k half ks2), the same 32 k in both operands.  A token
+// scale operand that is zero makes every product of its group zero, so the
+// group adds exactly nothing: `keep` false zeroes a group past K (the empty
+// half of an odd count's last stage, or a stage a k-split half runs only to
+// pair its barriers).  WB = 1 builds the operands of both groups of a stage
+// with its group 0 (lanes 32-63 carry group 1, kept if `keep1`).
 template <int WB>
-__device__ __forceinline__ void make_frags(Frags<WB> &f, const Raw<WB> &rw, bool keep) {
+__device__ __forceinline__ void make_frags(Frags<WB> &f, const Raw<WB> &rw, bool keep,
+                                           bool keep1 = true, bool scales = true) {
 #pragma unroll
     for (int blk = 0; blk < WB; ++blk) {
         f.A[blk] = codes_to_fp8(rw.a[blk]);
         f.B[blk] = codes_to_fp8(rw.b[blk]);
-        const float va = rw.sa[blk];
-        const uint32_t ha = pack_bf16x2(va, va);
-        const float la = va - bf16_lo(ha);
-        f.AS[blk] = u32x2{ha, pack_bf16x2(la, la)};
-        const float vb = keep ? rw.sb[blk] : 0.0f;
-        const uint32_t hb = pack_bf16x2(vb, 0.0f);
-        const uint32_t hl = pack_bf16x2(vb, vb - bf16_lo(hb));
-        f.BS[blk] = u32x2{hl, hl};
+    }
+    if (WB == 2) {
+        f.PA = rw.sw;
+        f.PB0 = keep ? rw.sa0 : 0.0f;
+        f.PB1 = keep ? rw.sa1 : 0.0f;
+    } else if (scales) {
+        const bool k = (threadIdx.x & 32) ? keep && keep1 : keep;
+        f.PA = rw.sw;
+        f.PB0 = k ? rw.sa0 : 0.0f;
     }
 }
 
 // The MFMA -> VALU pipeline of a wave.  The blocks of the two groups of a
-// stage form one stream j = 0 .. 2 NB - 1 (block j % NB, result slot j & 1):
-// the two MFMAs of block j go out while the VALU accumulates block j - 1, so
-// the matrix unit and the VALU work side by side, also across the group
-// boundary.
+// stage form one stream j = 0 .. 2 NB - 1 (group j / NB, result slot j & 1),
+// in the order of the outer products: WB = 2 visits blocks (0,0), (1,1),
+// (0,1), (1,0), so that elements 2q and 2q + 1 are the two blocks of one
+// two-block product (rows l / 32 with columns l / 32, then with columns
+// 1 - l / 32); WB = 1 has one block, and its product covers the two groups.
+// The product of elements 2q, 2q + 1 goes out once element 2q - 1 has read
+// the previous one; the code MFMA of element j goes out while the VALU
+// accumulates element j - 1, so the matrix unit and the VALU work side by
+// side, also across the group boundary.
 struct Pipe {
     f32x16 S[2];
-    f32x16 P[2];
+    f32x32 P;
 };
 
 template <int WB>
-__device__ __forceinline__ void issue_block(Pipe &p, const Frags<WB> &f, int t, int k) {
-    const int bi = t / WB, bj = t % WB;
-    p.S[k] = mfma_codes_32x32x64(f.A[bi], f.B[bj]);
-    p.P[k] = mfma_bf16_32x32x8(f.AS[bi], f.BS[bj], f32x16{});
+__device__ __forceinline__ constexpr int block_of(int j) {
+    return WB == 1 ? 0 : (j % 4 == 0 ? 0 : j % 4 == 1 ? 3 : j % 4 == 2 ? 1 : 2);
+}
+
+template <int WB>
+__device__ __forceinline__ void issue_block(Pipe &p, const Frags<WB> &f, int j) {
+    const int t = block_of<WB>(j), bi = t / WB, bj = t % WB;
+    p.S[j & 1] = mfma_codes_32x32x64(f.A[bi], f.B[bj]);
+}
+
+template <int WB>
+__device__ __forceinline__ void issue_scales(Pipe &p, const Frags<WB> &f, int j) {
+    p.P = mfma_f32_outer2(f.PA, (WB == 2 && (j % 4) == 2) ? f.PB1 : f.PB0);
 }
 
 // What the VALU does with the group sums of stream element jj (block jj % NB,
@@ -287,7 +318,11 @@ struct TakeGroup {
 
 template <int NB, class SK>
 __device__ __forceinline__ void valu_block(f32x16 (&acc)[NB], const Pipe &p, int jj, const SK &sk) {
-    const int t = jj % NB, k = jj & 1;
+    constexpr int WB = NB == 4 ? 2 : 1;
+    const int t = block_of<WB>(jj), k = jj & 1;
+    f32x16 P;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) P[i] = p.P[16 * k + i];
     if constexpr (SK::on) {
         // acc += S w with w = 1 for the wanted group and 0 for the others (acc
         // starts at zero, so it ends as that group's sums).  w is taken
@@ -297,35 +332,39 @@ __device__ __forceinline__ void valu_block(f32x16 (&acc)[NB], const Pipe &p, int
         const float w = jj / NB == sk.gsel ? 1.0f : 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            acc[t][i] = __builtin_fmaf(p.S[k][i], __builtin_fmaf(p.P[k][i], 0.0f, w), acc[t][i]);
+            acc[t][i] = __builtin_fmaf(p.S[k][i], __builtin_fmaf(P[i], 0.0f, w), acc[t][i]);
     } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[t][i] = __builtin_fmaf(p.S[k][i], p.P[k][i], acc[t][i]);
+        for (int i = 0; i < 16; ++i) acc[t][i] = __builtin_fmaf(p.S[k][i], P[i], acc[t][i]);
     }
 }
 
-// Issue stream element j while the VALU finishes element j - 1: one MFMA,
-// then half of the VALU work, twice.  The empty asm pins the updated
-// accumulator so later passes cannot sink the VALU work below the following
-// MFMAs.
+// Issue stream element j while the VALU finishes element j - 1: the code
+// MFMA, the VALU work, and (even j with WB = 2) the next outer product after
+// it, which overwrites the one element j - 1 has just read.  The empty asm
+// pins the updated accumulator so later passes cannot sink the VALU work
+// below the following MFMAs.
 template <int WB, class SK>
 __device__ __forceinline__ void pair(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f, int j,
                                      const SK &sk) {
     constexpr int NB = WB * WB;
-    issue_block<WB>(p, f, j % NB, j & 1);
+    issue_block<WB>(p, f, j);
     valu_block<NB>(acc, p, j - 1, sk);
+    asm volatile("" : "+v"(acc[block_of<WB>(j - 1)]));
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    asm volatile("" : "+v"(acc[(j - 1) % NB]));
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+    if (WB == 2 && (j & 1) == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_scales<WB>(p, f, j);
+    }
     __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int WB, class SK>
 __device__ __forceinline__ void group_first(f32x16 (&acc)[WB * WB], Pipe &p, const Frags<WB> &f,
                                             const SK &sk) {
-    issue_block<WB>(p, f, 0, 0);
+    issue_block<WB>(p, f, 0);
+    issue_scales<WB>(p, f, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 1; j < WB * WB; ++j) pair<WB>(acc, p, f, j, sk);
@@ -340,7 +379,7 @@ template <int WB, class SK>
 __device__ __forceinline__ void group_drain(f32x16 (&acc)[WB * WB], Pipe &p, const SK &sk) {
     constexpr int NB = WB * WB;
     valu_block<NB>(acc, p, 2 * NB - 1, sk);
-    asm volatile("" : "+v"(acc[NB - 1]));
+    asm volatile("" : "+v"(acc[block_of<WB>(2 * NB - 1)]));
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -383,10 +422,12 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
     if (ns > 3) issue_stage<WB>(b3, cp, op, src(3), tail(3));
     wait_stages<L>(ns < 4 ? ns - 1 : 3);
     barrier();
+    // the last real stage, whose second group is empty for an odd count
+    const int last = NULLS ? nr - 1 : ns - 1;
     Raw<WB> raw;
     Frags<WB> f;
     read_raw<WB>(raw, b0, rp, 0);
-    make_frags<WB>(f, raw, rp.keep_b);
+    make_frags<WB>(f, raw, !NULLS || nr > 0, !(odd && last == 0));
 
     // Stage s: group 2s computes while group 2s + 1 is read; then stage
     // s + 1 is published and stage s's buffer (read by every wave before
@@ -399,10 +440,7 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
         read_raw<WB>(raw, cur, rp, 1);
         __builtin_amdgcn_sched_barrier(0);
         group_first<WB>(acc, p, f, sk);
-        if constexpr (NULLS)
-            make_frags<WB>(f, raw, rp.keep_b && s < nr && !(odd && s == nr - 1));
-        else
-            make_frags<WB>(f, raw, rp.keep_b && !(odd && s == ns - 1));
+        make_frags<WB>(f, raw, (!NULLS || s < nr) && !(odd && s == last), true, false);
         wait_next_stage<L>(s, ns);
         barrier();
         if (s + 4 < ns) issue_stage<WB>(cur, cp, op, src(s + 4), tail(s + 4));
@@ -411,10 +449,7 @@ __device__ __forceinline__ void k_loop(uint8_t *__restrict__ b0, uint8_t *__rest
         read_raw<WB>(raw, nxt, rp, 0);
         __builtin_amdgcn_sched_barrier(0);
         group_second<WB>(acc, p, f, sk);
-        if constexpr (NULLS)
-            make_frags<WB>(f, raw, rp.keep_b && s + 1 < nr);
-        else
-            make_frags<WB>(f, raw, rp.keep_b);
+        make_frags<WB>(f, raw, !NULLS || s + 1 < nr, !(odd && s + 1 == last));
         group_drain<WB>(acc, p, sk);
     };
     for (int s = 0; s < ns; s += 4) {
@@ -839,7 +874,7 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
                 uint32_t w = 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float y = __builtin_amdgcn_fmed3f(acc[bi * WB + bj][4 * q + j] * inv, -7.0f, 7.0f);
+                    const float y = acc[bi * WB + bj][4 * q + j] * inv;   // |y| < 7.5: no clamp
                     w |= (__float_as_uint(y + 12582912.0f) & 15u) << (4 * j);
                 }
                 const uint32_t sg = w & 0x8888u, one = sg >> 3;
@@ -1073,11 +1108,16 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
         if constexpr (MXF) {                      // [k block][row] bytes, k block ks2 of group 0
             rp.a_scale = C::SA_OFF + ks2 * BT + wn * 32 * WB + r32;
             rp.b_scale = C::SB_OFF + ks2 * BT + wm * 32 * WB + r32;
-        } else {
-            rp.a_scale = C::SA_OFF + (wn * 32 * WB + r32) * GC * 4;
-            rp.b_scale = C::SB_OFF + (wm * 32 * WB + r32) * GC * 4;
+            rp.b_scale1 = rp.b_scale;
+        } else if (WB == 2) {                     // [row][group] fp32, group 0
+            rp.a_scale = C::SA_OFF + (wn * 64 + lane) * GC * 4;
+            rp.b_scale = C::SB_OFF + (wm * 64 + lane) * GC * 4;
+            rp.b_scale1 = C::SB_OFF + (wm * 64 + (lane ^ 32)) * GC * 4;
+        } else {                                  // group ks2 of the stage
+            rp.a_scale = C::SA_OFF + (wn * 32 + r32) * GC * 4 + 4 * ks2;
+            rp.b_scale = C::SB_OFF + (wm * 32 + r32) * GC * 4 + 4 * ks2;
+            rp.b_scale1 = rp.b_scale;
         }
-        rp.keep_b = ks2 == 0;
     }
 
     f32x16 acc[NB];

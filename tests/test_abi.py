@@ -51,10 +51,17 @@ def test_version_and_status_strings(lib):
 def test_workspace_sizes(lib):
     K, r, M = 3072, 32, 4608
     down = lib.svdq_quantize_act_down_workspace_bytes(M, K, r)
-    assert down == 6 * M * r * 4                  # six chunks of 8 groups; 256-aligned here
+    # chunks of 4 groups for r <= 64 at up to 64 groups, 8 beyond, 2 for r > 64 or at most
+    # 512 tokens (r <= 32); a single chunk needs no partial sums
+    assert down == 12 * M * r * 4                 # twelve chunks of 4 groups; 256-aligned here
     assert lib.svdq_quantize_act_down_workspace_bytes(M, K, 0) == 0
-    assert lib.svdq_quantize_act_down_workspace_bytes(M, 512, 32) == 0     # one chunk
+    assert lib.svdq_quantize_act_down_workspace_bytes(M, 256, 32) == 0     # one chunk
+    assert lib.svdq_quantize_act_down_workspace_bytes(M, 512, 32) == 2 * M * 32 * 4
     assert lib.svdq_quantize_act_down_workspace_bytes(M, 512, 128) == 4 * M * 128 * 4
+    assert lib.svdq_quantize_act_down_workspace_bytes(M, 12288, 32) == 24 * M * 32 * 4
+    assert lib.svdq_quantize_act_down_workspace_bytes(M, 12288, 64) == 48 * M * 64 * 4
+    assert lib.svdq_quantize_act_down_workspace_bytes(256, K, 32) == 24 * 256 * 32 * 4
+    assert lib.svdq_quantize_act_down_workspace_bytes(256, 128, 32) == 0  # one chunk of 2
     assert lib.svdq_quantize_act_down_workspace_bytes(0, K, r) == 0
     lin = lib.svdq_linear_workspace_bytes(M, K, r)
     assert lin == M * K // 2 + M * (K // 64) * 4 + M * r * 4 + down
