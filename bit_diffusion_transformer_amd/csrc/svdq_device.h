@@ -100,15 +100,19 @@ __device__ __forceinline__ f32x16 mfma_mxfp4_32x32x64(u32x4 a, uint32_t sa, u32x
 // and erf(-z) = -erf(z); in fp32 with the hardware reciprocal and 2^x, the
 // result is within about 3e-7 |x| of the exact GELU (far below a bf16 ulp of
 // the output), for a fraction of the instructions of a full-precision erf.
+// With z = |x| / sqrt 2 folded into the constants (p / sqrt 2; the a_i
+// halved, so the polynomial gives h = (1 - erf(z)) / 2 directly;
+// exp(-z^2) = 2^(x^2 (-log2(e) / 2))): GELU(x) = x - x h for x >= 0, x h
+// otherwise.
 __device__ __forceinline__ float gelu_erf(float x) {
-    const float z = fabsf(x) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
-    float p = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
-    p = __builtin_fmaf(t, p, 1.421413741f);
-    p = __builtin_fmaf(t, p, -0.284496736f);
-    p = __builtin_fmaf(t, p, 0.254829592f);
-    const float q = p * t * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);   // 1 - erf(z)
-    return 0.5f * x * (x >= 0.0f ? 2.0f - q : q);
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(x), 0.23164188861846924f, 1.0f));
+    float p = __builtin_fmaf(t, 0.5307027101516724f, -0.726576030254364f);
+    p = __builtin_fmaf(t, p, 0.710706889629364f);
+    p = __builtin_fmaf(t, p, -0.14224836230278015f);
+    p = __builtin_fmaf(t, p, 0.1274147927761078f);
+    const float e = __builtin_amdgcn_exp2f(x * x * -0.7213475108146667f);
+    const float xh = x * (p * t * e);                        // x (1 - erf(z)) / 2
+    return x >= 0.0f ? x - xh : xh;
 }
 
 // ---------------------------------------------------------------- 4-bit operands

@@ -11,8 +11,9 @@
 namespace svdq {
 
 // One launch covers the whole output.  Workgroups [0, nq) are quarter tiles
-// (64 x 64): quadrant b % 4 of tile tq0 + b / 4 of the 128 x 128 tile grid,
-// used for the tiles of a partial last round.  They come first so that they
+// (64 x 64): with tq0 < 0 the tiles of the 64 x 64 grid (the whole output);
+// otherwise quadrant b % 4 of tile tq0 + b / 4 of the 128 x 128 tile grid,
+// for the tiles of a partial last round.  They come first so that they
 // run alongside the first round of full tiles instead of alone after the
 // last one.  Workgroups [nq, nq + nfull) are full tiles 0 .. nfull - 1, each
 // XCD taking a contiguous range of them (consecutive workgroups go to
@@ -31,7 +32,15 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
     } sm;
     const int64_t nbm = (M + TILE - 1) / TILE, nbn = (N + TILE - 1) / TILE;
     int64_t b = blockIdx.x, tm, tn;
-    if (b < nq) {
+    if (b < nq && tq0 < 0) {
+        // the whole output as 64 x 64 tiles, rastered on their own grid with
+        // each XCD taking a contiguous range (as the full tiles below)
+        const int64_t nqm = (M + 63) / 64, nqn = (N + 63) / 64;
+        if ((nq & 7) == 0) b = (b & 7) * (nq >> 3) + (b >> 3);
+        raster(b, nqm, nqn, tm, tn);
+        tile_body<1>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm.quarter, 64 * tm,
+                     64 * tn);
+    } else if (b < nq) {
         raster(tq0 + b / 4, nbm, nbn, tm, tn);
         const int64_t m0 = tm * TILE + 64 * (b & 1);
         const int64_t n0 = tn * TILE + 64 * ((b >> 1) & 1);
@@ -77,31 +86,41 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
                             int r, uint16_t *Y, hipStream_t stream) {
     const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
     const int policy = tile_policy();
-    // Grids of at most one 128 x 128 tile per compute unit run as k-split
-    // tiles (two waves per SIMD on half the K loop each instead of one on all
-    // of it); at most a quarter of a tile per compute unit, as k-split
-    // 64 x 64 tiles.  Needs three groups or more (each half gets one).
-    const int64_t cus = wg_slots() / 2;
+    // The automatic choice (measured on the layer shapes at 64 .. 4096 tokens):
+    //   - at most one 64 x 64 tile per two compute units, or per compute unit
+    //     with 96 groups or more along K: k-split 64 x 64 tiles (two waves
+    //     per SIMD on half the K loop each), given three groups or more (each
+    //     half gets one);
+    //   - a single partial round of at most 9/16 of the workgroup slots: all
+    //     64 x 64 tiles (four times the workgroups);
+    //   - otherwise 128 x 128 tiles, with a partial last round of at most a
+    //     quarter of the slots run as 64 x 64 tiles alongside the first round.
+    const int64_t slots = wg_slots();
+    const int64_t cus = slots / 2;
+    const int64_t qtiles = ((M + 63) / 64) * ((N + 63) / 64);
     const bool ks_ok = K / kGroup >= 3;
-    if (policy == 3 || policy == 4 || (policy == 0 && ks_ok && tiles <= cus)) {
-        if (ks_ok) {
-            const bool quarter = policy == 4 || (policy == 0 && 4 * tiles <= cus);
-            return launch_w4a4_gemm_ks(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, quarter,
-                                       stream);
+    const int pol = (policy == 3 || policy == 4) && !ks_ok ? 0 : policy;
+    const bool ks_auto = 2 * qtiles <= cus || (qtiles <= cus && K / kGroup >= 96);
+    if (pol == 3 || pol == 4 || (pol == 0 && ks_ok && ks_auto))
+        return launch_w4a4_gemm_ks(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, pol != 3,
+                                   stream);
+    int64_t rest = 0;
+    if (pol == 2) {
+        rest = tiles;
+    } else if (pol == 0) {
+        if (16 * tiles <= 9 * slots) {
+            rest = tiles;
+        } else {
+            rest = tiles % slots;
+            if (rest * 4 > slots) rest = 0;
         }
     }
-    int64_t rest = 0;
-    if (policy == 2) {
-        rest = tiles;
-    } else if (policy == 0) {
-        const int64_t slots = wg_slots();
-        rest = tiles % slots;
-        if (rest * 4 > slots * 3) rest = 0;
-    }
     const int64_t full = tiles - rest;
-    const int64_t nq = 4 * rest;
+    // all 64 x 64 tiles: one workgroup per tile of their own grid (tq0 = -1);
+    // a partial last round: the four quadrants of full tiles full .. tiles - 1
+    const int64_t nq = rest == tiles ? qtiles : 4 * rest;
     w4a4_lr_gemm_kernel<<<(unsigned)(nq + full), NTHR, 0, stream>>>(
-        qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, nq, full, full);
+        qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, nq, rest == tiles ? -1 : full, full);
     return hipGetLastError();
 }
 
