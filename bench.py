@@ -127,7 +127,15 @@ def k2_bytes(M, N, K, r):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_lr_gemm_qkv_traffic.txt")
 _CSRC = os.path.join(ROOT, "bit_diffusion_transformer_amd", "csrc")
-GEMM_SOURCE = (os.path.join(_CSRC, "w4a4_tile.h"), os.path.join(_CSRC, "w4a4_gemm.hip"))
+GEMM_SOURCE = tuple(os.path.join(_CSRC, f) for f in
+                    ("w4a4_tile.h", "w4a4_gemm.hip", "svdq_device.h", "svdq_internal.h"))
+K1_SOURCE = tuple(os.path.join(_CSRC, f) for f in
+                  ("quant_down.hip", "svdq_device.h", "svdq_internal.h"))
+# counter summaries of the default line's other kernels: K1 at the line's size, the
+# GEMM at 256 tokens
+K1_TRAFFIC = (os.path.join(ROOT, "profiles", "quantize_act_down_mlp_up_traffic.txt"), K1_SOURCE)
+M256_TRAFFIC = (os.path.join(ROOT, "profiles", "w4a4_lr_gemm_quarter_mlp_up_m256_traffic.txt"),
+                GEMM_SOURCE)
 
 
 # workload -> (committed counter summary, kernel source it was taken with)
@@ -159,6 +167,12 @@ def measured_traffic(workload):
     path, source = TRAFFIC[workload]
     if path is None:
         path, source = TRAFFIC_FILE, GEMM_SOURCE
+    return traffic_from(path, source)
+
+
+def traffic_from(path, source):
+    """traffic_bytes_per_call of a committed counter summary whose kernel_source_sha256
+    matches the current source files; else None."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -843,7 +857,9 @@ def small_m_line(spec, dev, n):
                                                / PEAK_HBM_GBS, 4),
            "linear_us": round(t["linear"] * 1e6, 2),
            "linear_tops": round(ops / t["linear"] / 1e12, 2),
-           "kernel": "w4a4_lr_gemm_kernel"}
+           "kernel": "w4a4_lr_gemm_quarter_kernel (64 x 64 tiles, the tile policy's choice "
+                     "at this size)",
+           "gemm_traffic": traffic_from(*M256_TRAFFIC) if spec.name == "mlp_up" else None}
     del lb
     return out
 
@@ -946,7 +962,10 @@ def main():
         "quantize_act_down": {"us": round(t_quant * 1e6, 2),
                               "algorithmic_bytes": k1_bytes(M, K, r),
                               "GB/s": round(k1_bytes(M, K, r) / t_quant / 1e9, 1),
-                              "hbm_frac": round(k1_bytes(M, K, r) / t_quant / 1e9 / PEAK_HBM_GBS, 4)},
+                              "hbm_frac": round(k1_bytes(M, K, r) / t_quant / 1e9 / PEAK_HBM_GBS, 4),
+                              "traffic": (traffic_from(*K1_TRAFFIC)
+                                          if args.workload == "mlp_up" and args.M is None
+                                          else None)},
         "timing": {"linear_us": round(t_lin * 1e6, 2),
                    "per_kernel": "median of 3 interleaved rounds; each round %.1f s of untimed "
                                  "calls, then %d calls between HIP events" % (SETTLE_S, n_k),

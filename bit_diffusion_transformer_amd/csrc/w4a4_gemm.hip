@@ -11,9 +11,8 @@
 namespace svdq {
 
 // One launch covers the whole output.  Workgroups [0, nq) are quarter tiles
-// (64 x 64): with tq0 < 0 the tiles of the 64 x 64 grid (the whole output);
-// otherwise quadrant b % 4 of tile tq0 + b / 4 of the 128 x 128 tile grid,
-// for the tiles of a partial last round.  They come first so that they
+// (64 x 64): quadrant b % 4 of tile tq0 + b / 4 of the 128 x 128 tile grid,
+// used for the tiles of a partial last round.  They come first so that they
 // run alongside the first round of full tiles instead of alone after the
 // last one.  Workgroups [nq, nq + nfull) are full tiles 0 .. nfull - 1, each
 // XCD taking a contiguous range of them (consecutive workgroups go to
@@ -32,15 +31,7 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
     } sm;
     const int64_t nbm = (M + TILE - 1) / TILE, nbn = (N + TILE - 1) / TILE;
     int64_t b = blockIdx.x, tm, tn;
-    if (b < nq && tq0 < 0) {
-        // the whole output as 64 x 64 tiles, rastered on their own grid with
-        // each XCD taking a contiguous range (as the full tiles below)
-        const int64_t nqm = (M + 63) / 64, nqn = (N + 63) / 64;
-        if ((nq & 7) == 0) b = (b & 7) * (nq >> 3) + (b >> 3);
-        raster(b, nqm, nqn, tm, tn);
-        tile_body<1>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm.quarter, 64 * tm,
-                     64 * tn);
-    } else if (b < nq) {
+    if (b < nq) {
         raster(tq0 + b / 4, nbm, nbn, tm, tn);
         const int64_t m0 = tm * TILE + 64 * (b & 1);
         const int64_t n0 = tn * TILE + 64 * ((b >> 1) & 1);
@@ -53,6 +44,25 @@ w4a4_lr_gemm_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa
         tile_body<2>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm.full, tm * TILE,
                      tn * TILE);
     }
+}
+
+// The whole output as 64 x 64 tiles, one workgroup each, rastered on their
+// own grid with each XCD taking a contiguous range (as the full tiles
+// above).  A kernel of its own so that its register budget allows three or
+// four workgroups per compute unit (the shared kernel is sized for 128 x 128
+// tiles: two).
+__global__ void __launch_bounds__(NTHR, 3)
+w4a4_lr_gemm_quarter_kernel(const uint8_t *__restrict__ qa, const float *__restrict__ sa,
+                            const uint8_t *__restrict__ qw, const float *__restrict__ sw,
+                            const float *__restrict__ xl1, const uint16_t *__restrict__ L2,
+                            const uint16_t *__restrict__ bias, int act, int64_t M, int64_t N,
+                            int64_t K, int r, uint16_t *__restrict__ Y) {
+    __shared__ Smem<1> sm;
+    const int64_t nqm = (M + 63) / 64, nqn = (N + 63) / 64, nq = nqm * nqn;
+    int64_t b = blockIdx.x, tm, tn;
+    if ((nq & 7) == 0) b = (b & 7) * (nq >> 3) + (b >> 3);
+    raster(b, nqm, nqn, tm, tn);
+    tile_body<1>(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, sm, 64 * tm, 64 * tn);
 }
 
 static std::atomic<int> g_tile_policy{0};
@@ -87,12 +97,11 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
     const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
     const int policy = tile_policy();
     // The automatic choice (measured on the layer shapes at 64 .. 4096 tokens):
-    //   - at most one 64 x 64 tile per two compute units, or per compute unit
-    //     with 96 groups or more along K: k-split 64 x 64 tiles (two waves
-    //     per SIMD on half the K loop each), given three groups or more (each
-    //     half gets one);
-    //   - a single partial round of at most 9/16 of the workgroup slots: all
-    //     64 x 64 tiles (four times the workgroups);
+    //   - at most one 64 x 64 tile per compute unit: k-split 64 x 64 tiles
+    //     (two waves per SIMD on half the K loop each), given three groups or
+    //     more (each half gets one);
+    //   - 128 x 128 tiles for at most 3/4 of the workgroup slots: all 64 x 64
+    //     tiles (four times the workgroups, up to four per compute unit);
     //   - otherwise 128 x 128 tiles, with a partial last round of at most a
     //     quarter of the slots run as 64 x 64 tiles alongside the first round.
     const int64_t slots = wg_slots();
@@ -100,27 +109,29 @@ hipError_t launch_w4a4_gemm(const uint8_t *qa, const float *sa, const uint8_t *q
     const int64_t qtiles = ((M + 63) / 64) * ((N + 63) / 64);
     const bool ks_ok = K / kGroup >= 3;
     const int pol = (policy == 3 || policy == 4) && !ks_ok ? 0 : policy;
-    const bool ks_auto = 2 * qtiles <= cus || (qtiles <= cus && K / kGroup >= 96);
-    if (pol == 3 || pol == 4 || (pol == 0 && ks_ok && ks_auto))
+    if (pol == 3 || pol == 4 || (pol == 0 && ks_ok && qtiles <= cus))
         return launch_w4a4_gemm_ks(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, pol != 3,
                                    stream);
     int64_t rest = 0;
     if (pol == 2) {
         rest = tiles;
     } else if (pol == 0) {
-        if (16 * tiles <= 9 * slots) {
+        if (4 * tiles <= 3 * slots) {
             rest = tiles;
         } else {
             rest = tiles % slots;
             if (rest * 4 > slots) rest = 0;
         }
     }
+    if (rest == tiles) {
+        w4a4_lr_gemm_quarter_kernel<<<(unsigned)qtiles, NTHR, 0, stream>>>(
+            qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y);
+        return hipGetLastError();
+    }
     const int64_t full = tiles - rest;
-    // all 64 x 64 tiles: one workgroup per tile of their own grid (tq0 = -1);
-    // a partial last round: the four quadrants of full tiles full .. tiles - 1
-    const int64_t nq = rest == tiles ? qtiles : 4 * rest;
+    const int64_t nq = 4 * rest;
     w4a4_lr_gemm_kernel<<<(unsigned)(nq + full), NTHR, 0, stream>>>(
-        qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, nq, rest == tiles ? -1 : full, full);
+        qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r, Y, nq, full, full);
     return hipGetLastError();
 }
 

@@ -481,16 +481,16 @@ int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *packed, const ui
 /*
  * Test hook: how svdq_w4a4_lr_gemm (and svdq_linear, svdq_linear_noalloc)
  * tile the output.
- *   SVDQ_TILES_AUTO    the default, with S workgroup slots (two per compute
- *                      unit): when the output has at most one 64 x 64 tile
- *                      per two compute units, or per compute unit with
- *                      K / 64 >= 96 (and K / 64 >= 3), k-split 64 x 64
- *                      tiles (each workgroup's two halves run half of the K
- *                      loop each and add their partial sums in LDS); else,
- *                      when its 128 x 128 tiles fill at most 9/16 of S, all
- *                      64 x 64 tiles; else 128 x 128 tiles for whole rounds
- *                      of S and 64 x 64 tiles for a partial last round of at
- *                      most S / 4 tiles (a larger one runs as 128 x 128)
+ *   SVDQ_TILES_AUTO    the default, with S workgroup slots for 128 x 128
+ *                      tiles (two per compute unit): when the output has at
+ *                      most one 64 x 64 tile per compute unit (and
+ *                      K / 64 >= 3), k-split 64 x 64 tiles (each workgroup's
+ *                      two halves run half of the K loop each and add their
+ *                      partial sums in LDS); else, when its 128 x 128 tiles
+ *                      fill at most 3/4 of S, all 64 x 64 tiles; else
+ *                      128 x 128 tiles for whole rounds of S and 64 x 64
+ *                      tiles for a partial last round of at most S / 4 tiles
+ *                      (a larger one runs as 128 x 128)
  *   SVDQ_TILES_FULL    128 x 128 tiles only
  *   SVDQ_TILES_QUARTER 64 x 64 tiles only
  *   SVDQ_TILES_KSPLIT, SVDQ_TILES_KSPLIT_QUARTER  k-split 128 x 128 / 64 x 64
