@@ -64,6 +64,15 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
     const int nt = r >> 4;
     const int64_t kbase = g0 * kGroup;
     const int kvalid = gc * kGroup;
+    // Stored addresses: a per-lane part here, a wave-uniform part per group.
+    // Codes (row pairs, code_offset): byte 32 g + 8 ks of the row is at
+    // (row / 2) K + (row % 2) w + 64 g - 32 (g % 2) + 8 ks, w = 64 except in
+    // the 32-byte last chunk of an odd group count (w = 32).  Scales
+    // (stage-major, scale_index): 2 row + 2 M (g / 2) + g % 2.
+    const int64_t kb = K / 2;
+    uint8_t *const qrow = qa + (row >> 1) * 2 * kb + 8 * ks;
+    const int64_t qodd = (row & 1) * 64;
+    float *const srow = static_cast<float *>(sa) + 2 * row;
 
     // 1. lambda and the L1 chunk, then X, all in flight together
     float lam[NLAM];
@@ -151,11 +160,13 @@ quant_down_kernel(const uint16_t *X, const float *__restrict__ lambda,
             } else {
                 const float s = quantize_group16(v, packed);
                 if (row_ok) {
-                    *reinterpret_cast<u32x2 *>(qa + code_offset(row, K / 2, g * (kGroup / 2) + 8 * ks)) = packed;
+                    const bool half = (G & 1) && g == G - 1;           // 32-byte last chunk
+                    const int64_t go = 64 * g - 32 * (g & 1);
+                    *reinterpret_cast<u32x2 *>(qrow + go + (half ? qodd / 2 : qodd)) = packed;
                     if (ks == 0) {
-                        float *sp = static_cast<float *>(sa);
-                        sp[scale_index(row, g, M)] = s;
-                        if ((G & 1) && g == G - 1) sp[scale_index(row, G, M)] = 0.0f;   // pad
+                        const int64_t so = 2 * M * (g >> 1) + (g & 1);
+                        srow[so] = s;
+                        if (half) srow[so + 1] = 0.0f;                  // pad (g even here)
                     }
                 }
             }
