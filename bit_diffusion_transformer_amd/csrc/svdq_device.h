@@ -116,52 +116,76 @@ __device__ __forceinline__ float gelu_erf(float x) {
 }
 
 // ---------------------------------------------------------------- 4-bit operands
-// Stored layout of the INT4 codes (qa, qw): two per byte, code e of each block
-// of 16 consecutive codes in nibble e of the block's 8 bytes (element 2j in
-// the low nibble of byte j); a nibble holds |c_e| in its low three bits and
-// the sign of c_((e - 1) mod 16) in its top bit.  One AND then gives the FP8
-// (E4M3) bytes of the even codes and a funnel shift plus an AND those of the
-// odd codes: the byte s000 0mmm is the E4M3 subnormal (-1)^s m 2^-9, so the
-// codes enter the FP8 matrix instruction as exact multiples of 2^-9, and the
-// instruction's block scale 2^9 on each operand makes its sums exact
-// integers (|sum| <= 64 * 49).
+// Stored layout of the INT4 codes (qa, qw): each block of 16 consecutive codes
+// of a row takes 8 bytes (two little-endian words W0, W1).  Code e = 8h + i
+// (h = 0, 1; i = 0..7) is field 2i + h of a 96-bit image (bits 6f .. 6f + 5
+// for field f) holding the OCP FP6 E2M3 encoding of c / 8: |c| in bits 0-2,
+// bits 3-4 zero, the sign in bit 5 (a zero code has none).  With the image
+// words I0, I1, I2 (bits 0-31, 32-63, 64-95),
+//   W0 = I0 | (I2 & kFree0),   W1 = I1 | (I2 & kFree1),
+// where kFree0 / kFree1 are the always-zero bits 3-4 of the fields of I0 / I1
+// (bit positions p with p mod 6 in {3, 4}); the two masks are disjoint and
+// together cover every bit I2 can hold, so the fold loses nothing and one AND
+// per word (two for I2) unfolds it.  The E2M3 subnormal m / 8 is exact, so the
+// codes enter the FP6 matrix instruction as exact multiples of 1/8 and the
+// instruction's block scale 2^3 on each operand makes its sums exact integers
+// (|sum| <= 64 * 49).
+constexpr uint32_t kFree0 = 0x18618618u, kFree1 = 0x86186186u;
+constexpr uint32_t kKeep0 = ~kFree0, kKeep1 = ~kFree1;     // fields of I0 / I1
+
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+
+// The FP6 images of two 16-code blocks from 32 values that are exact
+// multiples of 1/8 in [-7/8, 7/8] (v_cvt_scalef32_2xpk16_fp6_f32, scale 1:
+// element j of a goes to field 2j, element j of b to field 2j + 1; so a block's
+// codes 0-7 go in a, its codes 8-15 in b, the first block at j < 8).  Words
+// 0-2 are the first block's image, words 3-5 the second's.
+__device__ __forceinline__ i32x6 fp6_images(const f32x16v &a, const f32x16v &b) {
+    return __builtin_bit_cast(i32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f));
+}
+
+// Fold one block's image words into the stored words.
+__device__ __forceinline__ u32x2 fold_image(uint32_t i0, uint32_t i1, uint32_t i2) {
+    return u32x2{(i2 & kFree0) | i0, (i2 & kFree1) | i1};
+}
+
+// c / 8 from a value y whose nearest integer (ties to even) is the code c:
+// y + 1.5 * 2^23 rounds to 1.5 * 2^23 + c, and one fma scales that by 1/8 and
+// removes the bias exactly (every term is a multiple of 1/8 far inside fp32's
+// range); a zero code comes out as +0, never -0.
+__device__ __forceinline__ float code_eighths(float y) {
+    return __builtin_fmaf(y + 12582912.0f, 0.125f, -1572864.0f);
+}
 
 // Two words of 8 two's-complement nibbles (codes 0-7 and 8-15 of a block,
 // code e in nibble e mod 8, every code in [-7, 7]) -> the stored words.
 __device__ __forceinline__ u32x2 store_code_words(uint32_t w0, uint32_t w1) {
-    // nibble-wise two's complement -> sign | magnitude: a negative nibble t
-    // (bit 3 set) becomes 8 | (16 - t), i.e. its bits flipped, plus one
-    auto sign_mag = [](uint32_t w) {
-        const uint32_t sg = w & 0x88888888u;
-        const uint32_t one = sg >> 3;
-        const uint32_t flip = (sg << 1) - one;       // 0xF in each negative nibble
-        return (((w ^ flip) + one) & 0x77777777u) | sg;
-    };
-    const uint32_t s0 = sign_mag(w0), s1 = sign_mag(w1);
-    // each nibble takes the sign bit of the nibble below it (cyclically over
-    // the block's 16 nibbles)
-    const uint32_t r0 = __builtin_amdgcn_alignbit(s0, s1, 28);
-    const uint32_t r1 = __builtin_amdgcn_alignbit(s1, s0, 28);
-    return u32x2{(r0 & 0x88888888u) | (s0 & 0x77777777u), (r1 & 0x88888888u) | (s1 & 0x77777777u)};
+    f32x16v a = {}, b = {};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (float)((int)(w0 << (28 - 4 * j)) >> 28) * 0.125f;
+        b[j] = (float)((int)(w1 << (28 - 4 * j)) >> 28) * 0.125f;
+    }
+    const i32x6 img = fp6_images(a, b);
+    return fold_image((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
 }
 
-// The FP8 operand of 32 stored codes (two blocks, one 16-byte read).  The
-// slot order (codes 0, 2, 4, 6 | 1, 3, 5, 7 | 8, 10, .. of each block) is the
-// same for both GEMM operands, so the k pairing is preserved.
-__device__ __forceinline__ i32x8 codes_to_fp8(u32x4 x) {
-    constexpr uint32_t M = 0x87878787u;
-    return i32x8{(int)(x.x & M), (int)(__builtin_amdgcn_alignbit(x.y, x.x, 4) & M),
-                 (int)(x.y & M), (int)(__builtin_amdgcn_alignbit(x.x, x.y, 4) & M),
-                 (int)(x.z & M), (int)(__builtin_amdgcn_alignbit(x.w, x.z, 4) & M),
-                 (int)(x.w & M), (int)(__builtin_amdgcn_alignbit(x.z, x.w, 4) & M)};
+// The FP6 operand of 32 stored codes (two blocks, one 16-byte read): the two
+// images unfolded, 192 bits in six registers.  Field order is the same for
+// both GEMM operands, so the k pairing is preserved.
+__device__ __forceinline__ i32x8 codes_to_fp6(u32x4 x) {
+    return i32x8{(int)(x.x & kKeep0), (int)(x.y & kKeep1), (int)((x.x & kFree0) | (x.y & kFree1)),
+                 (int)(x.z & kKeep0), (int)(x.w & kKeep1), (int)((x.z & kFree0) | (x.w & kFree1)),
+                 0, 0};
 }
 
 // 32x32 output tile of exact per-group code sums S = sum_k qa qw over one
 // group of 64: lane l supplies row l % 32 and 32 of the group's codes
-// (k half l / 32) as FP8; the 32x32 output layout.  Scale bytes 127 + 9
-// multiply each operand by 2^9.
+// (k half l / 32) as FP6 (E2M3); the 32x32 output layout.  Scale bytes 127 + 3
+// multiply each operand by 2^3.
 __device__ __forceinline__ f32x16 mfma_codes_32x32x64(i32x8 a, i32x8 b) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, f32x16{}, 0, 0, 0, 136, 0, 136);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, f32x16{}, 2, 2, 0, 130, 0, 130);
 }
 
 // ---------------------------------------------------------------- quantizer
@@ -170,7 +194,7 @@ __device__ __forceinline__ f32x16 mfma_codes_32x32x64(i32x8 a, i32x8 b) {
 // l, l^16, l^32, l^48 (16 consecutive values per lane).  Returns the group
 // scale s = max|v| / 7 (every lane of the group gets it) and writes the
 // lane's 16 codes (one block of the stored layout above) into `packed`.
-// The code is rint(fl32(v * fl32(1/s))) clamped to [-7, 7]; a
+// The code is rint(fl32(v * fl32(1/s))), always within [-7, 7]; a
 // zero scale or a non-finite 1/s gives zero codes.  Division is IEEE
 // correctly rounded (hipcc's default); no contraction is allowed here.
 __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &packed) {
@@ -197,21 +221,15 @@ __device__ __forceinline__ float quantize_group16(const float (&v)[16], u32x2 &p
     // No clamp is needed: with s = fl(amax / 7) and inv = fl(1 / s) finite
     // (s >= 2^-128, so s keeps at least 21 significant bits),
     // |v inv| <= amax inv <= 7 (1 + 2^-20) < 7.5, which rounds to at most 7.
-    // rint via the 1.5*2^23 bias: y + 12582912 rounds (nearest even) to an
-    // integer whose low 4 bits are the code's two's-complement nibble.  Funnel-shifting the nibbles in from the top
-    // leaves element j in nibble j; store_code_words makes the stored form.
-    uint32_t w0 = 0, w1 = 0;
+    // Codes 0-7 of the block go to a, 8-15 to b (the stored field order).
+    f32x16v a = {}, b = {};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float y = v[j] * inv;
-        w0 = __builtin_amdgcn_alignbit(__float_as_uint(y + 12582912.0f), w0, 4);
+        a[j] = code_eighths(v[j] * inv);
+        b[j] = code_eighths(v[8 + j] * inv);
     }
-#pragma unroll
-    for (int j = 8; j < 16; ++j) {
-        const float y = v[j] * inv;
-        w1 = __builtin_amdgcn_alignbit(__float_as_uint(y + 12582912.0f), w1, 4);
-    }
-    packed = store_code_words(w0, w1);
+    const i32x6 img = fp6_images(a, b);
+    packed = fold_image((uint32_t)img[0], (uint32_t)img[1], (uint32_t)img[2]);
     return s;
 }
 

@@ -1,6 +1,6 @@
 // w4a4_gemm_sums.hip -- test hook: the exact per-group integer sums of the
 // W4A4 GEMM, taken from the production tile code (w4a4_tile.h: the same
-// global -> LDS ring, swizzle, row-pair copies, odd-group tail stage, FP8
+// global -> LDS ring, swizzle, row-pair copies, odd-group tail stage, FP6
 // operand form and matrix instruction as the GEMM), one group per launch.
 // A translation unit of its own, so that the GEMM's schedule does not depend
 // on it.

@@ -18,9 +18,10 @@
 // in LDS in [m][n] order and leaves as 16-byte row segments.
 //
 // Per group of 64 along K and per 32 x 32 output block the wave issues
-//   - one v_mfma_scale_f32_32x32x64_f8f6f4 on the codes as FP8 (the stored
-//     code layout turns them into E4M3 subnormals with three VALU ops per
-//     8 codes, svdq_device.h): S, the group's exact integer sums, in fp32;
+//   - one v_mfma_scale_f32_32x32x64_f8f6f4 on the codes as FP6 (the stored
+//     code layout unfolds into E2M3 subnormals with four VALU ops per 16
+//     codes, svdq_device.h; FP6 runs at twice the FP8 rate): S, the group's
+//     exact integer sums, in fp32;
 //   - half of a v_mfma_f32_32x32x1_2b_f32, which forms the scale products
 //     P[n][m] = fl32(sw[n] sa[m]) of two 32 x 32 blocks at once (fp32
 //     outer products, straight from the fp32 scales in LDS) in the same
@@ -37,7 +38,7 @@
 // rows is one 128-byte line) and raw fp32 scales go from global memory
 // straight into a four-stage LDS ring with global_load_lds (no registers, no
 // LDS write instructions), up to three stages ahead of the one being read; each wave reads its fragments with 16-byte LDS reads
-// (XOR-swizzled rows, no bank conflicts) and turns the codes into FP8 in
+// (XOR-swizzled rows, no bank conflicts) and turns the codes into FP6 in
 // registers.
 #include "svdq_device.h"
 #include "svdq_internal.h"
@@ -220,7 +221,7 @@ struct Raw {
 };
 template <int WB>
 struct Frags {
-    i32x8 A[WB], B[WB];            // FP8 codes of the group, per block
+    i32x8 A[WB], B[WB];            // FP6 codes of the group, per block (6 of 8 words used)
     float PA, PB0, PB1;            // outer-product operands (weight, token scales)
 };
 
@@ -244,7 +245,7 @@ __device__ __forceinline__ void read_raw(Raw<WB> &rw, const uint8_t *st, const R
     }
 }
 
-// FP8 codes and the outer-product operands.  A lane holds 32 codes of its
+// FP6 codes and the outer-product operands.  A lane holds 32 codes of its
 // row (the group's k half ks2), the same 32 k in both operands.  A token
 // scale operand that is zero makes every product of its group zero, so the
 // group adds exactly nothing: `keep` false zeroes a group past K (the empty
@@ -256,8 +257,8 @@ __device__ __forceinline__ void make_frags(Frags<WB> &f, const Raw<WB> &rw, bool
                                            bool keep1 = true, bool scales = true) {
 #pragma unroll
     for (int blk = 0; blk < WB; ++blk) {
-        f.A[blk] = codes_to_fp8(rw.a[blk]);
-        f.B[blk] = codes_to_fp8(rw.b[blk]);
+        f.A[blk] = codes_to_fp6(rw.a[blk]);
+        f.B[blk] = codes_to_fp6(rw.b[blk]);
     }
     if (WB == 2) {
         f.PA = rw.sw;
@@ -799,7 +800,7 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
 //   x^ = fl32(h fl32(1 / lambda[n]))        (smoothing of the next layer)
 //   per token and group of 64 columns -- exactly one wave's columns, the
 //   lane's 32 values and those of its v_permlane32_swap partner --
-//   s = max|x^| / 7, code = rint(clamp(x^ fl32(1/s), -7, 7)): the same
+//   s = max|x^| / 7, code = rint(x^ fl32(1/s)) (within [-7, 7]): the same
 //   quantizer as K1, stored as the next layer's codes and scales;
 //   the tile's share of x^ L1 over its 128 columns: x^ as a bf16 hi/lo pair
 //   on v_mfma_f32_32x32x16_bf16 (rows: the lane's tokens, which is the
@@ -860,50 +861,50 @@ mlp_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const MlpArgs &ma
             const float t = 1.0f / s;
             inv = __builtin_isfinite(t) ? t : 0.0f;
         }
-        // The lane's codes come in groups of four (nibbles e0 .. e0 + 3 of a
-        // stored block, e0 = 8 (q % 2) + 4 ks2); the stored nibble e carries
-        // the sign of code e - 1, so nibble e0 takes the sign of the last code
-        // of a group held by lane l ^ 32 (same token): q ^ 1 for ks2 = 0, q
-        // for ks2 = 1.
-        uint32_t wsm[WB][4];                 // sign | magnitude nibbles
-        uint32_t last = 0;                   // their last codes' signs, bit 4 bi + q
+        // Column 32 bi + 8 q + 4 ks2 + j of the wave's group is code
+        // e = 8 (q % 2) + 4 ks2 + j of stored block 2 bi + q / 2, i.e. field
+        // 2 (4 ks2 + j) + q % 2 of that block's image: lane ks2 = 0 holds
+        // fields 0-7 (image bits 0-47) of each of the group's four blocks,
+        // its partner l ^ 32 fields 8-15 (bits 48-95).  Each lane converts
+        // its half as fields 0-7 (one FP6 conversion per block pair bi) and
+        // a ks2 = 1 lane moves it up by 48 bits; the partners then swap the
+        // halves of the pair the other one stores (lane ks2 stores pair
+        // bi = ks2: blocks 2 ks2, 2 ks2 + 1, 16 bytes) and OR them in.
+        uint32_t img[WB][6];
 #pragma unroll
         for (int bi = 0; bi < WB; ++bi) {
+            f32x16v a = {}, b = {};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t w = 0;
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float y = acc[bi * WB + bj][4 * q + j] * inv;   // |y| < 7.5: no clamp
-                    w |= (__float_as_uint(y + 12582912.0f) & 15u) << (4 * j);
+                    // |y| < 7.5: no clamp
+                    a[8 * u + j] = code_eighths(acc[bi * WB + bj][4 * (2 * u) + j] * inv);
+                    b[8 * u + j] = code_eighths(acc[bi * WB + bj][4 * (2 * u + 1) + j] * inv);
                 }
-                const uint32_t sg = w & 0x8888u, one = sg >> 3;
-                w = (((w ^ ((sg << 1) - one)) + one) & 0x7777u) | sg;
-                wsm[bi][q] = w;
-                last |= (w >> 15) << (4 * bi + q);
+            const i32x6 im = fp6_images(a, b);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t w0 = (uint32_t)im[3 * u], w1 = (uint32_t)im[3 * u + 1];
+                img[bi][3 * u] = ks2 ? 0u : w0;
+                img[bi][3 * u + 1] = ks2 ? (w0 << 16) : w1;
+                img[bi][3 * u + 2] = ks2 ? __builtin_amdgcn_alignbit(w1, w0, 16) : 0u;
             }
         }
-        const auto pl = __builtin_amdgcn_permlane32_swap(last, last, false, false);
-        const uint32_t other = pl[0] ^ pl[1] ^ last;   // the value of lane l ^ 32
-        // Stored 16-bit pieces: piece (bi, q) is bytes 16 bi + 4 q + 2 ks2 of
-        // the wave's 32 bytes of this token.  The partner lanes swap halves
-        // so that lane ks2 = 0 holds the four words of bi = 0 and lane ks2 = 1
-        // those of bi = 1: one 16-byte store each instead of eight 2-byte
-        // stores spread over 32 rows per instruction.
         u32x4 words;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t st[WB];
+        for (int u = 0; u < 2; ++u) {
+            uint32_t full[3];
 #pragma unroll
-            for (int bi = 0; bi < WB; ++bi) {
-                const uint32_t w = wsm[bi][q];
-                const uint32_t first = (other >> (4 * bi + (ks2 ? q : (q ^ 1)))) & 1u;
-                st[bi] = (w & 0x7777u) | ((w << 4) & 0x8880u) | (first << 3);
+            for (int w = 0; w < 3; ++w) {
+                const uint32_t give = ks2 ? img[0][3 * u + w] : img[1][3 * u + w];
+                const auto sw = __builtin_amdgcn_permlane32_swap(give, give, false, false);
+                const uint32_t got = sw[0] ^ sw[1] ^ give;           // the partner's half
+                full[w] = got | (ks2 ? img[1][3 * u + w] : img[0][3 * u + w]);
             }
-            const uint32_t give = ks2 ? st[0] : st[1];           // what the partner keeps
-            const auto sw = __builtin_amdgcn_permlane32_swap(give, give, false, false);
-            const uint32_t got = sw[0] ^ sw[1] ^ give;           // the partner's piece
-            words[q] = ks2 ? (got | (st[1] << 16)) : (st[0] | (got << 16));
+            const u32x2 st = fold_image(full[0], full[1], full[2]);
+            words[2 * u] = st.x;
+            words[2 * u + 1] = st.y;
         }
         if (m < M) {
             *reinterpret_cast<u32x4 *>(ma.qa + code_offset(m, kb, nw / 2 + 16 * ks2)) = words;

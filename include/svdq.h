@@ -32,13 +32,19 @@
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are
  *     row-major and contiguous.  Pointers marked "device" must point to
  *     memory of the current HIP device and be 16-byte aligned.
- *   - Packed INT4 codes (qa, qw): kb = K/2 bytes per row, two codes per
- *     byte; in each block of 16 consecutive codes of a row (8 bytes), code
- *     e sits in nibble e (element 2j in the low nibble of byte j) and that
- *     nibble holds |c_e| in bits 0-2 and the sign of c_((e-1) mod 16) in
- *     bit 3 (zero is stored without sign).  With this layout the GEMM turns
- *     the codes into FP8 (E4M3) operands of the matrix unit with three bit
- *     operations per 8 codes.  Rows are stored in pairs, [ceil(rows/2),
+ *   - Packed INT4 codes (qa, qw): kb = K/2 bytes per row, 4 bits per
+ *     code; each block of 16 consecutive codes of a row takes 8 bytes, two
+ *     little-endian words W0, W1.  Code e = 8h + i of the block (h = 0, 1;
+ *     i = 0..7) is field 2i + h of a 96-bit image, bits 6f .. 6f + 5 for
+ *     field f, holding the FP6 E2M3 encoding of c_e / 8: |c_e| in bits 0-2,
+ *     bits 3-4 zero, bit 5 set when c_e < 0 (zero is stored without sign).
+ *     With the image words I0, I1, I2 (bits 0-31, 32-63, 64-95),
+ *     W0 = I0 | (I2 & 0x18618618) and W1 = I1 | (I2 & 0x86186186): the
+ *     masks are the always-zero bits 3-4 of the fields of I0 and of I1
+ *     (positions p with p mod 6 = 3 or 4), disjoint, and together every bit
+ *     I2 can hold.  With this layout the GEMM unfolds the codes into FP6
+ *     operands of the matrix unit with four bit operations per 16 codes.
+ *     Rows are stored in pairs, [ceil(rows/2),
  *     2 kb] = [ceil(rows/2), K] bytes: each 64-byte chunk of a row (128
  *     codes, one stage of the GEMM) is followed by the same chunk of its
  *     pair partner, so one 128-byte line holds a stage of both rows; when
@@ -77,7 +83,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 3
+#define SVDQ_ABI_VERSION 4
 #define SVDQ_GROUP 64      /* quantization group along K */
 #define SVDQ_MAX_RANK 128  /* largest supported low-rank r */
 /* Size limits, so that every offset the kernels form within a tile fits its
@@ -398,7 +404,7 @@ int32_t svdq_mx_linear(const uint16_t *X, const float *lambda, const uint16_t *L
 
 /*
  * Test hook: the exact per-group integer sums of a block, taken from the
- * GEMM's own tile code (the same global -> LDS staging, code layout, FP8
+ * GEMM's own tile code (the same global -> LDS staging, code layout, FP6
  * operand form and matrix instruction as svdq_w4a4_lr_gemm; 128 x 128 tiles,
  * or 64 x 64 under SVDQ_TILES_QUARTER), one launch per group of 64.
  *   qa, sa, qw, sw  device codes and scales as svdq_w4a4_lr_gemm takes them

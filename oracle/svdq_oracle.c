@@ -23,12 +23,18 @@
  *   - the code is rint(fl32(v * fl32(1 / scale))), ties to even; a zero
  *     scale, or a scale whose reciprocal overflows, gives all-zero codes;
  *   - smoothing is one fp32 multiply by fl32(1 / lambda);
- *   - codes are packed two per byte, code k in the low nibble of byte k/2
- *     when k is even and in the high nibble when odd, row-major [rows, K/2];
- *     within each block of 16 consecutive codes of a row the nibble of code
- *     e holds |c_e| in bits 0-2 and the sign of code (e - 1) mod 16 of the
- *     same block in bit 3 (a zero code has no sign) -- the layout lets a GPU
- *     hand the codes to an FP8 matrix instruction as exact subnormals;
+ *   - codes are stored 4 bits each, row-major [rows, K/2] bytes; each block
+ *     of 16 consecutive codes of a row takes 8 bytes, built as follows.
+ *     Code e = 8h + i of the block (h = 0, 1; i = 0..7) becomes the 6-bit
+ *     field 2i + h of a 96-bit image (image bits 6f .. 6f + 5 for field f):
+ *     |c_e| in the field's bits 0-2, bits 3-4 zero, bit 5 set when c_e < 0
+ *     (a zero code has no sign) -- the OCP FP6 E2M3 encoding of c_e / 8.
+ *     Every field's bits 3-4 are zero, so image bits 0..63 carry 16 free
+ *     bits, and image bits 64..95 are stored in them: bit 64 + o goes to
+ *     stored bit o when bit o is a free bit of the first 32, otherwise to
+ *     stored bit 32 + o (which is then a free bit).  Stored bits 0..63 are
+ *     the block's 8 bytes, bit 8j + b in bit b of byte j -- the layout lets a
+ *     GPU hand the codes to an FP6 matrix instruction as exact subnormals;
  *     scales row-major [rows, K/64];
  *   - the rescale, the low-rank products, bias and the erf-form GELU are
  *     taken in fp64, and the output is ONE correct rounding of that fp64
@@ -52,11 +58,40 @@ static float bf16_to_float(uint16_t h)
     return f;
 }
 
-/* Nibble of code e of a block of 16 codes: |c_e|, and the sign of the code
- * before it (cyclically) in bit 3. */
-static unsigned code_nibble(const int *blk, int e)
+/* Image field (0..15) of code e (0..15) of a block: code 8h + i -> field
+ * 2i + h. */
+static int code_field(int e)
 {
-    return (unsigned)abs(blk[e]) | (blk[(e + 15) % 16] < 0 ? 8u : 0u);
+    return 2 * (e % 8) + e / 8;
+}
+
+/* Stored bit (0..63) of image bit p (0..95) of a block.  Bits 3 and 4 of
+ * every 6-bit field are zero in the image ("free"); bits 64.. of the image
+ * move into free bits at the same offset within a 32-bit word. */
+static int is_free_bit(int p)
+{
+    return p % 6 == 3 || p % 6 == 4;
+}
+static int stored_bit(int p)
+{
+    if (p < 64)
+        return p;
+    const int o = p - 64;
+    return is_free_bit(o) ? o : 32 + o;
+}
+
+/* Pack the 16 codes of one block into its 8 bytes. */
+static void pack_block(const int *blk, uint8_t *dst)
+{
+    memset(dst, 0, 8);
+    for (int e = 0; e < 16; ++e) {
+        const unsigned v = (unsigned)abs(blk[e]) | (blk[e] < 0 ? 32u : 0u);
+        for (int b = 0; b < 6; ++b)
+            if (v >> b & 1u) {   /* bits 3-4 of v are zero */
+                const int q = stored_bit(6 * code_field(e) + b);
+                dst[q / 8] |= (uint8_t)(1u << (q % 8));
+            }
+    }
 }
 
 /*
@@ -156,29 +191,29 @@ void oracle_quantize_groups(const float *v, int64_t rows, int64_t K,
                 q[j] = (int)c;
             }
             uint8_t *dst = packed + row * (K / 2) + g * (GROUP / 2);
-            for (int b = 0; b < GROUP / 2; ++b) {
-                const int *blk = q + 16 * ((2 * b) / 16);
-                const int e = (2 * b) % 16;
-                dst[b] = (uint8_t)(code_nibble(blk, e) | (code_nibble(blk, e + 1) << 4));
-            }
+            for (int t = 0; t < GROUP / 16; ++t)
+                pack_block(q + 16 * t, dst + 8 * t);
         }
     }
 }
 
-/* Decode packed codes [rows, K/2] into one int8 per element [rows, K]: the
- * magnitude of code e from its own nibble, its sign from bit 3 of the nibble
- * of code (e + 1) mod 16 of the block. */
+/* Decode packed codes [rows, K/2] into one int8 per element [rows, K]:
+ * each code's 6-bit field read back bit by bit from its stored bits. */
 void oracle_unpack(const uint8_t *packed, int64_t rows, int64_t K, int8_t *codes)
 {
     for (int64_t row = 0; row < rows; ++row)
         for (int64_t t = 0; t < K / 16; ++t) {
             const uint8_t *src = packed + row * (K / 2) + 8 * t;
-            unsigned nib[16];
-            for (int e = 0; e < 16; ++e)
-                nib[e] = (e % 2 == 0) ? (src[e / 2] & 0xFu) : (src[e / 2] >> 4);
             for (int e = 0; e < 16; ++e) {
-                const int mag = (int)(nib[e] & 7u);
-                codes[row * K + 16 * t + e] = (int8_t)((nib[(e + 1) % 16] & 8u) ? -mag : mag);
+                unsigned v = 0;
+                for (int b = 0; b < 6; ++b) {
+                    if (b == 3 || b == 4)
+                        continue;            /* the free bits, zero in the image */
+                    const int q = stored_bit(6 * code_field(e) + b);
+                    v |= (unsigned)(src[q / 8] >> (q % 8) & 1u) << b;
+                }
+                const int mag = (int)(v & 7u);
+                codes[row * K + 16 * t + e] = (int8_t)((v & 32u) ? -mag : mag);
             }
         }
 }

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bdt.svdq_abi_version() == 3
+    assert bdt.svdq_abi_version() == 4
     assert bdt.svdq_status_string(0) == "ok"
     assert bdt.svdq_status_string(MISALIGNED) == "misaligned pointer"
     assert bdt.svdq_status_string(99) == "unknown status"

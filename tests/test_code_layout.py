@@ -1,9 +1,9 @@
 """The packed INT4 code layout (include/svdq.h): within a row the oracle and the
 library store the same bytes; the library keeps rows in pairs, which the tests'
 converter maps to and from the oracle's row-major bytes.  Also the property the
-GEMM relies on: one AND gives the E4M3 bytes of the even codes of a block of 16
-and a funnel shift plus an AND those of the odd codes, each the E4M3 subnormal
-code * 2^-9.  Host-side arithmetic only (no GPU)."""
+GEMM relies on: one AND per stored word (two for the third image word) unfolds a
+block of 16 codes into its 96-bit FP6 (E2M3) image, each field the E2M3 subnormal
+code / 8.  Host-side arithmetic only (no GPU)."""
 import numpy as np
 import pytest
 
@@ -38,28 +38,30 @@ def test_round_trip_and_zero_has_no_sign():
     assert p[0, 0] == 0x07 and not p[0, 1:].any()
 
 
-def _e4m3_subnormal(b):
-    """Value of E4M3 bytes whose exponent field is 0: (-1)^s m 2^-9."""
-    b = np.asarray(b, np.uint32)
-    assert np.all((b & 0x78) == 0)
-    return np.where(b & 0x80, -1.0, 1.0) * (b & 7) * 2.0 ** -9
+def _e2m3_subnormal(f):
+    """Value of 6-bit E2M3 fields whose exponent bits (3-4) are 0: (-1)^s m / 8."""
+    f = np.asarray(f, np.int64)
+    assert np.all((f & 0x18) == 0)
+    return np.where(f & 0x20, -1.0, 1.0) * (f & 7) / 8.0
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_fp8_operand_form(seed):
+def test_fp6_operand_form(seed):
     rng = np.random.default_rng(seed)
     c = _codes(rng, 1, 64)[0]
-    x = _pack(c[None, :])[0, :16].view("<u4")          # one 16-byte read: codes 0..31
-    M = 0x87878787
-
-    def align4(hi, lo):                                # funnel shift of hi:lo right by 4
-        return ((int(hi) << 32 | int(lo)) >> 4) & 0xFFFFFFFF
-
-    words = [int(x[0]) & M, align4(x[1], x[0]) & M, int(x[1]) & M, align4(x[0], x[1]) & M,
-             int(x[2]) & M, align4(x[3], x[2]) & M, int(x[3]) & M, align4(x[2], x[3]) & M]
-    got = _e4m3_subnormal(np.array(words, "<u4").view(np.uint8)) * 2.0 ** 9
-    order = [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]
-    want = np.concatenate([c[:16][order], c[16:32][order]])
+    x = [int(w) for w in _pack(c[None, :])[0, :16].view("<u4")]   # one 16-byte read: codes 0..31
+    # the always-zero bits of the image: bits 3-4 of each 6-bit field
+    free = [sum(1 << o for o in range(32) if (32 * w + o) % 6 in (3, 4)) for w in (0, 1)]
+    keep = [0xFFFFFFFF ^ f for f in free]
+    words = []
+    for u in range(2):                                  # the two blocks of the read
+        w0, w1 = x[2 * u], x[2 * u + 1]
+        words += [w0 & keep[0], w1 & keep[1], (w0 & free[0]) | (w1 & free[1])]
+    bits = sum(w << (32 * i) for i, w in enumerate(words))
+    fields = [(bits >> (6 * f)) & 63 for f in range(32)]
+    got = _e2m3_subnormal(fields) * 8.0
+    # field f of block u holds code 16 u + 8 (f % 2) + f // 2
+    want = np.array([c[16 * (f // 16) + 8 * (f % 2) + (f % 16) // 2] for f in range(32)])
     assert np.array_equal(got, want)
 
 

@@ -37,12 +37,13 @@ MUTATIONS = [
     ("code_roundf", "svdq_oracle.c", "float c = rintf(y);", "float c = roundf(y);"),
     # scale as amax times a rounded 1/7
     ("scale_recip7", "svdq_oracle.c", "float s = amax / 7.0f;", "float s = amax * (1.0f / 7.0f);"),
-    # the sign bit taken from the next code instead of the previous one
-    ("sign_direction", "svdq_oracle.c", "blk[(e + 15) % 16] < 0", "blk[(e + 1) % 16] < 0"),
-    # nibble order swapped within a byte
-    ("nibble_order", "svdq_oracle.c",
-     "code_nibble(blk, e) | (code_nibble(blk, e + 1) << 4)",
-     "code_nibble(blk, e + 1) | (code_nibble(blk, e) << 4)"),
+    # codes in natural field order instead of the halves interleaved
+    ("field_order", "svdq_oracle.c", "return 2 * (e % 8) + e / 8;", "return e;"),
+    # the sign in the field's bit 3 instead of bit 5
+    ("sign_bit", "svdq_oracle.c", "(blk[e] < 0 ? 32u : 0u)", "(blk[e] < 0 ? 8u : 0u)"),
+    # the third image word folded into the wrong word (free bits of the other word)
+    ("fold_word", "svdq_oracle.c", "return is_free_bit(o) ? o : 32 + o;",
+     "return is_free_bit(o) ? 32 + o : o;"),
     # L2 read transposed
     ("l2_transposed", "svdq_oracle.c", "L2[(int64_t)i * N + n]", "L2[n * r + i]"),
     # bias dropped

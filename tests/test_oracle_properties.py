@@ -34,15 +34,23 @@ def _quant(vals):
 
 
 def _decode(packed, K):
-    """Codes from the packed layout as its definition states: code k in nibble k of the
-    row (low nibble of byte k/2 for even k); in each block of 16, nibble e holds |c_e| in
-    bits 0-2 and the sign of c_((e-1) mod 16) in bit 3."""
-    nib = np.empty((packed.shape[0], K), np.int64)
-    nib[:, 0::2] = packed & 0xF
-    nib[:, 1::2] = packed >> 4
-    blk = nib.reshape(packed.shape[0], K // 16, 16)
-    neg = np.roll(blk >> 3, -1, axis=-1)
-    return np.where(neg == 1, -(blk & 7), blk & 7).reshape(packed.shape[0], K)
+    """Codes from the packed layout, written from its definition: in each 8-byte block
+    of 16 codes (two little-endian words W0, W1), the 96-bit image of 6-bit fields is
+    I0 = W0 without its free bits, I1 = W1 without its free bits, I2 = the free bits of
+    both (a free bit is bit 3 or 4 of a field: image position p with p mod 6 in {3, 4});
+    code 8h + i is field 2i + h: |c| in bits 0-2, the sign in bit 5."""
+    free = [sum(1 << o for o in range(32) if (32 * w + o) % 6 in (3, 4)) for w in (0, 1)]
+    words = np.ascontiguousarray(packed, dtype=np.uint8).view("<u4").astype(object)
+    W0, W1 = words[:, 0::2], words[:, 1::2]                  # [rows, K / 16], Python ints
+    img = ((W0 & (0xFFFFFFFF ^ free[0])) | ((W1 & (0xFFFFFFFF ^ free[1])) << 32)
+           | (((W0 & free[0]) | (W1 & free[1])) << 64))
+    out = np.empty((packed.shape[0], K), np.int64)
+    for e in range(16):
+        f = 2 * (e % 8) + e // 8
+        v = (img >> (6 * f)) & 63
+        mag = (v & 7).astype(np.int64)
+        out[:, e::16] = np.where((v & 32).astype(np.int64) != 0, -mag, mag)
+    return out
 
 
 @SETTINGS
