@@ -31,8 +31,10 @@ PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP4 (and FP6) MFMA, 10.1 PFLOP/s
 # instruction, so its roofline is the FP6 peak; the fraction of the 8-bit peak
 # (the reference the metric's name gives) is reported beside it.
 PEAK_FP6_TFLOPS = PEAK_FP4_TFLOPS
-# VALU lane-operations per second without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# fp32 FMA lane-operations per second, from the published fp32 vector peak (157.3 TFLOP/s =
+# 256 CUs x 4 SIMDs x 32 lanes x 2 flops x 2.4 GHz); two waves of a SIMD were measured
+# issuing about 28 lanes of fp32 FMA per cycle together, so 16 lanes is not the ceiling
+PEAK_VALU_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 CACHE_BYTES = 256 << 20      # Infinity Cache; rotating input sets exceed 2x this
 METRIC = "effective TOPS (2MNK/t) of W4A4+rank-32 linear; % of INT8 MFMA / HBM peak"
 
