@@ -122,7 +122,9 @@ const char *svdq_last_error(void);
  * Offline weight preparation of the 4-bit residual (stage 3 of the SVDQuant
  * overview; the offline toolchain's "quantize, pack" steps in the blog's
  * section "Quantize your own model").
- *   R   device fp32 [N, K]  residual weight (nn.Linear orientation, out x in)
+ *   R   device fp32 [N, K]  residual weight (nn.Linear orientation, out x in),
+ *                           finite (a NaN or an infinity gives unspecified
+ *                           codes and scales)
  *   qw  device u8   [ceil(N/2), K] packed 4-bit codes, row pairs (out)
  *   sw  device fp32 [ceil(K/128), N, 2] group scales, stage-major (out)
  * Same quantizer as the activations, without smoothing.  N >= 0 (0: no-op),
@@ -158,7 +160,8 @@ size_t svdq_quantize_act_down_workspace_bytes(int64_t M, int64_t K, int32_t r);
  * Smoothing, activation quantization and low-rank down-projection in one
  * pass over X (model card, section "Nunchaku engine design", item (b): the
  * down-projection and the quantizer share their input).
- *   X       device bf16 [M, K]   activations
+ *   X       device bf16 [M, K]   activations, finite (a NaN or an infinity
+ *                                gives unspecified codes and scales)
  *   lambda  device fp32 [K]      smoothing factors, finite and > 0
  *   L1      device bf16 [K, r]   low-rank down factor (NULL iff r == 0)
  *   qa      device u8   [ceil(M/2), K] packed codes of X diag(lambda)^-1 (out)
