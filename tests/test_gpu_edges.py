@@ -204,3 +204,24 @@ def test_gelu_epilogue_accuracy():
     bound = 0.5 * oracle.bf16_ulp(exact) + 4e-7 * np.abs(b) + 1e-38
     assert np.all(np.abs(y - exact[None, :]) <= bound[None, :])
     assert np.all(y == y[0:1])                     # every row the same
+
+
+@pytest.mark.parametrize("K", [65536, 65472])
+def test_long_k_whole_layer(K):
+    # A long reduction: 1024 (even) and 1023 (odd) groups, so that K1 adds 512 chunks of
+    # partial down-projections (two groups each at this token count) and the GEMM's K loop
+    # runs 512 stages, the odd count ending in a one-group stage.  Ragged M and N, GELU,
+    # r = 32.  Codes and scales bit-exact, every output element within the tolerance.
+    M, N, r = 70, 136, 32
+    L = make_layer(LayerSpec("longk", M, K, N, r, 0.01, 20.0, 4, False, act=1, cfg_id=260 + K % 7))
+    qa_o, sa_o, _ = oracle.quantize_act(L.X, L.lam)
+    print("long K: M=%d K=%d N=%d r=%d" % (M, K, N, r), flush=True)
+    qa, sa, xl1 = bdt.quantize_act_down(to_dev(L.X), to_dev(L.lam), to_dev(L.L1))
+    assert np.array_equal(from_pairs(qa, M), qa_o)
+    assert np.array_equal(from_stage_major(sa, M, K // 64).view(np.uint32), sa_o.view(np.uint32))
+    qw_o, sw_o = oracle.pack_weights(L.R)
+    Y = bf16_host(bdt.linear(to_dev(L.X), to_dev(L.lam), to_dev(L.L1), pdev(qw_o), sdev(sw_o),
+                             to_dev(L.L2), to_dev(L.bias), 1))
+    _, y_or = oracle.linear(L.X, L.lam, L.L1, qw_o, sw_o, L.L2, L.bias, 1)
+    worst = assert_y_close(Y, y_or, "long K %d" % K)
+    print("  worst |err|/tol = %.3f" % worst, flush=True)
