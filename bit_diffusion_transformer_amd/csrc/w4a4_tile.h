@@ -637,7 +637,8 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
     }
     // The tile goes out through LDS (as the plain store): staged in [m][n]
     // order past the L2^T rows, then written as 16-byte segments of 8
-    // consecutive d of one token and head, eight lanes per 128-byte line.
+    // consecutive d of one token and head, eight lanes per 128-byte line,
+    // non-temporal as the plain store.
     constexpr int BT = 64 * WB;
     constexpr int OP = 2 * BT + 16;                          // staged row pitch, bytes
     uint8_t *ost = reinterpret_cast<uint8_t *>(&sm) + BT * (SVDQ_MAX_RANK_DEV + 8) * 2;
@@ -785,8 +786,8 @@ qkv_epilogue(f32x16 (&acc)[WB * WB], const u32x2 (&bb)[WB][4], const QkvArgs &qk
         const int64_t nl = nsec + 8 * ch;
         const int64_t h = nl / D, d = nl - h * D;
         const int64_t b = m / S, sp = m - b * S;
-        *reinterpret_cast<u32x4 *>(dst + ((b * qk.H + h) * S + sp) * D + d) =
-            *reinterpret_cast<const u32x4 *>(ost + row * OP + 16 * ch);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(ost + row * OP + 16 * ch),
+                                    reinterpret_cast<u32x4 *>(dst + ((b * qk.H + h) * S + sp) * D + d));
     }
 }
 
@@ -1311,7 +1312,9 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
     // The tile goes out through LDS: staged in [m][n] order, then written as
     // 16-byte row segments, eight lanes per 128-byte line (a direct store
     // from the transposed tile would write 8 bytes into each of 32 rows per
-    // instruction).  The staging area lies past the L2^T rows that other
+    // instruction).  The stores are non-temporal: the output is written once
+    // and not read here, so it should not displace from L2 the operands that
+    // the XCD's other tiles still read.  The staging area lies past the L2^T rows that other
     // waves may still be reading for the rank-r step.
     // Block (bi, bj); element i of the lane is n = base + 8 (i / 4) +
     // 4 (lane / 32) + i % 4, m = base + lane % 32.
@@ -1348,8 +1351,8 @@ tile_body(const uint8_t *__restrict__ qa, const void *__restrict__ sa,
         const int row = idx / CH, ch = idx % CH;
         const int64_t m = m0 + row, n = n0 + 8 * ch;
         if (m < M && n < N)
-            *reinterpret_cast<u32x4 *>(Y + m * N + n) =
-                *reinterpret_cast<const u32x4 *>(ost + row * OP + 16 * ch);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(ost + row * OP + 16 * ch),
+                                        reinterpret_cast<u32x4 *>(Y + m * N + n));
     }
 }
 
