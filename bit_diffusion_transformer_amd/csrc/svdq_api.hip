@@ -106,11 +106,35 @@ int32_t check_n(int64_t N) {
     return check_rows(N, "N");
 }
 
+// A launch's work-items (workgroups x threads) must fit the 32-bit grid size
+// of a dispatch.  Shapes inside the row and K limits can still exceed it
+// (e.g. 2^28 tokens with a wide N); they are rejected here rather than
+// launched with a truncated grid.
+int32_t check_grid(int64_t workgroups, int64_t threads, const char *what) {
+    if (workgroups > (int64_t)0xFFFFFFFF / threads)
+        return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
+                    "%s would need %lld workgroups of %lld threads, more than 2^32 - 1 work-items",
+                    what, (long long)workgroups, (long long)threads);
+    return SVDQ_OK;
+}
+
 #define SVDQ_TRY(expr)                       \
     do {                                     \
         int32_t _s = (expr);                 \
         if (_s != SVDQ_OK) return _s;        \
     } while (0)
+
+// The activation step (at most one workgroup per 64 rows and two groups)
+// and its partial-sum reduce; the GEMM's largest tile family (64 x 64 tiles
+// of up to 512 threads).
+int32_t check_down_grid(int64_t M, int64_t K, int32_t r) {
+    SVDQ_TRY(check_grid((M + 63) / 64 * ((K / SVDQ_GROUP + 1) / 2), 256, "the activation step"));
+    return check_grid((M * r / 4 + 63) / 64, 256, "the partial-sum reduce");
+}
+
+int32_t check_gemm_grid(int64_t M, int64_t N) {
+    return check_grid((M + 63) / 64 * ((N + 63) / 64), 512, "the GEMM");
+}
 
 int32_t need_ptr(const void *p, const char *name) {
     if (!p) return fail(SVDQ_ERR_INVALID_ARG, "%s must not be NULL", name);
@@ -135,6 +159,7 @@ int32_t validate_down(const uint16_t *X, const float *lambda, const uint16_t *L1
     SVDQ_TRY(check_k(K));
     SVDQ_TRY(check_r(r));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_down_grid(M, K, r));
     SVDQ_TRY(need_ptr(X, "X"));
     SVDQ_TRY(need_ptr(lambda, "lambda"));
     SVDQ_TRY(need_ptr(qa, "qa"));
@@ -157,6 +182,7 @@ int32_t validate_gemm(const uint8_t *qa, const void *sa, const uint8_t *qw, cons
     SVDQ_TRY(check_k(K));
     SVDQ_TRY(check_r(r));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_gemm_grid(M, N));
     SVDQ_TRY(need_ptr(qa, "qa"));
     SVDQ_TRY(need_ptr(sa, "sa"));
     SVDQ_TRY(need_ptr(qw, "qw"));
@@ -275,7 +301,8 @@ int32_t check_awq_pack_shape(int64_t N, int64_t K) {
     SVDQ_TRY(check_rows(N, "N"));
     SVDQ_TRY(check_k(K));
     if (N > 0) SVDQ_TRY(check_n(N));
-    return SVDQ_OK;
+    const int64_t threads = (N + 15) / 16 * 16 * 4 * ((K / SVDQ_GROUP + 3) / 4);
+    return check_grid((threads + 255) / 256, 256, "the W4A16 packer");
 }
 
 // Per-device cache of the per-workgroup LDS limit.
@@ -385,6 +412,7 @@ int32_t svdq_repack_weights(const uint8_t *codes, const float *scales, int64_t N
     SVDQ_TRY(check_rows(N, "N"));
     SVDQ_TRY(check_k(K));
     if (N == 0) return SVDQ_OK;
+    SVDQ_TRY(check_grid((N * (K / 16) + 255) / 256, 256, "the repack"));
     SVDQ_TRY(need_ptr(codes, "codes"));
     SVDQ_TRY(need_ptr(scales, "scales"));
     SVDQ_TRY(need_ptr(qw, "qw"));
@@ -459,6 +487,8 @@ int32_t svdq_linear(const uint16_t *X, const float *lambda, const uint16_t *L1,
     SVDQ_TRY(check_k(K));
     SVDQ_TRY(check_r(r));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_down_grid(M, K, r));
+    SVDQ_TRY(check_gemm_grid(M, N));
     SVDQ_TRY(need_ptr(X, "X"));
     SVDQ_TRY(need_ptr(lambda, "lambda"));
     SVDQ_TRY(need_ptr(qw, "qw"));
@@ -495,6 +525,8 @@ int32_t svdq_linear_noalloc(const uint16_t *X, const float *lambda, const uint16
     SVDQ_TRY(check_k(K));
     SVDQ_TRY(check_r(r));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_down_grid(M, K, r));
+    SVDQ_TRY(check_gemm_grid(M, N));
     SVDQ_TRY(need_ptr(X, "X"));
     SVDQ_TRY(need_ptr(lambda, "lambda"));
     SVDQ_TRY(need_ptr(qw, "qw"));
@@ -533,6 +565,8 @@ int32_t svdq_linear_qkv(const uint16_t *X, const float *lambda, const uint16_t *
     SVDQ_TRY(check_k(K));
     SVDQ_TRY(check_r(r));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_down_grid(M, K, r));
+    SVDQ_TRY(check_gemm_grid(M, 3 * (int64_t)epi->heads * epi->head_dim));
     SVDQ_TRY(need_ptr(X, "X"));
     SVDQ_TRY(need_ptr(lambda, "lambda"));
     SVDQ_TRY(need_ptr(qw, "qw"));
@@ -576,6 +610,7 @@ int32_t svdq_w4a4_lr_gemm_quant_down(const uint8_t *qa, const float *sa, const u
     SVDQ_TRY(validate_gemm(qa, sa, qw, sw, xl1, L2, bias, act, M, N, K, r,
                            reinterpret_cast<const uint16_t *>(qa_next)));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_down_grid(M, N, r_next));
     SVDQ_TRY(need_ptr(lambda_next, "lambda_next"));
     SVDQ_TRY(need_ptr(sa_next, "sa_next"));
     SVDQ_TRY(lr_ptrs(L1_next, "L1_next", xl1_next, "xl1_next", r_next));
@@ -622,6 +657,10 @@ int32_t svdq_mlp(const uint16_t *X, const float *lambda_up, const uint16_t *L1_u
     SVDQ_TRY(check_r(r_down));
     SVDQ_TRY(check_next_shape(N_hidden, r_down));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_down_grid(M, K, r_up));
+    SVDQ_TRY(check_gemm_grid(M, N_hidden));
+    SVDQ_TRY(check_down_grid(M, N_hidden, r_down));
+    SVDQ_TRY(check_gemm_grid(M, K));
     SVDQ_TRY(need_ptr(X, "X"));
     SVDQ_TRY(need_ptr(lambda_up, "lambda_up"));
     SVDQ_TRY(need_ptr(qw_up, "qw_up"));
@@ -723,6 +762,8 @@ int32_t svdq_mx_linear(const uint16_t *X, const float *lambda, const uint16_t *L
     SVDQ_TRY(check_k_mx(K));
     SVDQ_TRY(check_r(r));
     if (M == 0) return SVDQ_OK;
+    SVDQ_TRY(check_down_grid(M, K, r));
+    SVDQ_TRY(check_gemm_grid(M, N));
     SVDQ_TRY(need_ptr(X, "X"));
     SVDQ_TRY(need_ptr(lambda, "lambda"));
     SVDQ_TRY(need_ptr(qw, "qw"));
@@ -832,6 +873,7 @@ int32_t svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *packed, const ui
         return fail(SVDQ_ERR_UNSUPPORTED_SHAPE,
                     "K = %lld: one activation row does not fit the %zu-byte workgroup LDS",
                     (long long)K, limit);
+    SVDQ_TRY(check_grid((N + 15) / 16 * ((M + MT - 1) / MT), 256, "the W4A16 linear"));
     return hip_status(
         svdq::launch_awq_linear(X, packed, bias, M, N, K, MT, Y, (hipStream_t)stream),
         "awq_w4a16_linear launch");

@@ -89,14 +89,16 @@ extern "C" {
 /* Size limits, so that every offset the kernels form within a tile fits its
  * integer type: K (in-features) at most 2^20, and M (tokens) and N
  * (out-features) at most 2^28 each.  Larger sizes are rejected with
- * SVDQ_ERR_UNSUPPORTED_SHAPE. */
+ * SVDQ_ERR_UNSUPPORTED_SHAPE, and so are shapes inside these limits whose
+ * launches would need more than 2^32 - 1 work-items (a dispatch's grid size;
+ * e.g. the GEMM at M = 2^28 with N = 2^16: far beyond any device memory). */
 #define SVDQ_MAX_K (1 << 20)
 #define SVDQ_MAX_ROWS (1 << 28)
 
 typedef enum {
     SVDQ_OK = 0,
     SVDQ_ERR_INVALID_ARG = 1,       /* NULL pointer where data is needed, negative size, bad act */
-    SVDQ_ERR_UNSUPPORTED_SHAPE = 2, /* K % 64 != 0, K < 64, N % 8 != 0, r not a multiple of 16 or > 128, a size past SVDQ_MAX_K / SVDQ_MAX_ROWS */
+    SVDQ_ERR_UNSUPPORTED_SHAPE = 2, /* K % 64 != 0, K < 64, N % 8 != 0, r not a multiple of 16 or > 128, a size past SVDQ_MAX_K / SVDQ_MAX_ROWS, a launch past 2^32 - 1 work-items */
     SVDQ_ERR_MISALIGNED = 3,        /* a device pointer not 16-byte aligned */
     SVDQ_ERR_WORKSPACE_TOO_SMALL = 4,
     SVDQ_ERR_UNSUPPORTED_DEVICE = 5, /* current device is not gfx950 (or no device) */

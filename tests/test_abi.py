@@ -124,6 +124,21 @@ def test_linear_rejects(lib, kw, code):
     assert _lin(lib, **kw) == code
 
 
+# Shapes within the row and K limits whose launches would exceed the 2^32 - 1 work-items of a
+# dispatch grid: rejected as unsupported before any device call (no GPU needed here).
+@pytest.mark.parametrize("call", [
+    lambda lib: _down(lib, M=1 << 28, K=1 << 20, r=16),          # the activation step
+    lambda lib: _down(lib, M=1 << 28, K=128, r=128),             # its partial-sum reduce
+    lambda lib: _gemm(lib, M=1 << 28, N=1 << 16, K=128),         # the GEMM
+    lambda lib: _lin(lib, M=1 << 28, N=1 << 16, K=128),
+    lambda lib: lib.svdq_repack_weights(P(A), P(A), 1 << 28, 1 << 20, P(A), P(A), None),
+    lambda lib: lib.svdq_awq_pack_weights(P(A), 1 << 28, 1 << 20, P(A), None),
+])
+def test_oversized_launches_rejected(lib, call):
+    assert call(lib) == SHAPE
+    assert b"work-items" in lib.svdq_last_error()
+
+
 def test_pack_and_debug_reject(lib):
     assert lib.svdq_pack_weights(P(A), -1, 128, P(A), P(A), None) == INVALID
     assert lib.svdq_pack_weights(P(A), 8, 100, P(A), P(A), None) == SHAPE
